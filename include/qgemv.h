@@ -1,0 +1,250 @@
+/*
+ * qgemv.h -- C interface of libqgemv: block-quantized weight x Q8-quantized
+ * activation products for decode on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the statement of the problem on these pages:
+ *
+ *  [PR623] "ROCm: restore DeepSeek V4 Flash decode performance and Q4 SSD
+ *          streaming", antirez/ds4 pull request 623 -- Summary (prequantized
+ *          Q8 decode for regular, paired, HC-expand and low-rank attention
+ *          output projections; the compact selected-expert table staged before
+ *          the pointer-backed routed-MoE launch), Correctness (the missing
+ *          compact table is a hard error) and the review comments (per-stage
+ *          timing of the Q8_0 entry points; "selected expert id -1 outside
+ *          0..256" as a failed decode).
+ *  [PR621] "Support AProjQ4 GGUFs: Q4_K dense attention projections ...",
+ *          antirez/ds4 pull request 621 -- Q4_K dense attention projections
+ *          and the dequantize + GEMM prefill path.
+ *  [SOOT]  "DeepSeek V4 Flash on Strix Halo: tuning ROCm, matching Vulkan"
+ *          (soothill.io) -- "Why I did not keep a ROCm kernel patch": the
+ *          decode mat-vec plus the Q8 activation quantizer with a block sum.
+ *  [ATOM]  ROCm/ATOM "DeepSeek-V4 Usage Guide" -- sigmoid routing of 6
+ *          experts out of 256 or 384.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller, 16-byte
+ *    aligned, row-major and densely packed.  The library never allocates,
+ *    frees or retains them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on it and returns; nothing synchronizes.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Return value: QG_OK (0) when the work was enqueued; a negative QG_ERR_*
+ *    code when the host-side checks fail, in which case NOTHING was launched
+ *    and no output was touched.  QG_ERR_LAUNCH reports a failed launch.
+ *  - Data errors that only the device can see (expert ids) are reported in a
+ *    caller-provided device int32 status word (see moe_routed_qgemv).
+ *  - The library keeps no global mutable state; calls on different streams
+ *    may run concurrently.  Results are deterministic: the same inputs give
+ *    bit-identical outputs, and row t of a batched call equals the M = 1 call
+ *    on token t.
+ *
+ * Weight formats (the pages name Q8_0 and Q4_K but print no byte layout; this
+ * library defines its own, "Q4_K-style"):
+ *
+ *  QG_FMT_Q8_0  blocks of 32 weights, 34 bytes: fp16 scale d (little endian),
+ *               then 32 int8 quants q.  weight = d * q.
+ *  QG_FMT_Q4K   superblocks of 256 weights, 144 bytes: fp16 d, fp16 dmin,
+ *               then 12 bytes holding sixteen 6-bit fields as one
+ *               little-endian 96-bit string (field f = bits [6f, 6f+6);
+ *               fields 0..7 are sub-block scales sc[j], 8..15 sub-block mins
+ *               m[j]), then 128 bytes of 4-bit quants: sub-block 2p (p=0..3)
+ *               in the low nibbles of bytes 16+32p .. 16+32p+31, sub-block
+ *               2p+1 in the high nibbles of the same bytes.
+ *               weight = d * sc[j] * q - dmin * m[j].
+ *  A weight matrix with N rows (outputs) and K columns (inputs) is N rows of
+ *  K/32 Q8_0 blocks or K/256 Q4_K superblocks; rows are consecutive.  Every
+ *  projection here needs K % 256 == 0 (so each row is 16-byte aligned) and
+ *  256 <= K <= QG_MAX_K.
+ *
+ * Q8 activation (what quantize_act_q8 produces and every projection consumes):
+ *  qx int8 [M, K]; dx fp32 [M, K/32], the scale of each 32-block;
+ *  sx int32 [M, K/32], the sum of each block's quants (used by Q4_K's min term).
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define QG_OK 0
+#define QG_ERR_NULL (-1)      /* a required pointer is NULL */
+#define QG_ERR_SHAPE (-2)     /* a size is out of range (see each call) */
+#define QG_ERR_ALIGN (-3)     /* a pointer is not 16-byte aligned */
+#define QG_ERR_FORMAT (-4)    /* unknown weight format */
+#define QG_ERR_WORKSPACE (-5) /* workspace smaller than moe_routed_workspace_bytes() */
+#define QG_ERR_LAUNCH (-6)    /* the kernel launch failed (hipGetLastError) */
+
+/* device status word values (moe_routed_qgemv) */
+#define QG_DEV_OK 0
+#define QG_DEV_BAD_EXPERT 1  /* an expert id outside [0, E) */
+#define QG_DEV_NULL_EXPERT 2 /* a selected expert has a NULL weight pointer */
+
+/* weight formats */
+#define QG_FMT_Q8_0 0
+#define QG_FMT_Q4K 1
+
+/* limits */
+#define QG_MAX_K 16384        /* largest K (inputs) of a projection */
+#define QG_MAX_M 32           /* largest token batch of qgemv_* */
+#define QG_MAX_MOE_PAIRS 8192 /* largest T * topk of moe_routed_qgemv */
+#define QG_MAX_EXPERTS 4096   /* largest E of moe_routed_qgemv */
+
+/* ---- activation quantization ------------------------------------------- */
+/*
+ * quantize_act_q8 -- [PR623] Summary: quantize the decode activation to Q8
+ * once, then feed every Q8 projection; [SOOT] the quantizer that keeps a block
+ * sum next to the scale.
+ *
+ * For each row m < M and each block b < K/32 of x (fp32 [M, K]):
+ *   amax = max |x|;  d = amax / 127 (IEEE fp32 division, round to nearest);
+ *   q_i  = round-half-to-even(x_i / d) clamped to [-127, 127], or 0 when d == 0;
+ *   dx[m, b] = d;  sx[m, b] = sum_i q_i;  qx[m, 32b + i] = q_i.
+ * Bit-exact: the fp32 quotient is correctly rounded, subnormals are kept.
+ * NaN or Inf inputs are outside the contract.
+ * Errors: QG_ERR_NULL; QG_ERR_SHAPE unless M >= 1 and K >= 32, K % 32 == 0;
+ * QG_ERR_ALIGN.
+ */
+int quantize_act_q8(const float *x, int M, int K, int8_t *qx, float *dx, int32_t *sx, void *stream);
+
+/* ---- decode mat-vec ---------------------------------------------------- */
+/*
+ * qgemv_q8_0 -- [PR623] the regular Q8_0 projection on a prequantized
+ * activation (matmul_q8_0_tensor in the per-stage table).
+ *   y[m, n] = sum_b dw[n, b] * dx[m, b] * sum_{i<32} qw[n, b, i] * qx[m, 32b + i]
+ * W: QG_FMT_Q8_0 [N, K]; qx/dx: Q8 activation of M tokens; y fp32 [M, N].
+ * Each weight block is read once for all M tokens.  The per-block integer
+ * sums are exact; scaling and accumulation are fp32 (error well under
+ * 1e-5 * sum |w * x| per output).
+ * Errors: QG_ERR_NULL; QG_ERR_SHAPE unless N >= 1, 1 <= M <= QG_MAX_M,
+ * K % 256 == 0, 256 <= K <= QG_MAX_K; QG_ERR_ALIGN; QG_ERR_LAUNCH.
+ */
+int qgemv_q8_0(const void *W, int N, int K, const int8_t *qx, const float *dx, int M, float *y, void *stream);
+
+/*
+ * qgemv_q4k -- [PR621] Q4_K dense attention projection on a Q8 activation.
+ *   y[m, n] = sum_s sum_j dx[m, sj] * ( d[n,s] * sc[n,s,j] * sum_i q[n,s,j,i] * qx[m, ...]
+ *                                      - dmin[n,s] * m[n,s,j] * sx[m, sj] )
+ * (s = superblock, j = sub-block; sj = 8s + j is the 32-block index.)
+ * W: QG_FMT_Q4K [N, K]; qx/dx/sx as from quantize_act_q8; y fp32 [M, N].
+ * Errors: as qgemv_q8_0.
+ */
+int qgemv_q4k(const void *W, int N, int K, const int8_t *qx, const float *dx, const int32_t *sx, int M, float *y,
+              void *stream);
+
+/*
+ * qgemv_paired -- [PR623] the paired projection (matmul_q8_0_pair_tensor):
+ * one prequantized activation feeds two weight matrices in a single launch,
+ * e.g. the low-rank style 4096->1024 and 4096->512 pair.
+ *   y1 = W1 . x  ([M, N1]),   y2 = W2 . x  ([M, N2])
+ * Both matrices have format `fmt` and K inputs.  Each output equals the
+ * single-matrix call bit for bit.  sx may be NULL for QG_FMT_Q8_0.
+ * Errors: QG_ERR_FORMAT; otherwise as qgemv_q8_0 (N1, N2 >= 1).
+ */
+int qgemv_paired(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const int8_t *qx, const float *dx,
+                 const int32_t *sx, int M, float *y1, float *y2, void *stream);
+
+/* ---- routed MoE -------------------------------------------------------- */
+/*
+ * Workspace of moe_routed_qgemv, in bytes, for the given sizes (0 if a size
+ * is out of range).  The caller allocates it on the device; its contents
+ * after a call are described by moe_routed_workspace_layout.
+ */
+size_t moe_routed_workspace_bytes(int T, int topk, int E, int D, int F);
+
+/* regions of the MoE workspace (byte offsets from moe_routed_workspace_layout) */
+#define QG_WS_NUNIQ 0    /* int32 [1]      number of distinct valid experts U */
+#define QG_WS_UNIQ 1     /* int32 [Ucap]   distinct expert ids, ascending */
+#define QG_WS_SLOT 2     /* int32 [P]      index in uniq of pair p's expert, -1 if invalid */
+#define QG_WS_PAIR_OFF 3 /* int32 [Ucap+1] CSR offsets into pairs */
+#define QG_WS_PAIRS 4    /* int32 [P]      pair indices grouped by expert, ascending within */
+#define QG_WS_G 5        /* fp32  [P, F]   gate outputs */
+#define QG_WS_V 6        /* fp32  [P, F]   up outputs */
+#define QG_WS_H 7        /* fp32  [P, F]   silu(g) * v */
+#define QG_WS_HQ 8       /* int8  [P, F]   Q8 quants of h */
+#define QG_WS_HD 9       /* fp32  [P, F/32] Q8 scales of h */
+#define QG_WS_HS 10      /* int32 [P, F/32] Q8 block sums of h */
+#define QG_WS_O 11       /* fp32  [P, D]   down outputs per pair */
+#define QG_WS_COUNT 12
+/* P = T * topk, Ucap = min(P, E).  Rows of pairs with an invalid id are not written. */
+
+/*
+ * moe_routed_workspace_layout -- byte offsets of the regions above, written
+ * to offsets[0 .. QG_WS_COUNT).  Returns QG_OK or QG_ERR_SHAPE / QG_ERR_NULL.
+ */
+int moe_routed_workspace_layout(int T, int topk, int E, int D, int F, size_t *offsets);
+
+/*
+ * moe_routed_qgemv -- [PR623] routed-MoE decode driven by a compact
+ * selected-expert table built on the device before the pointer-backed expert
+ * launches (Summary; "missing compact selected experts" was the failure it
+ * fixes); [ATOM] top-6 sigmoid-normalized routing.
+ *
+ * For T tokens with Q8 activations qx/dx/sx ([T, D]) and selected experts
+ * ids int32 [T, topk] with routing weights rw fp32 [T, topk]:
+ *   1. table: uniq = distinct valid ids ascending, slot, CSR pairs (workspace);
+ *   2. for each distinct expert e and each of its pairs p = (t, k):
+ *        g = gate_e . x_t,  v = up_e . x_t             (Q4_K, F x D)
+ *        h = silu(g) * v  (fp32),  (hq, hd, hs) = Q8-quantize(h)
+ *   3.   o_p = down_e . hq                              (Q4_K, D x F)
+ *   4. y[t] = sum_k rw[t, k] * o_(t,k)   in k order (fp32).
+ * Each selected expert's weights are streamed once for all of its pairs.
+ * gate/up/down are DEVICE arrays of E device pointers (pointer-backed expert
+ * table); experts that are not selected are never dereferenced and may be
+ * NULL.  The host never waits for the table: the number of distinct experts
+ * stays on the device.
+ *
+ * Data errors: an id outside [0, E) sets *d_status to QG_DEV_BAD_EXPERT, and
+ * a selected expert with a NULL pointer sets QG_DEV_NULL_EXPERT (whichever
+ * is found first is kept); such a pair contributes 0 to y and every other
+ * pair is still computed.  *d_status is written with QG_DEV_OK first, on the
+ * stream, so the caller reads it after synchronizing.
+ *
+ * Errors: QG_ERR_NULL (any pointer except unselected experts);
+ * QG_ERR_SHAPE unless 1 <= T, 1 <= topk, T*topk <= QG_MAX_MOE_PAIRS,
+ * 1 <= E <= QG_MAX_EXPERTS, D and F multiples of 256 in [256, QG_MAX_K];
+ * QG_ERR_WORKSPACE if ws_bytes < moe_routed_workspace_bytes(...);
+ * QG_ERR_ALIGN; QG_ERR_LAUNCH.
+ */
+int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t *sx, int T, int D, int F, int E, int topk,
+                     const int32_t *ids, const float *rw, const void *const *gate, const void *const *up,
+                     const void *const *down, float *y, void *ws, size_t ws_bytes, int32_t *d_status, void *stream);
+
+/* ---- prefill ----------------------------------------------------------- */
+/*
+ * qgemm_prefill -- [PR621] the dequantize-then-GEMM path for prefill batches
+ * of Q4_K projections (the path whose ~16x regression and recovery the page
+ * reports).
+ *   Y[m, n] = sum_k w[n, k] * x[m, k],  w from QG_FMT_Q4K W [N, K],
+ *   x bf16 [M, K] (raw bits), Y fp32 [M, N], fp32 accumulation on matrix
+ *   cores (error well under 1e-5 * sum |w * x| per output).
+ * Errors: QG_ERR_FORMAT (only QG_FMT_Q4K); QG_ERR_NULL; QG_ERR_SHAPE unless
+ * M >= 1, N >= 1, K % 256 == 0, 256 <= K <= QG_MAX_K; QG_ERR_ALIGN;
+ * QG_ERR_LAUNCH.
+ */
+int qgemm_prefill(int fmt, const void *W, int N, int K, const uint16_t *x_bf16, int M, float *y, void *stream);
+
+/* ---- diagnostics ------------------------------------------------------- */
+/* Human-readable text for a QG_* status or QG_DEV_* value (static storage). */
+const char *qg_status_string(int status);
+
+/*
+ * qgemv_debug_block_isums -- the exact per-block integer sums that the GEMV
+ * kernels form, from the same device code:
+ *   isum[m, n, b] = sum_{i<32} q_w[n, b, i] * qx[m, 32b + i]
+ * (q_w = int8 quant for Q8_0, 4-bit quant 0..15 of sub-block b for Q4_K).
+ * isum int32 [M, N, K/32].  For testing; errors as qgemv_q8_0.
+ */
+int qgemv_debug_block_isums(int fmt, const void *W, int N, int K, const int8_t *qx, int M, int32_t *isum,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,153 @@
+"""Python binding of libqgemv -- argument marshalling only.
+
+Every function has the name and argument order of the C entry point declared
+in ``include/qgemv.h``; device buffers are passed as torch tensors in the
+pointer positions (their ``data_ptr()`` is handed to the library) and the
+stream defaults to torch's current stream on the tensors' device.  All
+arithmetic happens in the HIP kernels of ``libqgemv.so``: if the library is
+missing this module raises at import time; nothing falls back to another path.
+
+A negative status from the library raises :class:`QGError`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "QGError", "FMT_Q8_0", "FMT_Q4K", "library_path", "quantize_act_q8", "qgemv_q8_0", "qgemv_q4k",
+    "qgemv_paired", "moe_routed_workspace_bytes", "moe_routed_workspace_layout", "moe_routed_qgemv",
+    "qgemm_prefill", "qg_status_string", "qgemv_debug_block_isums", "pointer_table", "WS_REGIONS",
+]
+
+FMT_Q8_0 = 0
+FMT_Q4K = 1
+DEV_OK, DEV_BAD_EXPERT, DEV_NULL_EXPERT = 0, 1, 2
+MAX_K, MAX_M, MAX_MOE_PAIRS, MAX_EXPERTS = 16384, 32, 8192, 4096
+WS_REGIONS = ["NUNIQ", "UNIQ", "SLOT", "PAIR_OFF", "PAIRS", "G", "V", "H", "HQ", "HD", "HS", "O"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError("libqgemv.so is not built (run __graft_entry__.build()); there is no fallback path")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+
+
+def _sig(name, restype, argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = argtypes
+    return f
+
+
+_c_quantize = _sig("quantize_act_q8", _i, [_vp, _i, _i, _vp, _vp, _vp, _vp])
+_c_q8_0 = _sig("qgemv_q8_0", _i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp])
+_c_q4k = _sig("qgemv_q4k", _i, [_vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp])
+_c_paired = _sig("qgemv_paired", _i, [_i, _vp, _i, _vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp])
+_c_isums = _sig("qgemv_debug_block_isums", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
+_c_status = _sig("qg_status_string", ctypes.c_char_p, [_i])
+try:
+    _c_ws_bytes = _sig("moe_routed_workspace_bytes", _sz, [_i, _i, _i, _i, _i])
+    _c_ws_layout = _sig("moe_routed_workspace_layout", _i, [_i, _i, _i, _i, _i, _vp])
+    _c_moe = _sig("moe_routed_qgemv", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _sz, _vp, _vp])
+except AttributeError:  # library built before the MoE sources existed
+    _c_ws_bytes = _c_ws_layout = _c_moe = None
+try:
+    _c_prefill = _sig("qgemm_prefill", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
+except AttributeError:
+    _c_prefill = None
+
+
+class QGError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (what, qg_status_string(status), status))
+
+
+def qg_status_string(status: int) -> str:
+    return _c_status(int(status)).decode()
+
+
+def _ptr(t):
+    """Device pointer of a torch tensor (or None -> NULL)."""
+    if t is None:
+        return None
+    if hasattr(t, "data_ptr"):
+        if not t.is_cuda:
+            raise TypeError("libqgemv takes device tensors; got a tensor on %s" % t.device)
+        if not t.is_contiguous():
+            raise TypeError("libqgemv takes contiguous tensors")
+        return t.data_ptr()
+    return int(t)
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+    import torch
+    for t in tensors:
+        if t is not None and hasattr(t, "device"):
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ok(rc: int, what: str):
+    if rc != 0:
+        raise QGError(rc, what)
+
+
+def quantize_act_q8(x, M: int, K: int, qx, dx, sx, stream=None) -> None:
+    _ok(_c_quantize(_ptr(x), M, K, _ptr(qx), _ptr(dx), _ptr(sx), _stream(stream, x)), "quantize_act_q8")
+
+
+def qgemv_q8_0(W, N: int, K: int, qx, dx, M: int, y, stream=None) -> None:
+    _ok(_c_q8_0(_ptr(W), N, K, _ptr(qx), _ptr(dx), M, _ptr(y), _stream(stream, W)), "qgemv_q8_0")
+
+
+def qgemv_q4k(W, N: int, K: int, qx, dx, sx, M: int, y, stream=None) -> None:
+    _ok(_c_q4k(_ptr(W), N, K, _ptr(qx), _ptr(dx), _ptr(sx), M, _ptr(y), _stream(stream, W)), "qgemv_q4k")
+
+
+def qgemv_paired(fmt: int, W1, N1: int, W2, N2: int, K: int, qx, dx, sx, M: int, y1, y2, stream=None) -> None:
+    _ok(_c_paired(fmt, _ptr(W1), N1, _ptr(W2), N2, K, _ptr(qx), _ptr(dx), _ptr(sx), M, _ptr(y1), _ptr(y2),
+                  _stream(stream, W1)), "qgemv_paired")
+
+
+def qgemv_debug_block_isums(fmt: int, W, N: int, K: int, qx, M: int, isum, stream=None) -> None:
+    _ok(_c_isums(fmt, _ptr(W), N, K, _ptr(qx), M, _ptr(isum), _stream(stream, W)), "qgemv_debug_block_isums")
+
+
+def moe_routed_workspace_bytes(T: int, topk: int, E: int, D: int, F: int) -> int:
+    return int(_c_ws_bytes(T, topk, E, D, F))
+
+
+def moe_routed_workspace_layout(T: int, topk: int, E: int, D: int, F: int) -> dict:
+    offs = (ctypes.c_size_t * len(WS_REGIONS))()
+    _ok(_c_ws_layout(T, topk, E, D, F, ctypes.cast(offs, ctypes.c_void_p)), "moe_routed_workspace_layout")
+    return {name: int(offs[i]) for i, name in enumerate(WS_REGIONS)}
+
+
+def pointer_table(tensors, device):
+    """int64 device tensor holding the device addresses of `tensors` (None -> NULL)."""
+    import torch
+    addrs = [0 if t is None else _ptr(t) for t in tensors]
+    return torch.tensor(addrs, dtype=torch.int64, device=device)
+
+
+def moe_routed_qgemv(qx, dx, sx, T: int, D: int, F: int, E: int, topk: int, ids, rw, gate, up, down, y, ws,
+                     ws_bytes: int, d_status, stream=None) -> None:
+    _ok(_c_moe(_ptr(qx), _ptr(dx), _ptr(sx), T, D, F, E, topk, _ptr(ids), _ptr(rw), _ptr(gate), _ptr(up),
+               _ptr(down), _ptr(y), _ptr(ws), ws_bytes, _ptr(d_status), _stream(stream, qx)), "moe_routed_qgemv")
+
+
+def qgemm_prefill(fmt: int, W, N: int, K: int, x_bf16, M: int, y, stream=None) -> None:
+    _ok(_c_prefill(fmt, _ptr(W), N, K, _ptr(x_bf16), M, _ptr(y), _stream(stream, W)), "qgemm_prefill")

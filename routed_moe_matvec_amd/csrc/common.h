@@ -1,0 +1,63 @@
+// Device helpers shared by the libqgemv kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qgemv.h"
+
+namespace qg {
+
+constexpr int kWave = 64;
+
+// Weights per "group": the unit one lane decodes at a time.  For Q8_0 that
+// is 8 blocks (8 x 34 = 272 bytes, a multiple of 16), for Q4_K one superblock
+// (144 bytes).  Both cover 256 consecutive weights of a row, so rows with
+// K % 256 == 0 are whole numbers of groups and stay 16-byte aligned.
+constexpr int kGroupWeights = 256;
+
+template <int FMT>
+struct GroupBytes;
+template <>
+struct GroupBytes<QG_FMT_Q8_0> {
+    static constexpr int value = 272;
+};
+template <>
+struct GroupBytes<QG_FMT_Q4K> {
+    static constexpr int value = 144;
+};
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// low 32 bits of ({hi, lo} >> 8 * shift), shift in 0..3
+__device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t shift) {
+    return __builtin_amdgcn_alignbyte(hi, lo, shift);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
+}
+
+__device__ __forceinline__ float fmaf_exact(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+
+// 16-byte global -> LDS copy of one chunk per lane, written to
+// lds_base + 16 * lane (lds_base must be wave-uniform).
+__device__ __forceinline__ void global_to_lds16(const void *gsrc, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+// Wait until every outstanding vector-memory operation of this wave (including
+// global->LDS copies) has completed.  gfx9 s_waitcnt encoding: vmcnt = 0,
+// expcnt = 7 (no wait), lgkmcnt = 15 (no wait).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+template <class T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+}  // namespace qg

@@ -1,0 +1,257 @@
+"""GPU parity of the activation quantizer and the dense decode mat-vecs.
+
+The HIP library is called through its C ABI (the ctypes binding); expected
+values come only from the CPU oracle on the same seeded inputs.
+Bit-exact: qx/dx/sx and the per-block integer sums.  fp32 outputs:
+|y - y_oracle| <= 1e-5 * sum_k |w_k x_k| per output.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests import fmt_helpers as fh
+from tests.gpu_util import assert_within_bound, dev, empty, host, oracle_threads, progress, sentinel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qg():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import routed_moe_matvec_amd as qg
+    return qg
+
+
+def gpu_quantize(qg, x: np.ndarray):
+    import torch
+    M, K = x.shape
+    xd = dev(x.astype(np.float32))
+    qx = empty((M, K), torch.int8)
+    dx = empty((M, K // 32), torch.float32)
+    sx = empty((M, K // 32), torch.int32)
+    qg.quantize_act_q8(xd, M, K, qx, dx, sx)
+    return qx, dx, sx
+
+
+# ---------------------------------------------------------------- quantizer
+
+@pytest.mark.parametrize("M,K", [(1, 32), (1, 1024), (3, 4096), (8, 8192), (5, 2080)])
+def test_quantize_bit_exact(qg, orc, M, K):
+    progress("quantize M=%d K=%d" % (M, K))
+    g = np.random.default_rng(100 + M * 7 + K)
+    x = synth.activations(g, M, K) * np.float32(10.0) ** g.integers(-3, 4, size=(M, 1)).astype(np.float32)
+    nb = K // 32
+    # special blocks: all zero, exact ties at scale 1, subnormal scale, single spike
+    if nb >= 4:
+        x[0, 0:32] = 0.0
+        x[0, 32:64] = np.array([127.0, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, -1.5] * 4, np.float32)
+        x[0, 64:96] = np.float32(2.0 ** -149) * np.arange(-16, 16, dtype=np.float32) * 9
+        x[0, 96:128] = 0.0
+        x[0, 100] = -3.7
+    qx, dx, sx = gpu_quantize(qg, x)
+    rq, rd, rs = orc.quantize_act_q8(x)
+    assert np.array_equal(host(qx), rq)
+    assert np.array_equal(host(dx).view(np.uint32), rd.view(np.uint32))
+    assert np.array_equal(host(sx), rs)
+
+
+def test_quantize_errors(qg):
+    import torch
+    x = dev(np.zeros((1, 64), np.float32))
+    qx, dx, sx = empty((1, 64), torch.int8), empty((1, 2), torch.float32), empty((1, 2), torch.int32)
+    with pytest.raises(qg.QGError) as e:
+        qg.quantize_act_q8(x, 1, 48, qx, dx, sx)
+    assert e.value.status == -2
+    with pytest.raises(qg.QGError) as e:
+        qg.quantize_act_q8(x, 0, 64, qx, dx, sx)
+    assert e.value.status == -2
+    assert qg._c_quantize(x.data_ptr(), 1, 64, None, dx.data_ptr(), sx.data_ptr(), None) == -1
+    assert qg._c_quantize(x.data_ptr() + 4, 1, 32, qx.data_ptr(), dx.data_ptr(), sx.data_ptr(), None) == -3
+
+
+# ---------------------------------------------------------------- GEMV parity
+
+def _weights(fmt, g, N, K):
+    return synth.q8_0_weight(g, N, K) if fmt == 0 else synth.q4k_weight(g, N, K)
+
+
+def _run_gemv(qg, fmt, W, N, K, qx, dx, sx, M):
+    import torch
+    y = sentinel((M, N), torch.float32, 12345.0)
+    if fmt == 0:
+        qg.qgemv_q8_0(W, N, K, qx, dx, M, y)
+    else:
+        qg.qgemv_q4k(W, N, K, qx, dx, sx, M, y)
+    return host(y)
+
+
+GEMV_CASES = [
+    # fmt, N, K, M : the 512x1024 Q8_0 workload, ragged tiles, non-power-of-two
+    # groups per row, the largest K, odd batch sizes
+    (0, 512, 1024, 1),
+    (0, 37, 256, 1),
+    (0, 100, 1280, 3),
+    (0, 9, 12288, 2),
+    (0, 64, 16384, 1),
+    (0, 333, 2048, 9),
+    (1, 77, 4096, 1),
+    (1, 50, 1792, 4),
+    (1, 19, 16384, 2),
+    (1, 130, 256, 33 - 1),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,M", GEMV_CASES)
+def test_gemv_parity_small(qg, orc, fmt, N, K, M):
+    progress("gemv fmt=%d N=%d K=%d M=%d" % (fmt, N, K, M))
+    g = np.random.default_rng(1000 + fmt * 100 + N + K + M)
+    W = _weights(fmt, g, N, K)
+    x = synth.activations(g, M, K)
+    qx, dx, sx = gpu_quantize(qg, x)
+    y = _run_gemv(qg, fmt, dev(W), N, K, qx, dx, sx, M)
+    ref, bound = orc.gemv(fmt, W, N, K, host(qx), host(dx), nthreads=oracle_threads())
+    assert_within_bound(y, ref, bound, what="gemv fmt=%d N=%d K=%d M=%d" % (fmt, N, K, M))
+
+
+def test_q8_0_out_projection_full_size(qg, orc):
+    """The 8192 -> 4096 Q8_0 output projection, batch 1, every output vs the oracle."""
+    progress("q8_0 4096x8192 full")
+    w = synth.WORKLOADS["q8_0_out_4096x8192"]
+    g = synth.rng(w["seed"])
+    N, K = w["N"], w["K"]
+    W = synth.q8_0_weight(g, N, K)
+    x = synth.activations(g, 1, K)
+    qx, dx, sx = gpu_quantize(qg, x)
+    y = _run_gemv(qg, 0, dev(W), N, K, qx, dx, sx, 1)
+    ref, bound = orc.gemv(0, W, N, K, host(qx), host(dx), nthreads=oracle_threads())
+    assert_within_bound(y, ref, bound, what="q8_0 4096x8192")
+
+
+def test_q4k_projection_full_size(qg, orc):
+    """The 4096 -> 8192 Q4_K projection, batch 1, every output vs the oracle."""
+    progress("q4k 8192x4096 full")
+    w = synth.WORKLOADS["q4k_8192x4096"]
+    g = synth.rng(w["seed"])
+    N, K = w["N"], w["K"]
+    W = synth.q4k_weight(g, N, K)
+    x = synth.activations(g, 1, K)
+    qx, dx, sx = gpu_quantize(qg, x)
+    y = _run_gemv(qg, 1, dev(W), N, K, qx, dx, sx, 1)
+    ref, bound = orc.gemv(1, W, N, K, host(qx), host(dx), nthreads=oracle_threads())
+    assert_within_bound(y, ref, bound, what="q4k 8192x4096")
+
+
+def test_batched_sweep_full_size(qg, orc):
+    """Q8_0 4096 -> 16384 at M = 1..32: each row of a batched call equals the M = 1 call on
+    that token bit for bit; sampled outputs match the oracle."""
+    progress("q8_0 16384x4096 batched sweep")
+    w = synth.WORKLOADS["q8_0_16384x4096"]
+    g = synth.rng(w["seed"])
+    N, K = w["N"], w["K"]
+    W = synth.q8_0_weight(g, N, K)
+    Wd = dev(W)
+    x = synth.activations(g, 32, K)
+    qx, dx, sx = gpu_quantize(qg, x)
+    singles = [_run_gemv(qg, 0, Wd, N, K, qx[t:t + 1], dx[t:t + 1], sx[t:t + 1], 1) for t in range(32)]
+    rows = np.sort(g.choice(N, 96, replace=False))
+    Wsub = W[rows]
+    for M in w["Ms"]:
+        y = _run_gemv(qg, 0, Wd, N, K, qx[:M], dx[:M], sx[:M], M)
+        for t in range(M):
+            assert np.array_equal(y[t], singles[t][0]), "batch invariance M=%d t=%d" % (M, t)
+        ref, bound = orc.gemv(0, Wsub, len(rows), K, host(qx[:M]), host(dx[:M]), nthreads=oracle_threads())
+        assert_within_bound(y[:, rows], ref, bound, what="batched M=%d" % M)
+
+
+def test_paired_equals_two_singles_and_oracle(qg, orc):
+    """One quantized 4096-vector feeds 4096->1024 and 4096->512 in one launch."""
+    progress("paired 1024+512 x 4096")
+    w = synth.WORKLOADS["q8_0_pair_1024+512x4096"]
+    g = synth.rng(w["seed"])
+    K, N1, N2 = w["K"], w["N1"], w["N2"]
+    for fmt in (0, 1):
+        W1, W2 = _weights(fmt, g, N1, K), _weights(fmt, g, N2, K)
+        x = synth.activations(g, 2, K)
+        qx, dx, sx = gpu_quantize(qg, x)
+        import torch
+        for M in (1, 2):
+            y1, y2 = sentinel((M, N1), torch.float32), sentinel((M, N2), torch.float32)
+            qg.qgemv_paired(fmt, dev(W1), N1, dev(W2), N2, K, qx[:M], dx[:M], sx[:M], M, y1, y2)
+            s1 = _run_gemv(qg, fmt, dev(W1), N1, K, qx[:M], dx[:M], sx[:M], M)
+            s2 = _run_gemv(qg, fmt, dev(W2), N2, K, qx[:M], dx[:M], sx[:M], M)
+            assert np.array_equal(host(y1), s1) and np.array_equal(host(y2), s2)
+            r1, b1 = orc.gemv(fmt, W1, N1, K, host(qx[:M]), host(dx[:M]))
+            r2, b2 = orc.gemv(fmt, W2, N2, K, host(qx[:M]), host(dx[:M]))
+            assert_within_bound(host(y1), r1, b1, what="paired y1")
+            assert_within_bound(host(y2), r2, b2, what="paired y2")
+
+
+@pytest.mark.parametrize("fmt,N,K,M", [(0, 45, 1024, 2), (0, 8, 12288, 1), (1, 33, 2048, 3), (1, 5, 256, 1)])
+def test_block_isums_bit_exact(qg, orc, fmt, N, K, M):
+    import torch
+    progress("isums fmt=%d N=%d K=%d M=%d" % (fmt, N, K, M))
+    g = np.random.default_rng(2000 + fmt + N + K)
+    W = _weights(fmt, g, N, K)
+    qx, _, _ = gpu_quantize(qg, synth.activations(g, M, K))
+    isum = sentinel((M, N, K // 32), torch.int32)
+    qg.qgemv_debug_block_isums(fmt, dev(W), N, K, qx, M, isum)
+    assert np.array_equal(host(isum), orc.block_isums(fmt, W, N, K, host(qx)))
+
+
+def test_integer_weights_are_exact(qg):
+    """d = 1 Q8_0 weights and a scale-1 integer activation: every partial sum is an
+    integer below 2^24, so the fp32 result equals the int64 matmul exactly."""
+    g = np.random.default_rng(31)
+    N, K, M = 70, 1024, 2
+    q = g.integers(-40, 41, size=(N, K // 32, 32)).astype(np.int8)
+    W = synth.q8_0_from_parts(np.ones((N, K // 32), np.float16), q)
+    x = fh.integer_activation(g, M, K)
+    qx, dx, sx = gpu_quantize(qg, x)
+    assert np.all(host(dx) == 1.0)
+    y = _run_gemv(qg, 0, dev(W), N, K, qx, dx, sx, M)
+    assert np.array_equal(y.astype(np.float64), (x.astype(np.int64) @ q.reshape(N, K).astype(np.int64).T))
+
+
+def test_zero_weights_give_exact_zero(qg):
+    N, K = 16, 512
+    W = synth.q8_0_from_parts(np.zeros((N, K // 32), np.float16), np.ones((N, K // 32, 32), np.int8))
+    qx, dx, sx = gpu_quantize(qg, synth.activations(np.random.default_rng(3), 1, K))
+    y = _run_gemv(qg, 0, dev(W), N, K, qx, dx, sx, 1)
+    assert np.all(y == 0.0)
+
+
+def test_deterministic_across_calls(qg):
+    g = np.random.default_rng(77)
+    N, K = 1000, 4096
+    for fmt in (0, 1):
+        Wd = dev(_weights(fmt, g, N, K))
+        qx, dx, sx = gpu_quantize(qg, synth.activations(g, 4, K))
+        a = _run_gemv(qg, fmt, Wd, N, K, qx, dx, sx, 4)
+        b = _run_gemv(qg, fmt, Wd, N, K, qx, dx, sx, 4)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_gemv_errors_leave_outputs_untouched(qg):
+    import torch
+    g = np.random.default_rng(5)
+    N, K = 8, 512
+    Wd = dev(synth.q8_0_weight(g, N, K))
+    qx, dx, sx = gpu_quantize(qg, synth.activations(g, 2, K))
+    y = sentinel((2, N), torch.float32, 3.0)
+    cases = [
+        (lambda: qg._c_q8_0(Wd.data_ptr(), N, 300, qx.data_ptr(), dx.data_ptr(), 1, y.data_ptr(), None), -2),
+        (lambda: qg._c_q8_0(Wd.data_ptr(), N, K, qx.data_ptr(), dx.data_ptr(), 0, y.data_ptr(), None), -2),
+        (lambda: qg._c_q8_0(Wd.data_ptr(), N, K, qx.data_ptr(), dx.data_ptr(), 33, y.data_ptr(), None), -2),
+        (lambda: qg._c_q8_0(Wd.data_ptr(), 0, K, qx.data_ptr(), dx.data_ptr(), 1, y.data_ptr(), None), -2),
+        (lambda: qg._c_q8_0(Wd.data_ptr(), N, 32768, qx.data_ptr(), dx.data_ptr(), 1, y.data_ptr(), None), -2),
+        (lambda: qg._c_q8_0(None, N, K, qx.data_ptr(), dx.data_ptr(), 1, y.data_ptr(), None), -1),
+        (lambda: qg._c_q8_0(Wd.data_ptr(), N, K, qx.data_ptr(), dx.data_ptr(), 1, None, None), -1),
+        (lambda: qg._c_q8_0(Wd.data_ptr() + 2, N, K, qx.data_ptr(), dx.data_ptr(), 1, y.data_ptr(), None), -3),
+        (lambda: qg._c_q4k(Wd.data_ptr(), N, K, qx.data_ptr(), dx.data_ptr(), None, 1, y.data_ptr(), None), -1),
+        (lambda: qg._c_paired(7, Wd.data_ptr(), N, Wd.data_ptr(), N, K, qx.data_ptr(), dx.data_ptr(), None, 1,
+                              y.data_ptr(), y.data_ptr(), None), -4),
+    ]
+    for fn, want in cases:
+        assert fn() == want
+    assert np.all(host(y) == 3.0)
