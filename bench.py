@@ -1,0 +1,379 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized decode mat-vec on one MI355X.
+
+One step = one pass of the decode projections of the Q8_0 attention workload
+(batch 1): quantize an 8192-wide fp32 activation to Q8, the 8192 -> 4096 output
+projection, quantize a 4096-wide activation, and the paired 4096 -> 1024 +
+4096 -> 512 low-rank projection in one launch.  Inputs are seeded synthetic
+tensors resident in HBM before timing starts.  Weights rotate over copies that
+together exceed 1 GiB, so no step reads weights left in the 256 MB Infinity
+Cache or in L2 by an earlier step.  The steps are captured once in a HIP graph
+and replayed, so host launch cost does not enter the timed region.
+
+Prints ONE JSON line.  `value` is the achieved algorithmic HBM bandwidth of the
+whole step (packed weight blocks + activations + outputs, GB/s); `roofline`
+describes the dominant kernel (the 4096 x 8192 Q8_0 GEMV) timed live with HIP
+events; `cpu_baseline` is the fp64 CPU oracle on a bounded sample of the same
+step; `extra` holds the other workloads (latency, Q4_K, batched sweep, routed
+MoE tokens/s, prefill) measured the same way.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+       python bench.py --summarize-rocprof DIR   (turn rocprofv3 csv output into a text summary)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16, published
+ROTATE_BYTES = 1 << 30  # > 2x the 256 MB Infinity Cache
+METRIC = "decode GEMV µs and achieved HBM GB/s (% of peak); routed-MoE tokens/s"
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; profile summaries record it so stale counters are detected."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "routed_moe_matvec_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- timing helpers
+
+class Timer:
+    """HIP-event timing of work enqueued on one stream."""
+
+    def __init__(self, stream):
+        import torch
+        self.torch = torch
+        self.stream = stream
+
+    def run(self, fn):
+        torch = self.torch
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):  # graph replays go to the current stream
+            s.record(self.stream)
+            fn()
+            e.record(self.stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e-3  # seconds
+
+
+def capture(fn, n: int, stream):
+    """HIP graph of n calls fn(0..n-1) on `stream`."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn(0)  # make sure every lazily created resource exists before capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def rotation_count(bytes_per_copy: int) -> int:
+    return max(2, -(-ROTATE_BYTES // bytes_per_copy))
+
+
+# ----------------------------------------------------------------------------- workload
+
+class DecodeStep:
+    """The timed step: two quantizations and the out / paired Q8_0 projections."""
+
+    def __init__(self, qg, torch):
+        import synth
+        w_out = synth.WORKLOADS["q8_0_out_4096x8192"]
+        w_pair = synth.WORKLOADS["q8_0_pair_1024+512x4096"]
+        g = synth.rng(w_out["seed"])
+        self.N, self.K = w_out["N"], w_out["K"]
+        self.N1, self.N2, self.K2 = w_pair["N1"], w_pair["N2"], w_pair["K"]
+        self.W_host = synth.q8_0_weight(g, self.N, self.K)
+        self.x_host = synth.activations(g, 1, self.K)
+        self.W1_host = synth.q8_0_weight(g, self.N1, self.K2)
+        self.W2_host = synth.q8_0_weight(g, self.N2, self.K2)
+        self.x2_host = synth.activations(g, 1, self.K2)
+        per_copy = self.W_host.nbytes + self.W1_host.nbytes + self.W2_host.nbytes
+        self.R = rotation_count(per_copy)
+        dev = "cuda"
+        base = [torch.from_numpy(a).to(dev) for a in (self.W_host, self.W1_host, self.W2_host)]
+        self.W = [base[0]] + [base[0].clone() for _ in range(self.R - 1)]
+        self.W1 = [base[1]] + [base[1].clone() for _ in range(self.R - 1)]
+        self.W2 = [base[2]] + [base[2].clone() for _ in range(self.R - 1)]
+        self.x = torch.from_numpy(self.x_host).to(dev)
+        self.x2 = torch.from_numpy(self.x2_host).to(dev)
+        K, K2 = self.K, self.K2
+        self.qx = torch.empty(1, K, dtype=torch.int8, device=dev)
+        self.dx = torch.empty(1, K // 32, dtype=torch.float32, device=dev)
+        self.sx = torch.empty(1, K // 32, dtype=torch.int32, device=dev)
+        self.qx2 = torch.empty(1, K2, dtype=torch.int8, device=dev)
+        self.dx2 = torch.empty(1, K2 // 32, dtype=torch.float32, device=dev)
+        self.sx2 = torch.empty(1, K2 // 32, dtype=torch.int32, device=dev)
+        self.y = torch.empty(1, self.N, dtype=torch.float32, device=dev)
+        self.y1 = torch.empty(1, self.N1, dtype=torch.float32, device=dev)
+        self.y2 = torch.empty(1, self.N2, dtype=torch.float32, device=dev)
+        self.qg = qg
+        self.weight_bytes = per_copy
+
+    # algorithmic bytes (what the method must move), per kernel
+    def bytes_quantize(self, K):
+        return K * 4 + K + (K // 32) * 8
+
+    def bytes_gemv(self, Wbytes, N, K):
+        return Wbytes + K + (K // 32) * 4 + N * 4
+
+    @property
+    def out_gemv_bytes(self):
+        return self.bytes_gemv(self.W_host.nbytes, self.N, self.K)
+
+    @property
+    def step_bytes(self):
+        return (self.bytes_quantize(self.K) + self.out_gemv_bytes + self.bytes_quantize(self.K2)
+                + self.W1_host.nbytes + self.W2_host.nbytes + self.K2 + (self.K2 // 32) * 4
+                + (self.N1 + self.N2) * 4)
+
+    def step(self, i):
+        qg, r = self.qg, i % self.R
+        qg.quantize_act_q8(self.x, 1, self.K, self.qx, self.dx, self.sx)
+        qg.qgemv_q8_0(self.W[r], self.N, self.K, self.qx, self.dx, 1, self.y)
+        qg.quantize_act_q8(self.x2, 1, self.K2, self.qx2, self.dx2, self.sx2)
+        qg.qgemv_paired(qg.FMT_Q8_0, self.W1[r], self.N1, self.W2[r], self.N2, self.K2, self.qx2, self.dx2,
+                        self.sx2, 1, self.y1, self.y2)
+
+    def out_gemv(self, i):
+        self.qg.qgemv_q8_0(self.W[i % self.R], self.N, self.K, self.qx, self.dx, 1, self.y)
+
+
+def cpu_baseline(step: DecodeStep, budget_s: float = 12.0) -> dict:
+    """The CPU oracle, untuned, on the same step: quantize both activations and run the
+    three products in fp64 on all host cores; as many whole steps as fit in ~budget_s."""
+    import oracle
+    threads = max(1, os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        qx, dx, _ = oracle.quantize_act_q8(step.x_host)
+        oracle.gemv(oracle.FMT_Q8_0, step.W_host, step.N, step.K, qx, dx, nthreads=threads)
+        qx2, dx2, _ = oracle.quantize_act_q8(step.x2_host)
+        oracle.gemv(oracle.FMT_Q8_0, step.W1_host, step.N1, step.K2, qx2, dx2, nthreads=threads)
+        oracle.gemv(oracle.FMT_Q8_0, step.W2_host, step.N2, step.K2, qx2, dx2, nthreads=threads)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_step = el / n
+    return {"value": round(step.step_bytes / per_step / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "ms_per_step": round(per_step * 1e3, 3),
+            "sample": "%d whole steps of the same decode workload (quantize 8192 + Q8_0 4096x8192 + quantize "
+                      "4096 + Q8_0 1024x4096 and 512x4096), fp64 oracle with OpenMP over rows" % n}
+
+
+def load_traffic(kernel_key: str, src_hash: str):
+    """Measured HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- extra workloads
+
+def extra_measurements(qg, torch, stream, timer) -> dict:
+    import synth
+    out = {}
+    dev = "cuda"
+
+    def quantized(K, M=1, seed=0):
+        g = synth.rng(seed)
+        x = torch.from_numpy(synth.activations(g, M, K)).to(dev)
+        qx = torch.empty(M, K, dtype=torch.int8, device=dev)
+        dx = torch.empty(M, K // 32, dtype=torch.float32, device=dev)
+        sx = torch.empty(M, K // 32, dtype=torch.int32, device=dev)
+        qg.quantize_act_q8(x, M, K, qx, dx, sx)
+        return qx, dx, sx
+
+    def gemv_rate(fmt, W_host, N, K, Ms, label):
+        R = rotation_count(W_host.nbytes)
+        base = torch.from_numpy(W_host).to(dev)
+        copies = [base] + [base.clone() for _ in range(R - 1)]
+        res = {}
+        for M in Ms:
+            qx, dx, sx = quantized(K, M)
+            y = torch.empty(M, N, dtype=torch.float32, device=dev)
+            if fmt == 0:
+                fn = lambda i: qg.qgemv_q8_0(copies[i % R], N, K, qx, dx, M, y)
+            else:
+                fn = lambda i: qg.qgemv_q4k(copies[i % R], N, K, qx, dx, sx, M, y)
+            n = max(R, 64)
+            g = capture(fn, n, stream)
+            timer.run(g.replay)
+            sec = timer.run(g.replay) / n
+            byts = W_host.nbytes + M * K + M * (K // 32) * (8 if fmt else 4) + M * N * 4
+            res["M%d" % M] = {"us": round(sec * 1e6, 3), "GB_s": round(byts / sec / 1e9, 1),
+                              "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4)}
+            del g
+        del copies, base
+        torch.cuda.empty_cache()
+        out[label] = res
+
+    g = synth.rng(0)
+    w = synth.WORKLOADS["q8_0_512x1024"]
+    gemv_rate(0, synth.q8_0_weight(g, w["N"], w["K"]), w["N"], w["K"], [1], "q8_0_512x1024")
+    w = synth.WORKLOADS["q4k_8192x4096"]
+    gemv_rate(1, synth.q4k_weight(synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], [1], "q4k_8192x4096")
+    w = synth.WORKLOADS["q8_0_16384x4096"]
+    gemv_rate(0, synth.q8_0_weight(synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], list(w["Ms"]),
+              "q8_0_16384x4096")
+    return out
+
+
+# ----------------------------------------------------------------------------- rocprof summary
+
+def summarize_rocprof(path: str) -> str:
+    """Text summary of a rocprofv3 --kernel-trace --stats --output-format csv directory:
+    per (kernel, grid size) the number of dispatches and their average / min / max duration."""
+    import csv
+    import glob
+    import statistics
+    lines = []
+    for tr in sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(tr) as f:
+            rows = list(csv.DictReader(f))
+        groups = {}
+        for r in rows:
+            key = (r.get("Kernel_Name", "?"), r.get("Grid_Size_X", r.get("Grid_Size", "?")))
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault(key, []).append(d)
+        lines.append("# %s: per kernel and grid size, durations in microseconds" % os.path.relpath(tr, path))
+        lines.append("%-56s %9s %6s %10s %10s %10s %10s" % ("kernel", "grid_x", "calls", "avg_us", "median_us",
+                                                            "min_us", "max_us"))
+        for (name, grid), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            lines.append("%-56s %9s %6d %10.3f %10.3f %10.3f %10.3f" % (
+                name[:56], grid, len(ds), sum(ds) / len(ds), statistics.median(ds), min(ds), max(ds)))
+    for s in sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)):
+        with open(s) as f:
+            rows = list(csv.DictReader(f))
+        lines.append("# %s: rocprofv3 --stats per kernel name" % os.path.relpath(s, path))
+        for r in rows:
+            lines.append("%-70s calls=%s avg_us=%.3f min_us=%.3f max_us=%.3f" % (
+                r.get("Name", "?")[:70], r.get("Calls"), float(r.get("AverageNs", 0)) / 1e3,
+                float(r.get("MinNs", 0)) / 1e3, float(r.get("MaxNs", 0)) / 1e3))
+    return "\n".join(lines)
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--summarize-rocprof", default=None)
+    args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        print(summarize_rocprof(args.summarize_rocprof))
+        return 0
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the decode mat-vec would "
+              "shard by output rows with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import routed_moe_matvec_amd as qg
+
+    torch.cuda.init()
+    stream = torch.cuda.Stream()
+    timer = Timer(stream)
+    step = DecodeStep(qg, torch)
+
+    # warmup: W eager steps, then the graph of K steps replayed once untimed
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step.step(i)
+    torch.cuda.synchronize()
+    g_steps = capture(step.step, args.steps, stream)
+    timer.run(g_steps.replay)
+    sec = timer.run(g_steps.replay)
+    ms_per_step = sec / args.steps * 1e3
+    value = step.step_bytes / (sec / args.steps) / 1e9
+
+    # dominant kernel: the 4096 x 8192 Q8_0 GEMV, timed alone over a rotation of weights
+    n_k = max(step.R, 100)
+    g_k = capture(step.out_gemv, n_k, stream)
+    timer.run(g_k.replay)
+    ksec = timer.run(g_k.replay) / n_k
+    achieved = step.out_gemv_bytes / ksec / 1e9
+    src_hash = kernel_source_hash()
+    traffic = load_traffic("qgemv_q8_0_4096x8192", src_hash)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "Q8_0 attention projections, batch 1: quantize + out 8192->4096 + quantize + paired "
+                        "4096->1024 & 4096->512 (one launch)",
+            "tokens_per_step": 1,
+            "algorithmic_bytes_per_step": step.step_bytes,
+            "weight_rotation_copies": step.R,
+            "us_per_step": round(ms_per_step * 1e3, 3),
+            "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "qgemv_q8_0 N=4096 K=8192 M=1",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(ksec * 1e6, 3),
+            "algorithmic_bytes_per_launch": step.out_gemv_bytes,
+            "source_hash": src_hash,
+        },
+    }
+    del g_steps, g_k
+    if not args.no_extra:
+        result["extra"] = extra_measurements(qg, torch, stream, timer)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(step)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

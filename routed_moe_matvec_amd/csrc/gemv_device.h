@@ -136,11 +136,12 @@ __device__ __forceinline__ float group_dot_q4k(const uint32_t (&w)[36], const in
 
 // ---------------------------------------------------------------- tile engine
 
-// Copy tile `tile` of matrix W (rows tile*rpt .. +rpt, clipped to N) into the
-// wave's LDS buffer.  Returns the number of rows in the tile.
+// Start copying tile `tile` of matrix W (rows tile*rpt .. +rpt, clipped to N)
+// into the wave's LDS buffer; the copy is left in flight (wait with
+// wait_vmem_all before reading).  Returns the number of rows in the tile.
 template <int FMT>
-__device__ __forceinline__ int load_tile_to_lds(const uint8_t *__restrict__ W, int N, const TileGeom &tg, int tile,
-                                                uint8_t *lds_wave) {
+__device__ __forceinline__ int issue_tile_to_lds(const uint8_t *__restrict__ W, int N, const TileGeom &tg, int tile,
+                                                 uint8_t *lds_wave) {
     constexpr int GB = GroupBytes<FMT>::value;
     const int lane = lane_id();
     const int row0 = tile * tg.rpt;
@@ -151,7 +152,6 @@ __device__ __forceinline__ int load_tile_to_lds(const uint8_t *__restrict__ W, i
         const int c = i * kWave + lane;
         if (c < nchunks) global_to_lds16(src + (size_t)c * 16, lds_wave + i * 1024);
     }
-    wait_vmem_all();
     return nrows;
 }
 
