@@ -83,7 +83,7 @@ extern "C" {
 /* device status word values (moe_routed_qgemv) */
 #define QG_DEV_OK 0
 #define QG_DEV_BAD_EXPERT 1  /* an expert id outside [0, E) */
-#define QG_DEV_NULL_EXPERT 2 /* a selected expert has a NULL weight pointer */
+#define QG_DEV_NULL_EXPERT 2 /* a selected expert has a NULL or misaligned weight pointer */
 
 /* weight formats */
 #define QG_FMT_Q8_0 0
@@ -159,7 +159,7 @@ size_t moe_routed_workspace_bytes(int T, int topk, int E, int D, int F);
 
 /* regions of the MoE workspace (byte offsets from moe_routed_workspace_layout) */
 #define QG_WS_NUNIQ 0    /* int32 [1]      number of distinct valid experts U */
-#define QG_WS_UNIQ 1     /* int32 [Ucap]   distinct expert ids, ascending */
+#define QG_WS_UNIQ 1     /* int32 [Ucap]   distinct usable expert ids, ascending */
 #define QG_WS_SLOT 2     /* int32 [P]      index in uniq of pair p's expert, -1 if invalid */
 #define QG_WS_PAIR_OFF 3 /* int32 [Ucap+1] CSR offsets into pairs */
 #define QG_WS_PAIRS 4    /* int32 [P]      pair indices grouped by expert, ascending within */
@@ -200,9 +200,10 @@ int moe_routed_workspace_layout(int T, int topk, int E, int D, int F, size_t *of
  * stays on the device.
  *
  * Data errors: an id outside [0, E) sets *d_status to QG_DEV_BAD_EXPERT, and
- * a selected expert with a NULL pointer sets QG_DEV_NULL_EXPERT (whichever
- * is found first is kept); such a pair contributes 0 to y and every other
- * pair is still computed.  *d_status is written with QG_DEV_OK first, on the
+ * a selected expert whose gate, up or down pointer is NULL or not 16-byte
+ * aligned sets QG_DEV_NULL_EXPERT (whichever is found first is kept); such a
+ * pair gets slot -1, contributes 0 to y, and every other pair is still
+ * computed.  Such an expert is left out of uniq.  *d_status is written with QG_DEV_OK first, on the
  * stream, so the caller reads it after synchronizing.
  *
  * Errors: QG_ERR_NULL (any pointer except unselected experts);

@@ -12,9 +12,6 @@
 namespace qg {
 
 constexpr int kGemvWaves = 4;
-// LDS for staged activations per workgroup (the weight tiles take
-// kGemvWaves * 64 * group bytes on top; Q8_0: 68 KiB, Q4_K: 36 KiB).
-constexpr int kActLdsBudget = 44 * 1024;
 
 struct GemvArgs {
     const uint8_t *W0;
@@ -33,52 +30,10 @@ struct GemvArgs {
     int32_t *isum;  // per-block sums of matrix 0 (test export), else unused
 };
 
-// Activations are staged in LDS as one record per 256-input group: 64 dwords
-// of quants, 8 block scales (+ 8 block sums for Q4_K), padded so that the
-// record stride is an odd multiple of 4 dwords.  Lanes of a wave read
-// different groups at the same offset; with this stride their 16-byte reads
-// fall in disjoint banks (a 256-byte stride would put them all in one).
-template <int FMT>
-struct ActRecord {
-    static constexpr int dwords = FMT == QG_FMT_Q4K ? 84 : 76;  // 80 + 4 / 72 + 4
-    static constexpr int bytes = dwords * 4;
-};
-
-template <int FMT>
-__host__ __device__ inline int act_lds_bytes_per_token(int K) {
-    return (K / kGroupWeights) * ActRecord<FMT>::bytes;
-}
-
-// Stage tokens [m0, m0 + mt) of the Q8 activation into padded LDS records
-// (whole workgroup; global -> VGPR -> LDS, 16 bytes per access).
-template <int FMT>
-__device__ __forceinline__ void stage_activations(const int8_t *__restrict__ qx, const float *__restrict__ dx,
-                                                  const int32_t *__restrict__ sx, int K, int m0, int mt,
-                                                  uint8_t *lds) {
-    constexpr int REC = ActRecord<FMT>::bytes;
-    const int gpr = K / kGroupWeights;
-    const int nq = mt * K / 16;  // 16-byte chunks of quants
-    const uint4 *q = reinterpret_cast<const uint4 *>(qx + (size_t)m0 * K);
-    for (int c = threadIdx.x; c < nq; c += kGemvWaves * kWave) {
-        const int tg = c >> 4;  // token * gpr + group
-        *reinterpret_cast<uint4 *>(lds + (size_t)tg * REC + (c & 15) * 16) = q[c];
-    }
-    const int ns = mt * gpr * 2;  // 16-byte chunks of scales (two per group)
-    const uint4 *d = reinterpret_cast<const uint4 *>(dx + (size_t)m0 * (K / 32));
-    const uint4 *su = reinterpret_cast<const uint4 *>(sx + (size_t)m0 * (K / 32));
-    for (int c = threadIdx.x; c < ns; c += kGemvWaves * kWave) {
-        uint8_t *rec = lds + (size_t)(c >> 1) * REC + 256 + (c & 1) * 16;
-        *reinterpret_cast<uint4 *>(rec) = d[c];
-        if (FMT == QG_FMT_Q4K) *reinterpret_cast<uint4 *>(rec + 32) = su[c];
-    }
-}
-
 template <int FMT, bool DEBUG_ISUM>
 __global__ __launch_bounds__(kGemvWaves *kWave) void qgemv_kernel(GemvArgs a) {
-    constexpr int GB = GroupBytes<FMT>::value;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
     int tile = blockIdx.x * kGemvWaves + wave;
     const bool second = tile >= a.nt0;
     if (second) tile -= a.nt0;
@@ -87,51 +42,16 @@ __global__ __launch_bounds__(kGemvWaves *kWave) void qgemv_kernel(GemvArgs a) {
     const uint8_t *W = second ? a.W1 : a.W0;
     float *y = second ? a.y1 : a.y0;
     const int N = second ? a.N1 : a.N0;
-    const TileGeom tg = a.tg;
-    const int K = a.K;
-    const int nb = K / 32;
-
-    uint8_t *lw = smem + wave * kWave * GB;
-    uint8_t *lact = smem + kGemvWaves * kWave * GB;
-    constexpr int REC = ActRecord<FMT>::bytes;
-
-    // 1. this wave's weight tile: HBM -> LDS, left in flight
-    int nrows = 0;
-    if (has_tile) nrows = issue_tile_to_lds<FMT>(W, N, tg, tile, lw);
-    const int r = lane >> tg.lsh;
-    const int g = lane & (tg.lpr - 1);
-    const bool valid = has_tile && g < tg.gpr && r < nrows;
-    const int row = tile * tg.rpt + r;
-    GroupRegs<FMT> regs;
-
-    for (int m0 = 0; m0 < a.M; m0 += a.mt) {
-        const int mt = min(a.mt, a.M - m0);
-        if (m0 > 0) __syncthreads();  // every wave is done with the previous chunk
-        // 2. the chunk's activation quants, scales (and block sums), shared by the workgroup
-        stage_activations<FMT>(a.qx, a.dx, a.sx, K, m0, mt, lact);
-        wait_vmem_all();  // this wave's weight tile has landed in LDS
-        __syncthreads();
-        if (m0 == 0 && valid) read_group<FMT>(lw + (r * tg.gpr + g) * GB, regs);
-
-        for (int mm = 0; mm < mt; ++mm) {
-            const int m = m0 + mm;
-            float p = 0.0f;
-            if (valid) {
-                int32_t isum_tmp[8];
-                const uint8_t *rec = lact + (size_t)(mm * tg.gpr + g) * REC;
-                p = group_dot<FMT>(regs, reinterpret_cast<const int8_t *>(rec),
-                                   reinterpret_cast<const float *>(rec + 256),
-                                   reinterpret_cast<const int32_t *>(rec + 288), DEBUG_ISUM ? isum_tmp : nullptr);
-                if (DEBUG_ISUM) {
-                    int32_t *o = a.isum + ((size_t)m * N + row) * nb + g * 8;
+    const int nb = a.K / 32;
+    int32_t *isum = a.isum;
+    gemv_tiles_workgroup<FMT, kGemvWaves, DEBUG_ISUM>(
+        W, N, a.K, a.tg, tile, has_tile, a.qx, a.dx, a.sx, a.M, a.mt, smem, [](int m) { return m; },
+        [=](int m, int row, float v) { y[(size_t)m * N + row] = v; },
+        [=](int m, int row, int g, const int32_t *s8) {
+            int32_t *o = isum + ((size_t)m * N + row) * nb + g * 8;
 #pragma unroll
-                    for (int b = 0; b < 8; ++b) o[b] = isum_tmp[b];
-                }
-            }
-            p = row_reduce(p, tg.lpr);
-            if (!DEBUG_ISUM && valid && g == 0) y[(size_t)m * N + row] = p;
-        }
-    }
+            for (int b = 0; b < 8; ++b) o[b] = s8[b];
+        });
 }
 
 static inline bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; }
@@ -139,9 +59,8 @@ static inline bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; 
 template <int FMT, bool DEBUG_ISUM>
 static int launch_gemv(GemvArgs &a, hipStream_t stream) {
     constexpr int GB = GroupBytes<FMT>::value;
-    const int per_token = act_lds_bytes_per_token<FMT>(a.K);
-    a.mt = max(1, min(a.M, kActLdsBudget / per_token));
-    const size_t lds = (size_t)kGemvWaves * kWave * GB + (size_t)a.mt * per_token;
+    a.mt = tokens_per_chunk<FMT>(a.K, a.M);
+    const size_t lds = gemv_lds_bytes<FMT>(kGemvWaves, a.K, a.mt);
     static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_kernel<FMT, DEBUG_ISUM>),

@@ -202,4 +202,122 @@ __device__ __forceinline__ float row_reduce(float p, int lpr) {
     return p;
 }
 
+
+// ---------------------------------------------------------------- activation staging
+
+// LDS for staged activations per workgroup (the weight tiles take
+// waves * 64 * group bytes on top; 4 waves: Q8_0 68 KiB, Q4_K 36 KiB).
+constexpr int kActLdsBudget = 44 * 1024;
+
+// Activations are staged in LDS as one record per 256-input group: 64 dwords
+// of quants, 8 block scales (+ 8 block sums for Q4_K), padded so that the
+// record stride is an odd multiple of 4 dwords.  Lanes of a wave read
+// different groups at the same offset; with this stride their 16-byte reads
+// fall in disjoint banks (a 256-byte stride would put them all in one).
+template <int FMT>
+struct ActRecord {
+    static constexpr int dwords = FMT == QG_FMT_Q4K ? 84 : 76;  // 80 + 4 / 72 + 4
+    static constexpr int bytes = dwords * 4;
+};
+
+template <int FMT>
+__host__ __device__ inline int act_lds_bytes_per_token(int K) {
+    return (K / kGroupWeights) * ActRecord<FMT>::bytes;
+}
+
+template <int FMT>
+inline int tokens_per_chunk(int K, int M) {
+    return max(1, min(min(M, kMaxChunkTokens), kActLdsBudget / act_lds_bytes_per_token<FMT>(K)));
+}
+
+template <int FMT>
+inline size_t gemv_lds_bytes(int waves, int K, int mt) {
+    return (size_t)waves * kWave * GroupBytes<FMT>::value + (size_t)mt * act_lds_bytes_per_token<FMT>(K) +
+           (size_t)kMaxChunkTokens * sizeof(int);
+}
+
+// Stage tokens m0 .. m0+mt-1 (activation rows rows_lds[0..mt) of qx/dx/sx)
+// into padded LDS records (whole workgroup; global -> VGPR -> LDS, 16 bytes
+// per access).
+template <int FMT, int WAVES>
+__device__ __forceinline__ void stage_activations(const int8_t *__restrict__ qx, const float *__restrict__ dx,
+                                                  const int32_t *__restrict__ sx, int K, int mt,
+                                                  const int *rows_lds, uint8_t *lds) {
+    constexpr int REC = ActRecord<FMT>::bytes;
+    const int gpr = K / kGroupWeights;
+    const int cpt = K / 16;  // 16-byte chunks of quants per token
+    for (int c = threadIdx.x; c < mt * cpt; c += WAVES * kWave) {
+        const int mm = c / cpt;
+        const int w = c - mm * cpt;
+        const uint4 *q = reinterpret_cast<const uint4 *>(qx + (size_t)rows_lds[mm] * K);
+        *reinterpret_cast<uint4 *>(lds + (size_t)(mm * gpr + (w >> 4)) * REC + (w & 15) * 16) = q[w];
+    }
+    const int spt = gpr * 2;  // 16-byte chunks of scales per token
+    for (int c = threadIdx.x; c < mt * spt; c += WAVES * kWave) {
+        const int mm = c / spt;
+        const int w = c - mm * spt;
+        const size_t src = (size_t)rows_lds[mm] * (K / 32) / 4 + w;  // in uint4 units
+        uint8_t *rec = lds + (size_t)(mm * gpr + (w >> 1)) * REC + 256 + (w & 1) * 16;
+        *reinterpret_cast<uint4 *>(rec) = reinterpret_cast<const uint4 *>(dx)[src];
+        if (FMT == QG_FMT_Q4K) *reinterpret_cast<uint4 *>(rec + 32) = reinterpret_cast<const uint4 *>(sx)[src];
+    }
+}
+
+// ---------------------------------------------------------------- workgroup engine
+
+// One workgroup of WAVES waves; each wave owns weight tile `tile` of W (if
+// has_tile).  The tile is copied HBM -> LDS and kept; the M tokens are
+// processed in chunks of mt_max, each chunk staged once in LDS for the whole
+// workgroup.  token_row(m) gives the activation row of token m; out(m, row, v)
+// stores one result; isum_out(m, row, g, sums8) receives the exact block sums
+// when DEBUG_ISUM.  Every wave of the workgroup must call this (barriers).
+template <int FMT, int WAVES, bool DEBUG_ISUM, class TokenRow, class Out, class IsumOut>
+__device__ __forceinline__ void gemv_tiles_workgroup(const uint8_t *__restrict__ W, int N, int K, const TileGeom &tg,
+                                                     int tile, bool has_tile, const int8_t *qx, const float *dx,
+                                                     const int32_t *sx, int M, int mt_max, uint8_t *smem,
+                                                     TokenRow token_row, Out out, IsumOut isum_out) {
+    constexpr int GB = GroupBytes<FMT>::value;
+    constexpr int REC = ActRecord<FMT>::bytes;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    uint8_t *lw = smem + wave * kWave * GB;
+    uint8_t *lact = smem + WAVES * kWave * GB;
+    int *lrows = reinterpret_cast<int *>(lact + (size_t)mt_max * act_lds_bytes_per_token<FMT>(K));
+
+    // 1. this wave's weight tile: HBM -> LDS, left in flight
+    int nrows = 0;
+    if (has_tile) nrows = issue_tile_to_lds<FMT>(W, N, tg, tile, lw);
+    const int r = lane >> tg.lsh;
+    const int g = lane & (tg.lpr - 1);
+    const bool valid = has_tile && g < tg.gpr && r < nrows;
+    const int row = tile * tg.rpt + r;
+    GroupRegs<FMT> regs;
+
+    for (int m0 = 0; m0 < M; m0 += mt_max) {
+        const int mt = min(mt_max, M - m0);
+        if (m0 > 0) __syncthreads();  // every wave is done with the previous chunk
+        for (int i = threadIdx.x; i < mt; i += WAVES * kWave) lrows[i] = token_row(m0 + i);
+        __syncthreads();
+        // 2. the chunk's activation quants, scales (and block sums), shared by the workgroup
+        stage_activations<FMT, WAVES>(qx, dx, sx, K, mt, lrows, lact);
+        wait_vmem_all();  // this wave's weight tile has landed in LDS
+        __syncthreads();
+        if (m0 == 0 && valid) read_group<FMT>(lw + (r * tg.gpr + g) * GB, regs);
+
+        for (int mm = 0; mm < mt; ++mm) {
+            float p = 0.0f;
+            if (valid) {
+                int32_t isum_tmp[8];
+                const uint8_t *rec = lact + (size_t)(mm * tg.gpr + g) * REC;
+                p = group_dot<FMT>(regs, reinterpret_cast<const int8_t *>(rec),
+                                   reinterpret_cast<const float *>(rec + 256),
+                                   reinterpret_cast<const int32_t *>(rec + 288), DEBUG_ISUM ? isum_tmp : nullptr);
+                if (DEBUG_ISUM) isum_out(m0 + mm, row, g, isum_tmp);
+            }
+            p = row_reduce(p, tg.lpr);
+            if (!DEBUG_ISUM && valid && g == 0) out(m0 + mm, row, p);
+        }
+    }
+}
+
 }  // namespace qg
