@@ -1,0 +1,92 @@
+"""The C-ABI library without a GPU: it loads, exports every function the public
+header declares, and its host-side logic (argument checks, workspace sizing,
+status strings) behaves as documented.  No call here reaches a kernel launch:
+every checked call fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = re.sub(r"#[^\n]*", " ", src)
+    names = re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{}]*\)\s*;", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import routed_moe_matvec_amd as qg
+    return ctypes.CDLL(qg.library_path())
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["quantize_act_q8", "qgemv_q8_0", "qgemv_q4k", "qgemv_paired", "moe_routed_qgemv",
+                 "moe_routed_workspace_bytes", "moe_routed_workspace_layout", "qgemm_prefill", "qg_status_string",
+                 "qgemv_debug_block_isums"]:
+        assert want in names, want
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_the_header():
+    import routed_moe_matvec_amd as qg
+    for n in declared_functions():
+        assert callable(getattr(qg, n, None)), n
+
+
+def test_status_strings(lib):
+    import routed_moe_matvec_amd as qg
+    for code in range(-6, 1):
+        assert qg.qg_status_string(code) not in ("", "unknown status")
+    assert qg.qg_status_string(-77) == "unknown status"
+
+
+def test_host_validation_without_gpu(lib):
+    """Rejected calls return their code before touching the device."""
+    vp = ctypes.c_void_p
+    fake = vp(1 << 40)  # never dereferenced: every call below fails validation first
+    f = lib.qgemv_q8_0
+    f.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp]
+    assert f(None, 8, 512, fake, fake, 1, fake, None) == -1
+    assert f(fake, 8, 300, fake, fake, 1, fake, None) == -2
+    assert f(fake, 8, 512, fake, fake, 33, fake, None) == -2
+    assert f(fake, 0, 512, fake, fake, 1, fake, None) == -2
+    assert f(vp((1 << 40) + 8), 8, 512, fake, fake, 1, fake, None) == -3
+    q = lib.quantize_act_q8
+    q.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    assert q(fake, 1, 40, fake, fake, fake, None) == -2
+    assert q(fake, 1, 64, None, fake, fake, None) == -1
+    p = lib.qgemm_prefill
+    p.argtypes = [ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp]
+    assert p(0, fake, 8, 512, fake, 4, fake, None) == -4
+
+
+def test_moe_workspace_sizing():
+    import routed_moe_matvec_amd as qg
+    T, topk, E, D, F = 8, 6, 256, 4096, 2048
+    nbytes = qg.moe_routed_workspace_bytes(T, topk, E, D, F)
+    lay = qg.moe_routed_workspace_layout(T, topk, E, D, F)
+    P, Ucap = T * topk, min(T * topk, E)
+    sizes = {"NUNIQ": 4, "UNIQ": 4 * Ucap, "SLOT": 4 * P, "PAIR_OFF": 4 * (Ucap + 1), "PAIRS": 4 * P,
+             "G": 4 * P * F, "V": 4 * P * F, "H": 4 * P * F, "HQ": P * F, "HD": 4 * P * F // 32,
+             "HS": 4 * P * F // 32, "O": 4 * P * D}
+    names = qg.WS_REGIONS
+    for a, b in zip(names, names[1:]):
+        assert lay[b] >= lay[a] + sizes[a] and lay[b] % 256 == 0
+    assert nbytes >= lay["O"] + sizes["O"]
+    assert qg.moe_routed_workspace_bytes(8, 6, 256, 4000, 2048) == 0
+    assert qg.moe_routed_workspace_bytes(2000, 6, 256, 4096, 2048) == 0  # more than 8192 pairs
+    with pytest.raises(qg.QGError):
+        qg.moe_routed_workspace_layout(0, 6, 256, 4096, 2048)
