@@ -238,6 +238,72 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
         torch.cuda.empty_cache()
         out[label] = res
 
+    def moe_rate(key, n_sets):
+        w = synth.WORKLOADS[key]
+        E, D, F, T, topk = w["E"], w["D"], w["F"], w["T"], w["topk"]
+        g = synth.rng(w["seed"])
+        # two full expert pools, generated expert by expert straight to the device
+        pools = []
+        for _ in range(2):
+            pool = [[], [], []]
+            for e in range(E):
+                for lst, (n, k) in zip(pool, ((F, D), (F, D), (D, F))):
+                    lst.append(torch.from_numpy(synth.q4k_weight(g, n, k)).to(dev))
+            pools.append([qg.pointer_table(lst, dev) for lst in pool] + [pool])
+        draw = synth.moe_ids_zipf if w["ids"] == "zipf" else synth.moe_ids_uniform
+        ids = [draw(g, T, E, topk) for _ in range(n_sets)]
+        rws = [torch.from_numpy(synth.routing_weights(g, T, topk)).to(dev) for _ in range(n_sets)]
+        xs = [torch.from_numpy(synth.activations(g, T, D)).to(dev) for _ in range(n_sets)]
+        ids_d = [torch.from_numpy(i).to(dev) for i in ids]
+        qx = torch.empty(T, D, dtype=torch.int8, device=dev)
+        dx = torch.empty(T, D // 32, dtype=torch.float32, device=dev)
+        sx = torch.empty(T, D // 32, dtype=torch.int32, device=dev)
+        y = torch.empty(T, D, dtype=torch.float32, device=dev)
+        nbytes = qg.moe_routed_workspace_bytes(T, topk, E, D, F)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+
+        def call(i):
+            k = i % n_sets
+            pool = pools[i % 2]
+            qg.quantize_act_q8(xs[k], T, D, qx, dx, sx)
+            qg.moe_routed_qgemv(qx, dx, sx, T, D, F, E, topk, ids_d[k], rws[k], pool[0], pool[1], pool[2], y, ws,
+                                nbytes, status)
+
+        n = 2 * n_sets
+        gr = capture(call, n, stream)
+        timer.run(gr.replay)
+        sec = timer.run(gr.replay) / n
+        expert_bytes = 2 * F * (D // 256) * 144 + D * (F // 256) * 144
+        uniq = np.mean([len(np.unique(i)) for i in ids])
+        byts = uniq * expert_bytes + T * D * 4 * 2 + T * topk * 8
+        out["moe_" + key.split("_", 1)[1]] = {
+            "tokens_per_s": round(T / sec, 1), "us_per_call": round(sec * 1e6, 3), "mean_distinct_experts": float(uniq),
+            "GB_s": round(byts / sec / 1e9, 1), "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4),
+            "includes": "quantize_act_q8 of the T tokens + moe_routed_qgemv (5 launches)"}
+        del gr, pools, ws
+        torch.cuda.empty_cache()
+
+    def prefill_rate():
+        w = synth.WORKLOADS["q4k_prefill_512x8192x4096"]
+        g = synth.rng(w["seed"])
+        N, K, M = w["N"], w["K"], w["M"]
+        W_host = synth.q4k_weight(g, N, K)
+        R = rotation_count(W_host.nbytes)
+        base = torch.from_numpy(W_host).to(dev)
+        copies = [base] + [base.clone() for _ in range(R - 1)]
+        xb = torch.from_numpy(synth.bf16_activations(g, M, K).view(np.int16)).to(dev)
+        y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        gr = capture(lambda i: qg.qgemm_prefill(qg.FMT_Q4K, copies[i % R], N, K, xb, M, y), R, stream)
+        timer.run(gr.replay)
+        sec = timer.run(gr.replay) / R
+        flops = 2.0 * M * N * K
+        out["prefill_q4k_512x8192x4096"] = {
+            "us": round(sec * 1e6, 3), "TFLOP_s": round(flops / sec / 1e12, 1),
+            "mfma_frac": round(flops / sec / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4)}
+        del gr, copies, base
+        torch.cuda.empty_cache()
+
     g = synth.rng(0)
     w = synth.WORKLOADS["q8_0_512x1024"]
     gemv_rate(0, synth.q8_0_weight(g, w["N"], w["K"]), w["N"], w["K"], [1], "q8_0_512x1024")
@@ -246,6 +312,10 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
     w = synth.WORKLOADS["q8_0_16384x4096"]
     gemv_rate(0, synth.q8_0_weight(synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], list(w["Ms"]),
               "q8_0_16384x4096")
+    prefill_rate()
+    moe_rate("moe_e256_t1", 16)
+    moe_rate("moe_e256_t8", 16)
+    moe_rate("moe_e384_t64_zipf", 4)
     return out
 
 
