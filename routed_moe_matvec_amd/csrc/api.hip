@@ -1,5 +1,6 @@
 // Status strings and small host-side helpers of libqgemv.
 #include "common.h"
+#include "gemv_device.h"
 
 extern "C" const char *qg_status_string(int status) {
     switch (status) {
@@ -14,3 +15,20 @@ extern "C" const char *qg_status_string(int status) {
     }
     return "unknown status";
 }
+
+namespace qg {
+
+// Compute units of the current device, queried once per device.
+int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+}  // namespace qg

@@ -16,8 +16,6 @@ constexpr int kWave = 64;
 // K % 256 == 0 are whole numbers of groups and stay 16-byte aligned.
 constexpr int kGroupWeights = 256;
 
-// Largest number of tokens staged in LDS at once by the GEMV engine.
-constexpr int kMaxChunkTokens = 64;
 
 template <int FMT>
 struct GroupBytes;

@@ -11,12 +11,12 @@
 
 namespace qg {
 
-constexpr int kGemvWaves = 4;
+constexpr int kGemvWaves = 8;
 
 struct GemvArgs {
     const uint8_t *W0;
     float *y0;
-    int N0, nt0;
+    int N0, nt0, nwg0;  // rows, tiles, workgroups of matrix 0
     const uint8_t *W1;
     float *y1;
     int N1, nt1;
@@ -27,52 +27,76 @@ struct GemvArgs {
     const int32_t *sx;
     int M;
     int mt;         // tokens staged in LDS per chunk
+    int tpw;        // tiles per wave
     int32_t *isum;  // per-block sums of matrix 0 (test export), else unused
 };
 
-template <int FMT, bool DEBUG_ISUM>
+template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE>
 __global__ __launch_bounds__(kGemvWaves *kWave) void qgemv_kernel(GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int wave = threadIdx.x / kWave;
-    int tile = blockIdx.x * kGemvWaves + wave;
-    const bool second = tile >= a.nt0;
-    if (second) tile -= a.nt0;
-    // a wave without a tile still takes part in the workgroup's barriers
-    const bool has_tile = !second || tile < a.nt1;
+    // workgroups [0, nwg0) cover matrix 0, the rest matrix 1 (paired call)
+    const bool second = (int)blockIdx.x >= a.nwg0;
+    const int wg = second ? (int)blockIdx.x - a.nwg0 : (int)blockIdx.x;
     const uint8_t *W = second ? a.W1 : a.W0;
     float *y = second ? a.y1 : a.y0;
     const int N = second ? a.N1 : a.N0;
+    const int nt = second ? a.nt1 : a.nt0;
     const int nb = a.K / 32;
     int32_t *isum = a.isum;
-    gemv_tiles_workgroup<FMT, kGemvWaves, DEBUG_ISUM>(
-        W, N, a.K, a.tg, tile, has_tile, a.qx, a.dx, a.sx, a.M, a.mt, smem, [](int m) { return m; },
-        [=](int m, int row, float v) { y[(size_t)m * N + row] = v; },
-        [=](int m, int row, int g, const int32_t *s8) {
-            int32_t *o = isum + ((size_t)m * N + row) * nb + g * 8;
+    gemv_workgroup<FMT, NB, kGemvWaves, DEBUG_ISUM, PIPE, ONE>(
+        W, N, a.K, a.tg, wg * kGemvWaves * a.tpw, a.tpw, nt, a.qx, a.dx, a.sx, a.M, a.mt, smem,
+        [](int m) { return m; }, [=](int m, int row, float v) { y[(size_t)m * N + row] = v; },
+        [=](int m, int row, int unit, const int32_t *s) {
+            int32_t *o = isum + ((size_t)m * N + row) * nb + unit * NB;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) o[b] = s8[b];
+            for (int b = 0; b < NB; ++b) o[b] = s[b];
         });
 }
 
 static inline bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; }
 
-template <int FMT, bool DEBUG_ISUM>
-static int launch_gemv(GemvArgs &a, hipStream_t stream) {
-    constexpr int GB = GroupBytes<FMT>::value;
-    a.mt = tokens_per_chunk<FMT>(a.K, a.M);
-    const size_t lds = gemv_lds_bytes<FMT>(kGemvWaves, a.K, a.mt);
+template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE>
+static int launch_kernel(const GemvArgs &a, int grid, size_t lds, hipStream_t stream) {
     static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_kernel<FMT, DEBUG_ISUM>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kGemvWaves * kWave * GB + kActLdsBudget + 16 * 1024) != hipSuccess)
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
             return QG_ERR_LAUNCH;
         attr_set = true;
     }
-    const int tiles = a.nt0 + a.nt1;
-    const int grid = (tiles + kGemvWaves - 1) / kGemvWaves;
-    hipLaunchKernelGGL((qgemv_kernel<FMT, DEBUG_ISUM>), dim3(grid), dim3(kGemvWaves * kWave), lds, stream, a);
+    hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE>), dim3(grid), dim3(kGemvWaves * kWave), lds, stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+template <int FMT, int NB, bool DEBUG_ISUM>
+static int launch_gemv(GemvArgs &a, hipStream_t stream) {
+    using U = Unit<FMT, NB>;
+    constexpr int threads = kGemvWaves * kWave;
+    a.tg = make_tile_geom<U>(a.K);
+    a.nt0 = (a.N0 + a.tg.rpt - 1) / a.tg.rpt;
+    a.nt1 = a.W1 ? (a.N1 + a.tg.rpt - 1) / a.tg.rpt : 0;
+    a.mt = tokens_per_chunk<U>(a.K, a.M, threads);
+    const size_t lds = gemv_lds_bytes<U>(kGemvWaves, a.K, a.mt);
+    // about one round of resident waves (LDS bounds the workgroups per CU)
+    const int wg_per_cu = max(1, min(4, (int)((160 * 1024) / lds)));
+    // (the 8-block Q8_0 unit keeps one tile register set: two would spill)
+    a.tpw = tiles_per_wave(a.nt0 + a.nt1, device_cu_count() * wg_per_cu * kGemvWaves,
+                           a.M <= a.mt && !(FMT == QG_FMT_Q8_0 && NB == 8));
+    const int per_wg = kGemvWaves * a.tpw;
+    a.nwg0 = (a.nt0 + per_wg - 1) / per_wg;
+    const int grid = a.nwg0 + (a.nt1 + per_wg - 1) / per_wg;
+    if (a.M == 1)
+        return a.tpw > 1 ? launch_kernel<FMT, NB, DEBUG_ISUM, true, true>(a, grid, lds, stream)
+                         : launch_kernel<FMT, NB, DEBUG_ISUM, false, true>(a, grid, lds, stream);
+    return a.tpw > 1 ? launch_kernel<FMT, NB, DEBUG_ISUM, true, false>(a, grid, lds, stream)
+                     : launch_kernel<FMT, NB, DEBUG_ISUM, false, false>(a, grid, lds, stream);
+}
+
+template <bool DEBUG_ISUM>
+static int launch_fmt(int fmt, GemvArgs &a, hipStream_t stream) {
+    if (fmt == QG_FMT_Q4K) return launch_gemv<QG_FMT_Q4K, 8, DEBUG_ISUM>(a, stream);
+    if (a.K <= 8192) return launch_gemv<QG_FMT_Q8_0, 4, DEBUG_ISUM>(a, stream);
+    return launch_gemv<QG_FMT_Q8_0, 8, DEBUG_ISUM>(a, stream);
 }
 
 static int check_common(int N, int K, int M) {
@@ -95,28 +119,21 @@ static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2
         misaligned(y2) || misaligned(sx) || misaligned(isum))
         return QG_ERR_ALIGN;
     GemvArgs a{};
-    a.tg = make_tile_geom(K);
     a.K = K;
     a.W0 = (const uint8_t *)W1;
     a.y0 = y1;
     a.N0 = N1;
-    a.nt0 = (N1 + a.tg.rpt - 1) / a.tg.rpt;
     if (W2) {
         a.W1 = (const uint8_t *)W2;
         a.y1 = y2;
         a.N1 = N2;
-        a.nt1 = (N2 + a.tg.rpt - 1) / a.tg.rpt;
     }
     a.qx = qx;
     a.dx = dx;
     a.sx = sx;
     a.M = M;
     a.isum = isum;
-    if (isum) {
-        return fmt == QG_FMT_Q8_0 ? launch_gemv<QG_FMT_Q8_0, true>(a, stream)
-                                  : launch_gemv<QG_FMT_Q4K, true>(a, stream);
-    }
-    return fmt == QG_FMT_Q8_0 ? launch_gemv<QG_FMT_Q8_0, false>(a, stream) : launch_gemv<QG_FMT_Q4K, false>(a, stream);
+    return isum ? launch_fmt<true>(fmt, a, stream) : launch_fmt<false>(fmt, a, stream);
 }
 
 }  // namespace qg

@@ -1,66 +1,76 @@
-// Block-quantized weight x Q8 activation: the per-lane group decoders and the
-// wave-level tile engine shared by the dense GEMV and the routed-MoE kernels.
+// Block-quantized weight x Q8 activation: per-lane unit decoders and the
+// workgroup-level tile engine shared by the dense GEMV and the routed-MoE
+// kernels.
 //
 // Work decomposition (MI355X-first, not taken from the pages' kernels):
-//   * A "group" is 256 consecutive weights of one row: 8 Q8_0 blocks (272 B)
-//     or one Q4_K superblock (144 B).  One lane decodes one group.
-//   * A wave owns a "tile": R whole rows, R = 64 / lanes_per_row, where
-//     lanes_per_row is K/256 rounded up to a power of two (<= 64).  The tile
-//     is contiguous in memory, so the wave copies it HBM -> LDS with
-//     16-byte direct-to-LDS loads: every load instruction moves 1 KiB of
-//     consecutive bytes (fully coalesced), no VGPRs are used for staging.
-//   * Each lane then reads its own group from LDS (16-byte reads; the 34-byte
-//     Q8_0 blocks are re-aligned in registers with byte-align ops), forms the
-//     per-block int32 sums with 4-way int8 dot products against the Q8
-//     activation, scales them in fp32, and the lanes of a row combine their
-//     partial sums with a fixed xor-butterfly (deterministic, the same order
-//     for every token and every call).
+//   * A "unit" is the run of one row's weights that one lane decodes:
+//     4 Q8_0 blocks (128 weights, 136 B) when K <= 8192, 8 Q8_0 blocks (256
+//     weights, 272 B) for larger K, or one Q4_K superblock (256 weights, 144 B).
+//   * A wave owns a "tile" of whole rows, at most 64 units (8.5-17 KiB): rows
+//     are contiguous in memory, so the wave reads the tile with 16-byte loads
+//     in which every instruction moves 1 KiB of consecutive bytes.  Loads are
+//     non-temporal (the weights are streamed once) and land in VGPRs, so the
+//     compiler tracks their completion exactly; a wave keeps up to two tiles
+//     in flight in two register sets and decodes one while the next arrives.
+//   * To hand every lane its own unit, the wave writes the tile to a private
+//     LDS buffer and reads its unit back (8/16-byte LDS reads; the 34-byte
+//     Q8_0 blocks are re-aligned in registers with byte-align ops).
+//   * The per-block int32 sums come from 4-way int8 dot products against the
+//     Q8 activation, which the workgroup stages once in LDS as padded
+//     per-unit records; they are scaled in fp32 with explicit fma, and the
+//     lanes of a row combine their partial sums with a fixed xor butterfly
+//     (deterministic, the same order for every token and every call).
 #pragma once
 
 #include "common.h"
 
 namespace qg {
 
-struct TileGeom {
-    int gpr;  // groups per row = K / 256
-    int lpr;  // lanes per row (power of two >= gpr, <= 64)
-    int lsh;  // log2(lpr)
-    int rpt;  // rows per tile = 64 / lpr
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- units
+
+template <int FMT, int NB>
+struct Unit;
+// Q8_0, NB blocks of 34 bytes per lane
+template <int NB>
+struct Unit<QG_FMT_Q8_0, NB> {
+    static constexpr int blocks = NB;
+    static constexpr int weights = 32 * NB;
+    static constexpr int bytes = 34 * NB;
+    static constexpr int dwords = 17 * NB / 2;
+    // activation record: quants, then NB scales; stride an odd multiple of 4 dwords
+    static constexpr int rec_dwords = NB == 4 ? 36 : 76;
+};
+template <>
+struct Unit<QG_FMT_Q4K, 8> {
+    static constexpr int blocks = 8;
+    static constexpr int weights = 256;
+    static constexpr int bytes = 144;
+    static constexpr int dwords = 36;
+    static constexpr int rec_dwords = 84;  // 64 quants + 8 scales + 8 block sums + 4 pad
 };
 
-inline TileGeom make_tile_geom(int K) {
-    TileGeom t;
-    t.gpr = K / kGroupWeights;
-    t.lpr = 1;
-    t.lsh = 0;
-    while (t.lpr < t.gpr) {
-        t.lpr <<= 1;
-        t.lsh += 1;
-    }
-    t.rpt = kWave / t.lpr;
-    return t;
-}
+template <class U>
+struct UnitRegs {
+    uint32_t w[U::dwords];
+};
 
-// ---------------------------------------------------------------- decoders
-
-// One lane, one Q8_0 group (8 blocks, 68 dwords in w) against one token's
-// activation for the same 256 inputs: qx8 = 64 dwords of int8 quants, dxg =
-// the 8 block scales.  Returns sum_b (dw_b * dx_b) * isum_b in fp32 (blocks in
-// order).  If isum_out is non-null the 8 exact block sums are stored there.
-__device__ __forceinline__ float group_dot_q8_0(const uint32_t (&w)[68], const int8_t *__restrict__ qx8,
-                                                const float *__restrict__ dxg, int32_t *isum_out) {
-    const uint4 *qv = reinterpret_cast<const uint4 *>(qx8);
-    const float4 dlo = reinterpret_cast<const float4 *>(dxg)[0];
-    const float4 dhi = reinterpret_cast<const float4 *>(dxg)[1];
-    const float dx[8] = {dlo.x, dlo.y, dlo.z, dlo.w, dhi.x, dhi.y, dhi.z, dhi.w};
+// Q8_0 blocks of a unit against one token's record; returns
+// sum_b (dw_b * dx_b) * isum_b in fp32 in block order.
+template <int NB>
+__device__ __forceinline__ float unit_dot_q8_0(const uint32_t (&w)[17 * NB / 2], const uint8_t *rec,
+                                               int32_t *isum_out) {
+    const u32x4 *qv = reinterpret_cast<const u32x4 *>(rec);
+    const float *dxp = reinterpret_cast<const float *>(rec + 32 * NB);
     float acc = 0.0f;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const int byte0 = 34 * b;   // block start inside the group
+    for (int b = 0; b < NB; ++b) {
+        const int byte0 = 34 * b;   // block start inside the unit
         const int dw0 = byte0 / 4;  // dword holding the fp16 scale
         const uint32_t sbits = (b & 1) ? (w[dw0] >> 16) : (w[dw0] & 0xffffu);
         const float dwt = half_bits_to_float(sbits);
-        const uint4 q0 = qv[2 * b], q1 = qv[2 * b + 1];
+        const u32x4 q0 = qv[2 * b], q1 = qv[2 * b + 1];
         const uint32_t qa[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
         int isum = 0;
 #pragma unroll
@@ -73,12 +83,12 @@ __device__ __forceinline__ float group_dot_q8_0(const uint32_t (&w)[68], const i
             isum = sdot4(wq, qa[k], isum);
         }
         if (isum_out) isum_out[b] = isum;
-        acc = fmaf_exact((float)isum, dwt * dx[b], acc);
+        acc = fmaf_exact((float)isum, dwt * dxp[b], acc);
     }
     return acc;
 }
 
-// 6-bit field f (0..15) of the 96-bit little-endian string in s[0..2].
+// 6-bit field f (0..15) of the 96-bit little-endian string in s0..s2.
 __device__ __forceinline__ uint32_t q4k_field(const uint32_t s0, const uint32_t s1, const uint32_t s2, int f) {
     const int bit = 6 * f;
     const int word = bit >> 5;
@@ -89,28 +99,21 @@ __device__ __forceinline__ uint32_t q4k_field(const uint32_t s0, const uint32_t 
     return v & 63u;
 }
 
-// One lane, one Q4_K superblock (36 dwords in w) against one token's
-// activation for the same 256 inputs (qx8: 64 dwords, dxg/sxg: 8 scales and
-// block sums).  Per sub-block j:
+// One Q4_K superblock against one token's record (64 dwords of quants, 8
+// scales, 8 block sums).  Per sub-block j:
 //   dx_j * (d*sc_j * isum_j - dmin*m_j * sx_j)
 // with d*sc_j and dmin*m_j exact in fp32 (11-bit x 6-bit products).
-__device__ __forceinline__ float group_dot_q4k(const uint32_t (&w)[36], const int8_t *__restrict__ qx8,
-                                               const float *__restrict__ dxg, const int32_t *__restrict__ sxg,
-                                               int32_t *isum_out) {
-    const uint4 *qv = reinterpret_cast<const uint4 *>(qx8);
-    const float4 dlo = reinterpret_cast<const float4 *>(dxg)[0];
-    const float4 dhi = reinterpret_cast<const float4 *>(dxg)[1];
-    const int4 slo = reinterpret_cast<const int4 *>(sxg)[0];
-    const int4 shi = reinterpret_cast<const int4 *>(sxg)[1];
-    const float dx[8] = {dlo.x, dlo.y, dlo.z, dlo.w, dhi.x, dhi.y, dhi.z, dhi.w};
-    const int sx[8] = {slo.x, slo.y, slo.z, slo.w, shi.x, shi.y, shi.z, shi.w};
+__device__ __forceinline__ float unit_dot_q4k(const uint32_t (&w)[36], const uint8_t *rec, int32_t *isum_out) {
+    const u32x4 *qv = reinterpret_cast<const u32x4 *>(rec);
+    const float *dxp = reinterpret_cast<const float *>(rec + 256);
+    const int32_t *sxp = reinterpret_cast<const int32_t *>(rec + 288);
     const float d = half_bits_to_float(w[0]);
     const float dmin = half_bits_to_float(w[0] >> 16);
     float acc = 0.0f;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const uint4 a0 = qv[4 * p], a1 = qv[4 * p + 1];  // sub-block 2p
-        const uint4 b0 = qv[4 * p + 2], b1 = qv[4 * p + 3];  // sub-block 2p+1
+        const u32x4 a0 = qv[4 * p], a1 = qv[4 * p + 1];      // sub-block 2p
+        const u32x4 b0 = qv[4 * p + 2], b1 = qv[4 * p + 3];  // sub-block 2p+1
         const uint32_t qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
         const uint32_t qb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
         int ia = 0, ib = 0;
@@ -127,73 +130,170 @@ __device__ __forceinline__ float group_dot_q4k(const uint32_t (&w)[36], const in
             if (isum_out) isum_out[j] = isum;
             const float a = d * (float)q4k_field(w[1], w[2], w[3], j);
             const float bm = dmin * (float)q4k_field(w[1], w[2], w[3], 8 + j);
-            const float inner = fmaf_exact(a, (float)isum, -(bm * (float)sx[j]));
-            acc = fmaf_exact(inner, dx[j], acc);
+            const float inner = fmaf_exact(a, (float)isum, -(bm * (float)sxp[j]));
+            acc = fmaf_exact(inner, dxp[j], acc);
         }
     }
     return acc;
 }
 
-// ---------------------------------------------------------------- tile engine
-
-// Start copying tile `tile` of matrix W (rows tile*rpt .. +rpt, clipped to N)
-// into the wave's LDS buffer; the copy is left in flight (wait with
-// wait_vmem_all before reading).  Returns the number of rows in the tile.
-template <int FMT>
-__device__ __forceinline__ int issue_tile_to_lds(const uint8_t *__restrict__ W, int N, const TileGeom &tg, int tile,
-                                                 uint8_t *lds_wave) {
-    constexpr int GB = GroupBytes<FMT>::value;
-    const int lane = lane_id();
-    const int row0 = tile * tg.rpt;
-    const int nrows = min(tg.rpt, N - row0);
-    const uint8_t *src = W + (size_t)row0 * tg.gpr * GB;
-    const int nchunks = nrows * tg.gpr * (GB / 16);
-    for (int i = 0; i * kWave < nchunks; ++i) {
-        const int c = i * kWave + lane;
-        if (c < nchunks) global_to_lds16(src + (size_t)c * 16, lds_wave + i * 1024);
-    }
-    return nrows;
+template <int FMT, int NB>
+__device__ __forceinline__ float unit_dot(const UnitRegs<Unit<FMT, NB>> &u, const uint8_t *rec, int32_t *isum_out) {
+    if constexpr (FMT == QG_FMT_Q8_0)
+        return unit_dot_q8_0<NB>(u.w, rec, isum_out);
+    else
+        return unit_dot_q4k(u.w, rec, isum_out);
 }
 
-template <int FMT>
-struct GroupRegs;
-template <>
-struct GroupRegs<QG_FMT_Q8_0> {
-    uint32_t w[68];
-};
-template <>
-struct GroupRegs<QG_FMT_Q4K> {
-    uint32_t w[36];
-};
-
-// Read this lane's group from the wave's LDS tile buffer.
-template <int FMT>
-__device__ __forceinline__ void read_group(const uint8_t *lds_group, GroupRegs<FMT> &g) {
-    constexpr int NV = GroupBytes<FMT>::value / 16;
-    const uint4 *p = reinterpret_cast<const uint4 *>(lds_group);
+// Read this lane's unit from the wave's LDS tile buffer (16-byte reads when
+// the unit is 16-byte aligned, else 8-byte reads).
+template <class U>
+__device__ __forceinline__ void read_unit(const uint8_t *p, UnitRegs<U> &u) {
+    if constexpr (U::bytes % 16 == 0) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const uint4 v = p[i];
-        g.w[4 * i + 0] = v.x;
-        g.w[4 * i + 1] = v.y;
-        g.w[4 * i + 2] = v.z;
-        g.w[4 * i + 3] = v.w;
+        for (int i = 0; i < U::dwords / 4; ++i) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(p)[i];
+            u.w[4 * i] = v.x;
+            u.w[4 * i + 1] = v.y;
+            u.w[4 * i + 2] = v.z;
+            u.w[4 * i + 3] = v.w;
+        }
+    } else {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int i = 0; i < U::dwords / 2; ++i) {
+            const u32x2 v = reinterpret_cast<const u32x2 *>(p)[i];
+            u.w[2 * i] = v.x;
+            u.w[2 * i + 1] = v.y;
+        }
     }
 }
 
-template <int FMT>
-__device__ __forceinline__ float group_dot(const GroupRegs<FMT> &g, const int8_t *qx8, const float *dxg,
-                                           const int32_t *sxg, int32_t *isum_out);
-template <>
-__device__ __forceinline__ float group_dot<QG_FMT_Q8_0>(const GroupRegs<QG_FMT_Q8_0> &g, const int8_t *qx8,
-                                                        const float *dxg, const int32_t *, int32_t *isum_out) {
-    return group_dot_q8_0(g.w, qx8, dxg, isum_out);
+// ---------------------------------------------------------------- geometry
+
+struct TileGeom {
+    int upr;  // units per row
+    int lpr;  // lanes per row (power of two >= upr, <= 64)
+    int lsh;  // log2(lpr)
+    int rpt;  // rows per tile = 64 / lpr
+    int row_bytes;
+};
+
+template <class U>
+inline TileGeom make_tile_geom(int K) {
+    TileGeom t;
+    t.upr = K / U::weights;
+    t.lpr = 1;
+    t.lsh = 0;
+    while (t.lpr < t.upr) {
+        t.lpr <<= 1;
+        t.lsh += 1;
+    }
+    t.rpt = kWave / t.lpr;
+    t.row_bytes = t.upr * U::bytes;
+    return t;
 }
-template <>
-__device__ __forceinline__ float group_dot<QG_FMT_Q4K>(const GroupRegs<QG_FMT_Q4K> &g, const int8_t *qx8,
-                                                       const float *dxg, const int32_t *sxg, int32_t *isum_out) {
-    return group_dot_q4k(g.w, qx8, dxg, sxg, isum_out);
+
+template <class U>
+struct TileSize {
+    static constexpr int bytes = kWave * U::bytes;           // a full tile
+    static constexpr int instr = (bytes + 1023) / 1024;      // 16-byte loads per lane
+    static constexpr int lds = (bytes + 15) / 16 * 16;       // LDS it occupies
+};
+
+// ---------------------------------------------------------------- activation staging
+
+// LDS of one CU, and the most the staged activations of a workgroup take.
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kActLdsBudget = 44 * 1024;
+// 16-byte activation chunks each thread holds in registers while staging.
+constexpr int kActRegChunks = 4;
+
+template <class U>
+__host__ __device__ inline int act_lds_bytes_per_token(int K) {
+    return (K / U::weights) * U::rec_dwords * 4;
 }
+
+// Tokens staged at once: bounded by the LDS budget and by what the staging
+// registers of a workgroup of `threads` hold.
+template <class U>
+inline int tokens_per_chunk(int K, int M, int threads) {
+    const int budget = min(kActLdsBudget, kLdsBytes - (threads / kWave) * TileSize<U>::lds);
+    int mt = budget / act_lds_bytes_per_token<U>(K);
+    mt = min(mt, kActRegChunks * threads * 16 / K);
+    mt = min(mt, threads * 128 / K);
+    return max(1, min(mt, M));
+}
+
+template <class U>
+inline size_t gemv_lds_bytes(int waves, int K, int mt) {
+    return (size_t)waves * TileSize<U>::lds + (size_t)mt * act_lds_bytes_per_token<U>(K);
+}
+
+// Staging of one chunk of tokens [m0, m0 + mtc) of the Q8 activation into
+// padded per-unit LDS records, split in two halves: load() issues the global
+// reads into registers, store() writes the records.  Between the two the
+// caller issues its weight loads, which then stay in flight (the waits for
+// the activation registers only cover loads issued before them).
+// Needs mtc*K/16 <= kActRegChunks*threads and mtc*K/128 <= threads.
+template <int FMT, class U, int WAVES>
+struct ActStage {
+    static constexpr int NT = WAVES * kWave;
+    static constexpr int REC = U::rec_dwords * 4;
+    u32x4 q[kActRegChunks];
+    u32x4 d, s;
+
+    template <class TokenRow>
+    __device__ __forceinline__ void load(const int8_t *__restrict__ qx, const float *__restrict__ dx,
+                                         const int32_t *__restrict__ sx, int K, int m0, int mtc, TokenRow token_row) {
+        const int cpt = K / 16;
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k) {
+            const int c = (int)threadIdx.x + k * NT;
+            if (c < mtc * cpt) {
+                const int mm = c / cpt;
+                q[k] = reinterpret_cast<const u32x4 *>(qx + (size_t)token_row(m0 + mm) * K)[c - mm * cpt];
+            }
+        }
+        const int spt = K / 128;
+        const int c = threadIdx.x;
+        if (c < mtc * spt) {
+            const int mm = c / spt;
+            const size_t src = (size_t)token_row(m0 + mm) * (K / 32) / 4 + (c - mm * spt);
+            d = reinterpret_cast<const u32x4 *>(dx)[src];
+            if constexpr (FMT == QG_FMT_Q4K) s = reinterpret_cast<const u32x4 *>(sx)[src];
+        }
+    }
+
+    __device__ __forceinline__ void store(uint8_t *lds, int K, int mtc) const {
+        constexpr int QC = U::weights / 16;  // 16-byte chunks of quants per unit
+        constexpr int SC = U::blocks / 4;    // 16-byte chunks of scales per unit
+        const int upr = K / U::weights;
+        const int cpt = K / 16;
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k) {
+            const int c = (int)threadIdx.x + k * NT;
+            if (c < mtc * cpt) {
+                const int mm = c / cpt;
+                const int w = c - mm * cpt;
+                const int u = w / QC;
+                *reinterpret_cast<u32x4 *>(lds + (size_t)(mm * upr + u) * REC + (w - u * QC) * 16) = q[k];
+            }
+        }
+        const int spt = K / 128;
+        const int c = threadIdx.x;
+        if (c < mtc * spt) {
+            const int mm = c / spt;
+            const int w = c - mm * spt;
+            const int u = w / SC;
+            uint8_t *rec = lds + (size_t)(mm * upr + u) * REC + U::weights + (w - u * SC) * 16;
+            *reinterpret_cast<u32x4 *>(rec) = d;
+            if constexpr (FMT == QG_FMT_Q4K) *reinterpret_cast<u32x4 *>(rec + 32) = s;
+        }
+    }
+};
+
+// ---------------------------------------------------------------- tile engine
 
 // Sum over the lpr lanes of a row with a fixed xor butterfly; every lane of
 // the row ends with the same value.
@@ -202,122 +302,135 @@ __device__ __forceinline__ float row_reduce(float p, int lpr) {
     return p;
 }
 
-
-// ---------------------------------------------------------------- activation staging
-
-// LDS for staged activations per workgroup (the weight tiles take
-// waves * 64 * group bytes on top; 4 waves: Q8_0 68 KiB, Q4_K 36 KiB).
-constexpr int kActLdsBudget = 44 * 1024;
-
-// Activations are staged in LDS as one record per 256-input group: 64 dwords
-// of quants, 8 block scales (+ 8 block sums for Q4_K), padded so that the
-// record stride is an odd multiple of 4 dwords.  Lanes of a wave read
-// different groups at the same offset; with this stride their 16-byte reads
-// fall in disjoint banks (a 256-byte stride would put them all in one).
-template <int FMT>
-struct ActRecord {
-    static constexpr int dwords = FMT == QG_FMT_Q4K ? 84 : 76;  // 80 + 4 / 72 + 4
-    static constexpr int bytes = dwords * 4;
+template <class U>
+struct TileRegs {
+    u32x4 v[TileSize<U>::instr];
 };
 
-template <int FMT>
-__host__ __device__ inline int act_lds_bytes_per_token(int K) {
-    return (K / kGroupWeights) * ActRecord<FMT>::bytes;
-}
-
-template <int FMT>
-inline int tokens_per_chunk(int K, int M) {
-    return max(1, min(min(M, kMaxChunkTokens), kActLdsBudget / act_lds_bytes_per_token<FMT>(K)));
-}
-
-template <int FMT>
-inline size_t gemv_lds_bytes(int waves, int K, int mt) {
-    return (size_t)waves * kWave * GroupBytes<FMT>::value + (size_t)mt * act_lds_bytes_per_token<FMT>(K) +
-           (size_t)kMaxChunkTokens * sizeof(int);
-}
-
-// Stage tokens m0 .. m0+mt-1 (activation rows rows_lds[0..mt) of qx/dx/sx)
-// into padded LDS records (whole workgroup; global -> VGPR -> LDS, 16 bytes
-// per access).
-template <int FMT, int WAVES>
-__device__ __forceinline__ void stage_activations(const int8_t *__restrict__ qx, const float *__restrict__ dx,
-                                                  const int32_t *__restrict__ sx, int K, int mt,
-                                                  const int *rows_lds, uint8_t *lds) {
-    constexpr int REC = ActRecord<FMT>::bytes;
-    const int gpr = K / kGroupWeights;
-    const int cpt = K / 16;  // 16-byte chunks of quants per token
-    for (int c = threadIdx.x; c < mt * cpt; c += WAVES * kWave) {
-        const int mm = c / cpt;
-        const int w = c - mm * cpt;
-        const uint4 *q = reinterpret_cast<const uint4 *>(qx + (size_t)rows_lds[mm] * K);
-        *reinterpret_cast<uint4 *>(lds + (size_t)(mm * gpr + (w >> 4)) * REC + (w & 15) * 16) = q[w];
-    }
-    const int spt = gpr * 2;  // 16-byte chunks of scales per token
-    for (int c = threadIdx.x; c < mt * spt; c += WAVES * kWave) {
-        const int mm = c / spt;
-        const int w = c - mm * spt;
-        const size_t src = (size_t)rows_lds[mm] * (K / 32) / 4 + w;  // in uint4 units
-        uint8_t *rec = lds + (size_t)(mm * gpr + (w >> 1)) * REC + 256 + (w & 1) * 16;
-        *reinterpret_cast<uint4 *>(rec) = reinterpret_cast<const uint4 *>(dx)[src];
-        if (FMT == QG_FMT_Q4K) *reinterpret_cast<uint4 *>(rec + 32) = reinterpret_cast<const uint4 *>(sx)[src];
+// Issue the 16-byte non-temporal loads of tile `tile` (rows tile*rpt ..
+// +rpt clipped to N).  Lanes past the end of the tile re-read its last
+// chunk, so every lane issues every load and none leaves the matrix.
+template <class U>
+__device__ __forceinline__ void load_tile(const uint8_t *__restrict__ W, int N, const TileGeom &tg, int tile,
+                                          TileRegs<U> &r) {
+    const int lane = lane_id();
+    const int row0 = tile * tg.rpt;
+    const int nrows = min(tg.rpt, N - row0);
+    const int last = nrows * tg.row_bytes / 16 - 1;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(W + (size_t)row0 * tg.row_bytes);
+#pragma unroll
+    for (int i = 0; i < TileSize<U>::instr; ++i) {
+        const int c = min(i * kWave + lane, last);
+        r.v[i] = __builtin_nontemporal_load(src + c);
     }
 }
 
-// ---------------------------------------------------------------- workgroup engine
+// Write a loaded tile to the wave's LDS buffer and read this lane's unit back.
+template <class U>
+__device__ __forceinline__ void tile_to_unit(const TileRegs<U> &r, uint8_t *lw, int unit_index, bool valid,
+                                             UnitRegs<U> &u) {
+    const int lane = lane_id();
+    __builtin_amdgcn_wave_barrier();  // this wave's earlier reads of the buffer are issued first
+#pragma unroll
+    for (int i = 0; i < TileSize<U>::instr; ++i)
+        if (i * 1024 + lane * 16 < TileSize<U>::bytes) *reinterpret_cast<u32x4 *>(lw + i * 1024 + lane * 16) = r.v[i];
+    __builtin_amdgcn_wave_barrier();  // LDS executes one wave's accesses in order
+    if (valid) read_unit<U>(lw + unit_index * U::bytes, u);
+}
 
-// One workgroup of WAVES waves; each wave owns weight tile `tile` of W (if
-// has_tile).  The tile is copied HBM -> LDS and kept; the M tokens are
-// processed in chunks of mt_max, each chunk staged once in LDS for the whole
-// workgroup.  token_row(m) gives the activation row of token m; out(m, row, v)
-// stores one result; isum_out(m, row, g, sums8) receives the exact block sums
-// when DEBUG_ISUM.  Every wave of the workgroup must call this (barriers).
-template <int FMT, int WAVES, bool DEBUG_ISUM, class TokenRow, class Out, class IsumOut>
-__device__ __forceinline__ void gemv_tiles_workgroup(const uint8_t *__restrict__ W, int N, int K, const TileGeom &tg,
-                                                     int tile, bool has_tile, const int8_t *qx, const float *dx,
-                                                     const int32_t *sx, int M, int mt_max, uint8_t *smem,
-                                                     TokenRow token_row, Out out, IsumOut isum_out) {
-    constexpr int GB = GroupBytes<FMT>::value;
-    constexpr int REC = ActRecord<FMT>::bytes;
+// The workgroup engine.  Wave w of the workgroup processes tiles
+// tile_base + w*tpw + i (i < tpw, tile < ntiles) of matrix W against M tokens.
+// token_row(m) gives the activation row of token m; out(m, row, v) stores one
+// result; isum_out(m, row, unit, sums) receives the exact block sums when
+// DEBUG_ISUM.  Tokens are staged in chunks of mt; with more than one chunk,
+// tpw must be 1 (the tile stays in registers across chunks).  Every wave of
+// the workgroup must call this (it synchronizes).  PIPE = false limits tpw
+// to 1 and keeps only one tile register set; ONE = true is the M = 1 form
+// (no token loop, fewer live registers).
+template <int FMT, int NB, int WAVES, bool DEBUG_ISUM, bool PIPE, bool ONE, class TokenRow, class Out,
+          class IsumOut>
+__device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, int N, int K, const TileGeom &tg,
+                                               int tile_base, int tpw, int ntiles, const int8_t *qx, const float *dx,
+                                               const int32_t *sx, int M, int mt, uint8_t *smem, TokenRow token_row,
+                                               Out out, IsumOut isum_out) {
+    using U = Unit<FMT, NB>;
+    constexpr int REC = U::rec_dwords * 4;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    uint8_t *lw = smem + wave * kWave * GB;
-    uint8_t *lact = smem + WAVES * kWave * GB;
-    int *lrows = reinterpret_cast<int *>(lact + (size_t)mt_max * act_lds_bytes_per_token<FMT>(K));
-
-    // 1. this wave's weight tile: HBM -> LDS, left in flight
-    int nrows = 0;
-    if (has_tile) nrows = issue_tile_to_lds<FMT>(W, N, tg, tile, lw);
+    uint8_t *lw = smem + wave * TileSize<U>::lds;
+    uint8_t *lact = smem + WAVES * TileSize<U>::lds;
+    const int tile0 = tile_base + wave * tpw;
     const int r = lane >> tg.lsh;
     const int g = lane & (tg.lpr - 1);
-    const bool valid = has_tile && g < tg.gpr && r < nrows;
-    const int row = tile * tg.rpt + r;
-    GroupRegs<FMT> regs;
 
-    for (int m0 = 0; m0 < M; m0 += mt_max) {
-        const int mt = min(mt_max, M - m0);
-        if (m0 > 0) __syncthreads();  // every wave is done with the previous chunk
-        for (int i = threadIdx.x; i < mt; i += WAVES * kWave) lrows[i] = token_row(m0 + i);
-        __syncthreads();
-        // 2. the chunk's activation quants, scales (and block sums), shared by the workgroup
-        stage_activations<FMT, WAVES>(qx, dx, sx, K, mt, lrows, lact);
-        wait_vmem_all();  // this wave's weight tile has landed in LDS
-        __syncthreads();
-        if (m0 == 0 && valid) read_group<FMT>(lw + (r * tg.gpr + g) * GB, regs);
-
-        for (int mm = 0; mm < mt; ++mm) {
+    auto compute = [&](const UnitRegs<U> &u, int tile, bool valid, int m0, int mtc) {
+        const int row = tile * tg.rpt + r;
+        if (ONE) mtc = 1;
+        for (int mm = 0; mm < mtc; ++mm) {
             float p = 0.0f;
             if (valid) {
-                int32_t isum_tmp[8];
-                const uint8_t *rec = lact + (size_t)(mm * tg.gpr + g) * REC;
-                p = group_dot<FMT>(regs, reinterpret_cast<const int8_t *>(rec),
-                                   reinterpret_cast<const float *>(rec + 256),
-                                   reinterpret_cast<const int32_t *>(rec + 288), DEBUG_ISUM ? isum_tmp : nullptr);
+                int32_t isum_tmp[U::blocks];
+                p = unit_dot<FMT, NB>(u, lact + (size_t)(mm * tg.upr + g) * REC, DEBUG_ISUM ? isum_tmp : nullptr);
                 if (DEBUG_ISUM) isum_out(m0 + mm, row, g, isum_tmp);
             }
             p = row_reduce(p, tg.lpr);
             if (!DEBUG_ISUM && valid && g == 0) out(m0 + mm, row, p);
         }
+    };
+    auto unit_valid = [&](int tile) { return tile < ntiles && g < tg.upr && tile * tg.rpt + r < N; };
+
+    TileRegs<U> ra, rb;
+    UnitRegs<U> u;
+    ActStage<FMT, U, WAVES> st;
+    if (ONE || M <= mt) {
+        if (ONE) M = 1;
+        // one chunk of tokens: activation reads first, then up to two tiles in
+        // flight; tpw tiles in total
+        st.load(qx, dx, sx, K, 0, M, token_row);
+        if (tile0 < ntiles) load_tile<U>(W, N, tg, tile0, ra);
+        if (PIPE && tpw > 1 && tile0 + 1 < ntiles) load_tile<U>(W, N, tg, tile0 + 1, rb);
+        st.store(lact, K, M);
+        __syncthreads();
+        for (int i = 0; i < tpw; i += 2) {
+            const int ta = tile0 + i, tb = tile0 + i + 1;
+            if (ta < ntiles) {
+                const bool v = unit_valid(ta);
+                tile_to_unit<U>(ra, lw, r * tg.upr + g, v, u);
+                if (PIPE && i + 2 < tpw && ta + 2 < ntiles) load_tile<U>(W, N, tg, ta + 2, ra);
+                compute(u, ta, v, 0, M);
+            }
+            if (PIPE && i + 1 < tpw && tb < ntiles) {
+                const bool v = unit_valid(tb);
+                tile_to_unit<U>(rb, lw, r * tg.upr + g, v, u);
+                if (i + 3 < tpw && tb + 2 < ntiles) load_tile<U>(W, N, tg, tb + 2, rb);
+                compute(u, tb, v, 0, M);
+            }
+        }
+    } else if (!ONE) {
+        // several chunks of tokens: one tile, kept in registers across chunks
+        const bool v = unit_valid(tile0);
+        for (int m0 = 0; m0 < M; m0 += mt) {
+            const int mtc = min(mt, M - m0);
+            if (m0 > 0) __syncthreads();  // every wave is done with the previous chunk
+            st.load(qx, dx, sx, K, m0, mtc, token_row);
+            if (m0 == 0 && tile0 < ntiles) load_tile<U>(W, N, tg, tile0, ra);
+            st.store(lact, K, mtc);
+            __syncthreads();
+            if (m0 == 0 && tile0 < ntiles) tile_to_unit<U>(ra, lw, r * tg.upr + g, v, u);
+            if (tile0 < ntiles) compute(u, tile0, v, m0, mtc);
+        }
     }
 }
+
+// Tiles per wave for a launch: about one round of the chip's resident waves,
+// at most 4 (one chunk of tokens only).
+inline int tiles_per_wave(int ntiles, int resident_waves, bool single_chunk) {
+    if (!single_chunk) return 1;
+    const int t = (ntiles + resident_waves - 1) / resident_waves;
+    return t < 1 ? 1 : (t > 4 ? 4 : t);
+}
+
+// Compute units of the current device (queried once per process and device).
+int device_cu_count();
 
 }  // namespace qg

@@ -193,8 +193,10 @@ struct MoeArgs {
     int mt;       // tokens per LDS chunk
 };
 
-// gate and up of expert uniq[blockIdx.y]: tiles [0, F/rpt) are gate rows,
-// [F/rpt, 2F/rpt) up rows; the tokens are the expert's pairs' tokens.
+using QU = Unit<QG_FMT_Q4K, 8>;
+
+// gate and up of expert uniq[blockIdx.y]: workgroups [0, nwg) take gate rows,
+// [nwg, 2 nwg) up rows; the tokens are the expert's pairs' tokens.
 __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int u = blockIdx.y;
@@ -202,17 +204,16 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
     const int e = a.ws.uniq[u];
     const int p0 = a.ws.pair_off[u];
     const int cnt = a.ws.pair_off[u + 1] - p0;
-    const int half = (a.F + a.tg.rpt - 1) / a.tg.rpt;
-    int tile = blockIdx.x * kMoeWaves + threadIdx.x / kWave;
-    const bool is_up = tile >= half;
-    if (is_up) tile -= half;
-    const bool has_tile = tile < half;
+    const int ntiles = (a.F + a.tg.rpt - 1) / a.tg.rpt;
+    const int nwg = (ntiles + kMoeWaves - 1) / kMoeWaves;
+    const bool is_up = (int)blockIdx.x >= nwg;
+    const int wg = is_up ? (int)blockIdx.x - nwg : (int)blockIdx.x;
     const uint8_t *W = reinterpret_cast<const uint8_t *>(is_up ? a.up[e] : a.gate[e]);
     float *dst = is_up ? a.ws.v : a.ws.g;
     const int32_t *pairs = a.ws.pairs + p0;
     const int topk = a.topk, F = a.F;
-    gemv_tiles_workgroup<QG_FMT_Q4K, kMoeWaves, false>(
-        W, F, a.D, a.tg, tile, has_tile, a.qx, a.dx, a.sx, cnt, a.mt, smem,
+    gemv_workgroup<QG_FMT_Q4K, 8, kMoeWaves, false, false, false>(
+        W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, a.qx, a.dx, a.sx, cnt, a.mt, smem,
         [=](int m) { return pairs[m] / topk; },
         [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; },
         [](int, int, int, const int32_t *) {});
@@ -227,13 +228,12 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     const int p0 = a.ws.pair_off[u];
     const int cnt = a.ws.pair_off[u + 1] - p0;
     const int ntiles = (a.D + a.tg.rpt - 1) / a.tg.rpt;
-    const int tile = blockIdx.x * kMoeWaves + threadIdx.x / kWave;
     const uint8_t *W = reinterpret_cast<const uint8_t *>(a.down[e]);
     const int32_t *pairs = a.ws.pairs + p0;
     float *o = a.ws.o;
     const int D = a.D;
-    gemv_tiles_workgroup<QG_FMT_Q4K, kMoeWaves, false>(
-        W, D, a.F, a.tg, tile, tile < ntiles, a.ws.hq, a.ws.hd, a.ws.hs, cnt, a.mt, smem,
+    gemv_workgroup<QG_FMT_Q4K, 8, kMoeWaves, false, false, false>(
+        W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, a.ws.hq, a.ws.hd, a.ws.hs, cnt, a.mt, smem,
         [=](int m) { return pairs[m]; }, [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; },
         [](int, int, int, const int32_t *) {});
 }
@@ -373,16 +373,15 @@ extern "C" int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t
     a.ws = w;
 
     // gate/up: K = D
-    a.tg = make_tile_geom(D);
-    a.mt = tokens_per_chunk<QG_FMT_Q4K>(D, kMaxChunkTokens);
-    size_t lds = gemv_lds_bytes<QG_FMT_Q4K>(kMoeWaves, D, a.mt);
+    constexpr int threads = kMoeWaves * kWave;
+    a.tg = make_tile_geom<QU>(D);
+    a.mt = tokens_per_chunk<QU>(D, QG_MAX_MOE_PAIRS, threads);
+    size_t lds = gemv_lds_bytes<QU>(kMoeWaves, D, a.mt);
     static bool lds_gu = false, lds_dn = false;  // idempotent: raise the dynamic-LDS limit once
-    const size_t lds_max = (size_t)kMoeWaves * kWave * GroupBytes<QG_FMT_Q4K>::value + kActLdsBudget +
-                           kMaxChunkTokens * sizeof(int);
+    const size_t lds_max = kLdsBytes;
     if (!lds_gu) lds_gu = raise_lds_limit(moe_gate_up_kernel, lds_max);
-    int tiles = 2 * ((F + a.tg.rpt - 1) / a.tg.rpt);
-    hipLaunchKernelGGL(moe_gate_up_kernel, dim3((tiles + kMoeWaves - 1) / kMoeWaves, Ucap), dim3(kMoeWaves * kWave),
-                       lds, st, a);
+    int nwg = ((F + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
+    hipLaunchKernelGGL(moe_gate_up_kernel, dim3(2 * nwg, Ucap), dim3(threads), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
 
     const long long hthreads = (long long)P * (F / 32) * 8;
@@ -390,13 +389,12 @@ extern "C" int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
 
     // down: K = F
-    a.tg = make_tile_geom(F);
-    a.mt = tokens_per_chunk<QG_FMT_Q4K>(F, kMaxChunkTokens);
-    lds = gemv_lds_bytes<QG_FMT_Q4K>(kMoeWaves, F, a.mt);
+    a.tg = make_tile_geom<QU>(F);
+    a.mt = tokens_per_chunk<QU>(F, QG_MAX_MOE_PAIRS, threads);
+    lds = gemv_lds_bytes<QU>(kMoeWaves, F, a.mt);
     if (!lds_dn) lds_dn = raise_lds_limit(moe_down_kernel, lds_max);
-    tiles = (D + a.tg.rpt - 1) / a.tg.rpt;
-    hipLaunchKernelGGL(moe_down_kernel, dim3((tiles + kMoeWaves - 1) / kMoeWaves, Ucap), dim3(kMoeWaves * kWave),
-                       lds, st, a);
+    nwg = ((D + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
+    hipLaunchKernelGGL(moe_down_kernel, dim3(nwg, Ucap), dim3(threads), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
 
     const long long cthreads = (long long)T * (D / 4);
