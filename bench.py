@@ -4,7 +4,9 @@
 One step = one pass of the decode projections of the Q8_0 attention workload
 (batch 1): quantize an 8192-wide fp32 activation to Q8, the 8192 -> 4096 output
 projection, quantize a 4096-wide activation, and the paired 4096 -> 1024 +
-4096 -> 512 low-rank projection in one launch.  Inputs are seeded synthetic
+4096 -> 512 low-rank projection in one launch.  The same step with the
+quantization fused into the projections (qgemv_*_f32) is timed too
+(config.fused_quantize_step_us).  Inputs are seeded synthetic
 tensors resident in HBM before timing starts.  Weights rotate over copies that
 together exceed 1 GiB, so no step reads weights left in the 256 MB Infinity
 Cache or in L2 by an earlier step.  The steps are captured once in a HIP graph
@@ -148,12 +150,20 @@ class DecodeStep:
                 + (self.N1 + self.N2) * 4)
 
     def step(self, i):
+        """quantize_act_q8 once per activation, then the projections that consume it."""
         qg, r = self.qg, i % self.R
         qg.quantize_act_q8(self.x, 1, self.K, self.qx, self.dx, self.sx)
         qg.qgemv_q8_0(self.W[r], self.N, self.K, self.qx, self.dx, 1, self.y)
         qg.quantize_act_q8(self.x2, 1, self.K2, self.qx2, self.dx2, self.sx2)
         qg.qgemv_paired(qg.FMT_Q8_0, self.W1[r], self.N1, self.W2[r], self.N2, self.K2, self.qx2, self.dx2,
                         self.sx2, 1, self.y1, self.y2)
+
+    def step_fused(self, i):
+        """The same step with the quantization done inside the consuming projections."""
+        qg, r = self.qg, i % self.R
+        qg.qgemv_q8_0_f32(self.W[r], self.N, self.K, self.x, 1, self.y, self.qx, self.dx, self.sx)
+        qg.qgemv_paired_f32(qg.FMT_Q8_0, self.W1[r], self.N1, self.W2[r], self.N2, self.K2, self.x2, 1, self.y1,
+                            self.y2, self.qx2, self.dx2, self.sx2)
 
     def out_gemv(self, i):
         self.qg.qgemv_q8_0(self.W[i % self.R], self.N, self.K, self.qx, self.dx, 1, self.y)
@@ -436,7 +446,11 @@ def main():
             "source_hash": src_hash,
         },
     }
-    del g_steps, g_k
+    g_f = capture(step.step_fused, args.steps, stream)
+    timer.run(g_f.replay)
+    fsec = timer.run(g_f.replay) / args.steps
+    del g_steps, g_k, g_f
+    result["config"]["fused_quantize_step_us"] = round(fsec * 1e6, 3)
     if not args.no_extra:
         result["extra"] = extra_measurements(qg, torch, stream, timer)
     if not args.no_cpu:

@@ -149,6 +149,26 @@ int qgemv_q4k(const void *W, int N, int K, const int8_t *qx, const float *dx, co
 int qgemv_paired(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const int8_t *qx, const float *dx,
                  const int32_t *sx, int M, float *y1, float *y2, void *stream);
 
+/*
+ * qgemv_q8_0_f32, qgemv_q4k_f32, qgemv_paired_f32 -- the same products taking
+ * the fp32 activation x [M, K] instead of its Q8 form.  [PR623] Summary:
+ * the decode activation is quantized to Q8 once and fed to every projection;
+ * here the first projection that consumes x does the quantization inside its
+ * kernel (every workgroup quantizes x while staging it, exactly as
+ * quantize_act_q8 does), and writes the Q8 activation to qx [M, K], dx and sx
+ * [M, K/32] for the projections that follow; each of qx, dx, sx may be NULL.
+ * y (and y1, y2) equal the two-step quantize_act_q8 + qgemv_* result bit for
+ * bit, and qx/dx/sx equal quantize_act_q8's output.
+ * Errors: QG_ERR_NULL if x (or a weight or output) is NULL; otherwise as the
+ * Q8-activation forms.
+ */
+int qgemv_q8_0_f32(const void *W, int N, int K, const float *x, int M, float *y, int8_t *qx, float *dx, int32_t *sx,
+                   void *stream);
+int qgemv_q4k_f32(const void *W, int N, int K, const float *x, int M, float *y, int8_t *qx, float *dx, int32_t *sx,
+                  void *stream);
+int qgemv_paired_f32(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const float *x, int M, float *y1,
+                     float *y2, int8_t *qx, float *dx, int32_t *sx, void *stream);
+
 /* ---- routed MoE -------------------------------------------------------- */
 /*
  * Workspace of moe_routed_qgemv, in bytes, for the given sizes (0 if a size

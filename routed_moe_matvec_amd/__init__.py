@@ -18,6 +18,7 @@ __all__ = [
     "QGError", "FMT_Q8_0", "FMT_Q4K", "library_path", "quantize_act_q8", "qgemv_q8_0", "qgemv_q4k",
     "qgemv_paired", "moe_routed_workspace_bytes", "moe_routed_workspace_layout", "moe_routed_qgemv",
     "qgemm_prefill", "qg_status_string", "qgemv_debug_block_isums", "pointer_table", "WS_REGIONS",
+    "qgemv_q8_0_f32", "qgemv_q4k_f32", "qgemv_paired_f32",
 ]
 
 FMT_Q8_0 = 0
@@ -53,6 +54,9 @@ _c_q8_0 = _sig("qgemv_q8_0", _i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp])
 _c_q4k = _sig("qgemv_q4k", _i, [_vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp])
 _c_paired = _sig("qgemv_paired", _i, [_i, _vp, _i, _vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp])
 _c_isums = _sig("qgemv_debug_block_isums", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
+_c_q8_0_f32 = _sig("qgemv_q8_0_f32", _i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp])
+_c_q4k_f32 = _sig("qgemv_q4k_f32", _i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp])
+_c_paired_f32 = _sig("qgemv_paired_f32", _i, [_i, _vp, _i, _vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp])
 _c_status = _sig("qg_status_string", ctypes.c_char_p, [_i])
 try:
     _c_ws_bytes = _sig("moe_routed_workspace_bytes", _sz, [_i, _i, _i, _i, _i])
@@ -120,6 +124,22 @@ def qgemv_q4k(W, N: int, K: int, qx, dx, sx, M: int, y, stream=None) -> None:
 def qgemv_paired(fmt: int, W1, N1: int, W2, N2: int, K: int, qx, dx, sx, M: int, y1, y2, stream=None) -> None:
     _ok(_c_paired(fmt, _ptr(W1), N1, _ptr(W2), N2, K, _ptr(qx), _ptr(dx), _ptr(sx), M, _ptr(y1), _ptr(y2),
                   _stream(stream, W1)), "qgemv_paired")
+
+
+def qgemv_q8_0_f32(W, N: int, K: int, x, M: int, y, qx=None, dx=None, sx=None, stream=None) -> None:
+    _ok(_c_q8_0_f32(_ptr(W), N, K, _ptr(x), M, _ptr(y), _ptr(qx), _ptr(dx), _ptr(sx), _stream(stream, W)),
+        "qgemv_q8_0_f32")
+
+
+def qgemv_q4k_f32(W, N: int, K: int, x, M: int, y, qx=None, dx=None, sx=None, stream=None) -> None:
+    _ok(_c_q4k_f32(_ptr(W), N, K, _ptr(x), M, _ptr(y), _ptr(qx), _ptr(dx), _ptr(sx), _stream(stream, W)),
+        "qgemv_q4k_f32")
+
+
+def qgemv_paired_f32(fmt: int, W1, N1: int, W2, N2: int, K: int, x, M: int, y1, y2, qx=None, dx=None, sx=None,
+                     stream=None) -> None:
+    _ok(_c_paired_f32(fmt, _ptr(W1), N1, _ptr(W2), N2, K, _ptr(x), M, _ptr(y1), _ptr(y2), _ptr(qx), _ptr(dx),
+                      _ptr(sx), _stream(stream, W1)), "qgemv_paired_f32")
 
 
 def qgemv_debug_block_isums(fmt: int, W, N: int, K: int, qx, M: int, isum, stream=None) -> None:

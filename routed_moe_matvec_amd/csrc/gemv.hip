@@ -22,16 +22,14 @@ struct GemvArgs {
     int N1, nt1;
     int K;
     TileGeom tg;
-    const int8_t *qx;
-    const float *dx;
-    const int32_t *sx;
+    ActSrc act;  // Q8 activation, or fp32 activation quantized in the kernel
     int M;
     int mt;         // tokens staged in LDS per chunk
     int tpw;        // tiles per wave
     int32_t *isum;  // per-block sums of matrix 0 (test export), else unused
 };
 
-template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE>
+template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32>
 __global__ __launch_bounds__(kGemvWaves *kWave) void qgemv_kernel(GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // workgroups [0, nwg0) cover matrix 0, the rest matrix 1 (paired call)
@@ -43,8 +41,8 @@ __global__ __launch_bounds__(kGemvWaves *kWave) void qgemv_kernel(GemvArgs a) {
     const int nt = second ? a.nt1 : a.nt0;
     const int nb = a.K / 32;
     int32_t *isum = a.isum;
-    gemv_workgroup<FMT, NB, kGemvWaves, DEBUG_ISUM, PIPE, ONE>(
-        W, N, a.K, a.tg, wg * kGemvWaves * a.tpw, a.tpw, nt, a.qx, a.dx, a.sx, a.M, a.mt, smem,
+    gemv_workgroup<FMT, NB, kGemvWaves, DEBUG_ISUM, PIPE, ONE, F32>(
+        W, N, a.K, a.tg, wg * kGemvWaves * a.tpw, a.tpw, nt, a.act, a.M, a.mt, smem,
         [](int m) { return m; }, [=](int m, int row, float v) { y[(size_t)m * N + row] = v; },
         [=](int m, int row, int unit, const int32_t *s) {
             int32_t *o = isum + ((size_t)m * N + row) * nb + unit * NB;
@@ -55,27 +53,27 @@ __global__ __launch_bounds__(kGemvWaves *kWave) void qgemv_kernel(GemvArgs a) {
 
 static inline bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; }
 
-template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE>
+template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32>
 static int launch_kernel(const GemvArgs &a, int grid, size_t lds, hipStream_t stream) {
     static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
             return QG_ERR_LAUNCH;
         attr_set = true;
     }
-    hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE>), dim3(grid), dim3(kGemvWaves * kWave), lds, stream, a);
+    hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>), dim3(grid), dim3(kGemvWaves * kWave), lds, stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
-template <int FMT, int NB, bool DEBUG_ISUM>
+template <int FMT, int NB, bool DEBUG_ISUM, bool F32>
 static int launch_gemv(GemvArgs &a, hipStream_t stream) {
     using U = Unit<FMT, NB>;
     constexpr int threads = kGemvWaves * kWave;
     a.tg = make_tile_geom<U>(a.K);
     a.nt0 = (a.N0 + a.tg.rpt - 1) / a.tg.rpt;
     a.nt1 = a.W1 ? (a.N1 + a.tg.rpt - 1) / a.tg.rpt : 0;
-    a.mt = tokens_per_chunk<U>(a.K, a.M, threads);
+    a.mt = tokens_per_chunk<U>(a.K, a.M, threads, F32);
     const size_t lds = gemv_lds_bytes<U>(kGemvWaves, a.K, a.mt);
     // about one round of resident waves (LDS bounds the workgroups per CU)
     const int wg_per_cu = max(1, min(4, (int)((160 * 1024) / lds)));
@@ -86,17 +84,17 @@ static int launch_gemv(GemvArgs &a, hipStream_t stream) {
     a.nwg0 = (a.nt0 + per_wg - 1) / per_wg;
     const int grid = a.nwg0 + (a.nt1 + per_wg - 1) / per_wg;
     if (a.M == 1)
-        return a.tpw > 1 ? launch_kernel<FMT, NB, DEBUG_ISUM, true, true>(a, grid, lds, stream)
-                         : launch_kernel<FMT, NB, DEBUG_ISUM, false, true>(a, grid, lds, stream);
-    return a.tpw > 1 ? launch_kernel<FMT, NB, DEBUG_ISUM, true, false>(a, grid, lds, stream)
-                     : launch_kernel<FMT, NB, DEBUG_ISUM, false, false>(a, grid, lds, stream);
+        return a.tpw > 1 ? launch_kernel<FMT, NB, DEBUG_ISUM, true, true, F32>(a, grid, lds, stream)
+                         : launch_kernel<FMT, NB, DEBUG_ISUM, false, true, F32>(a, grid, lds, stream);
+    return a.tpw > 1 ? launch_kernel<FMT, NB, DEBUG_ISUM, true, false, F32>(a, grid, lds, stream)
+                     : launch_kernel<FMT, NB, DEBUG_ISUM, false, false, F32>(a, grid, lds, stream);
 }
 
-template <bool DEBUG_ISUM>
+template <bool DEBUG_ISUM, bool F32>
 static int launch_fmt(int fmt, GemvArgs &a, hipStream_t stream) {
-    if (fmt == QG_FMT_Q4K) return launch_gemv<QG_FMT_Q4K, 8, DEBUG_ISUM>(a, stream);
-    if (a.K <= 8192) return launch_gemv<QG_FMT_Q8_0, 4, DEBUG_ISUM>(a, stream);
-    return launch_gemv<QG_FMT_Q8_0, 8, DEBUG_ISUM>(a, stream);
+    if (fmt == QG_FMT_Q4K) return launch_gemv<QG_FMT_Q4K, 8, DEBUG_ISUM, F32>(a, stream);
+    if (a.K <= 8192) return launch_gemv<QG_FMT_Q8_0, 4, DEBUG_ISUM, F32>(a, stream);
+    return launch_gemv<QG_FMT_Q8_0, 8, DEBUG_ISUM, F32>(a, stream);
 }
 
 static int check_common(int N, int K, int M) {
@@ -105,18 +103,22 @@ static int check_common(int N, int K, int M) {
     return QG_OK;
 }
 
-static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const int8_t *qx,
-                         const float *dx, const int32_t *sx, int M, float *y1, float *y2, int32_t *isum,
-                         hipStream_t stream) {
+// Shared argument checks and launch.  Exactly one activation source is
+// given: (qx, dx[, sx]) or the fp32 x (then pqx/pdx/psx optionally receive
+// the Q8 activation).
+static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const ActSrc &act, int M,
+                         float *y1, float *y2, int32_t *isum, hipStream_t stream) {
     if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4K) return QG_ERR_FORMAT;
-    if (!W1 || !qx || !dx || (!y1 && !isum)) return QG_ERR_NULL;
-    if (fmt == QG_FMT_Q4K && !sx) return QG_ERR_NULL;
+    const bool f32 = act.x != nullptr;
+    if (!W1 || (!y1 && !isum)) return QG_ERR_NULL;
+    if (!f32 && (!act.qx || !act.dx || (fmt == QG_FMT_Q4K && !act.sx))) return QG_ERR_NULL;
     if (W2 && !y2) return QG_ERR_NULL;
     int rc = check_common(N1, K, M);
     if (rc) return rc;
     if (W2 && N2 < 1) return QG_ERR_SHAPE;
-    if (misaligned(W1) || misaligned(qx) || misaligned(dx) || (y1 && misaligned(y1)) || misaligned(W2) ||
-        misaligned(y2) || misaligned(sx) || misaligned(isum))
+    if (misaligned(W1) || misaligned(act.qx) || misaligned(act.dx) || misaligned(act.sx) || misaligned(act.x) ||
+        misaligned(act.pqx) || misaligned(act.pdx) || misaligned(act.psx) || (y1 && misaligned(y1)) ||
+        misaligned(W2) || misaligned(y2) || misaligned(isum))
         return QG_ERR_ALIGN;
     GemvArgs a{};
     a.K = K;
@@ -128,33 +130,74 @@ static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2
         a.y1 = y2;
         a.N1 = N2;
     }
-    a.qx = qx;
-    a.dx = dx;
-    a.sx = sx;
+    a.act = act;
     a.M = M;
     a.isum = isum;
-    return isum ? launch_fmt<true>(fmt, a, stream) : launch_fmt<false>(fmt, a, stream);
+    if (isum) return launch_fmt<true, false>(fmt, a, stream);
+    return f32 ? launch_fmt<false, true>(fmt, a, stream) : launch_fmt<false, false>(fmt, a, stream);
+}
+
+static ActSrc q8_src(const int8_t *qx, const float *dx, const int32_t *sx) {
+    ActSrc s{};
+    s.qx = qx;
+    s.dx = dx;
+    s.sx = sx;
+    return s;
+}
+
+static ActSrc f32_src(const float *x, int8_t *qx, float *dx, int32_t *sx) {
+    ActSrc s{};
+    s.x = x;
+    s.pqx = qx;
+    s.pdx = dx;
+    s.psx = sx;
+    return s;
 }
 
 }  // namespace qg
 
 extern "C" int qgemv_q8_0(const void *W, int N, int K, const int8_t *qx, const float *dx, int M, float *y,
                           void *stream) {
-    return qg::gemv_dispatch(QG_FMT_Q8_0, W, N, nullptr, 0, K, qx, dx, nullptr, M, y, nullptr, nullptr,
+    if (!qx || !dx) return QG_ERR_NULL;
+    return qg::gemv_dispatch(QG_FMT_Q8_0, W, N, nullptr, 0, K, qg::q8_src(qx, dx, nullptr), M, y, nullptr, nullptr,
                              (hipStream_t)stream);
 }
 
 extern "C" int qgemv_q4k(const void *W, int N, int K, const int8_t *qx, const float *dx, const int32_t *sx, int M,
                          float *y, void *stream) {
-    return qg::gemv_dispatch(QG_FMT_Q4K, W, N, nullptr, 0, K, qx, dx, sx, M, y, nullptr, nullptr,
+    if (!qx || !dx || !sx) return QG_ERR_NULL;
+    return qg::gemv_dispatch(QG_FMT_Q4K, W, N, nullptr, 0, K, qg::q8_src(qx, dx, sx), M, y, nullptr, nullptr,
                              (hipStream_t)stream);
 }
 
 extern "C" int qgemv_paired(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const int8_t *qx,
                             const float *dx, const int32_t *sx, int M, float *y1, float *y2, void *stream) {
     if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4K) return QG_ERR_FORMAT;
-    if (!W2 || !y2 || !y1) return QG_ERR_NULL;
-    return qg::gemv_dispatch(fmt, W1, N1, W2, N2, K, qx, dx, sx, M, y1, y2, nullptr, (hipStream_t)stream);
+    if (!W2 || !y2 || !y1 || !qx || !dx) return QG_ERR_NULL;
+    return qg::gemv_dispatch(fmt, W1, N1, W2, N2, K, qg::q8_src(qx, dx, sx), M, y1, y2, nullptr,
+                             (hipStream_t)stream);
+}
+
+extern "C" int qgemv_q8_0_f32(const void *W, int N, int K, const float *x, int M, float *y, int8_t *qx, float *dx,
+                              int32_t *sx, void *stream) {
+    if (!x) return QG_ERR_NULL;
+    return qg::gemv_dispatch(QG_FMT_Q8_0, W, N, nullptr, 0, K, qg::f32_src(x, qx, dx, sx), M, y, nullptr, nullptr,
+                             (hipStream_t)stream);
+}
+
+extern "C" int qgemv_q4k_f32(const void *W, int N, int K, const float *x, int M, float *y, int8_t *qx, float *dx,
+                             int32_t *sx, void *stream) {
+    if (!x) return QG_ERR_NULL;
+    return qg::gemv_dispatch(QG_FMT_Q4K, W, N, nullptr, 0, K, qg::f32_src(x, qx, dx, sx), M, y, nullptr, nullptr,
+                             (hipStream_t)stream);
+}
+
+extern "C" int qgemv_paired_f32(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const float *x, int M,
+                                float *y1, float *y2, int8_t *qx, float *dx, int32_t *sx, void *stream) {
+    if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4K) return QG_ERR_FORMAT;
+    if (!W2 || !y2 || !y1 || !x) return QG_ERR_NULL;
+    return qg::gemv_dispatch(fmt, W1, N1, W2, N2, K, qg::f32_src(x, qx, dx, sx), M, y1, y2, nullptr,
+                             (hipStream_t)stream);
 }
 
 extern "C" int qgemv_debug_block_isums(int fmt, const void *W, int N, int K, const int8_t *qx, int M, int32_t *isum,
@@ -166,6 +209,7 @@ extern "C" int qgemv_debug_block_isums(int fmt, const void *W, int N, int K, con
     // and only the exact integer sums are written.
     if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4K) return QG_ERR_FORMAT;
     if (!qx) return QG_ERR_NULL;
-    return qg::gemv_dispatch(fmt, W, N, nullptr, 0, K, qx, reinterpret_cast<const float *>(qx),
-                             reinterpret_cast<const int32_t *>(qx), M, nullptr, nullptr, isum, (hipStream_t)stream);
+    return qg::gemv_dispatch(fmt, W, N, nullptr, 0, K,
+                             qg::q8_src(qx, reinterpret_cast<const float *>(qx), reinterpret_cast<const int32_t *>(qx)),
+                             M, nullptr, nullptr, isum, (hipStream_t)stream);
 }

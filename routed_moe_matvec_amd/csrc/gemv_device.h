@@ -23,6 +23,7 @@
 #pragma once
 
 #include "common.h"
+#include "quantize_device.h"
 
 namespace qg {
 
@@ -217,10 +218,10 @@ __host__ __device__ inline int act_lds_bytes_per_token(int K) {
 // Tokens staged at once: bounded by the LDS budget and by what the staging
 // registers of a workgroup of `threads` hold.
 template <class U>
-inline int tokens_per_chunk(int K, int M, int threads) {
+inline int tokens_per_chunk(int K, int M, int threads, bool f32_input = false) {
     const int budget = min(kActLdsBudget, kLdsBytes - (threads / kWave) * TileSize<U>::lds);
     int mt = budget / act_lds_bytes_per_token<U>(K);
-    mt = min(mt, kActRegChunks * threads * 16 / K);
+    mt = min(mt, kActRegChunks * threads * (f32_input ? 4 : 16) / K);
     mt = min(mt, threads * 128 / K);
     return max(1, min(mt, M));
 }
@@ -293,6 +294,101 @@ struct ActStage {
     }
 };
 
+// Where a workgroup takes its activation from.  Either a Q8 activation
+// (qx/dx/sx, as quantize_act_q8 writes it), or the fp32 activation x, which
+// every workgroup quantizes itself while staging (the same 8-lane block
+// quantizer, so the records are bit-identical); workgroup 0 then also
+// publishes the Q8 activation to pqx/pdx/psx when they are given.
+struct ActSrc {
+    const int8_t *qx;
+    const float *dx;
+    const int32_t *sx;
+    const float *x;
+    int8_t *pqx;
+    float *pdx;
+    int32_t *psx;
+};
+
+// Staging from fp32: load() reads the first kActRegChunks 16-byte chunks
+// (4 values each) per thread into registers, store() quantizes each 32-block
+// on its 8 consecutive lanes and writes the records; chunks beyond what the
+// registers held are read and quantized in further passes inside store().
+template <int FMT, class U, int WAVES>
+struct ActStageF32 {
+    static constexpr int NT = WAVES * kWave;
+    static constexpr int REC = U::rec_dwords * 4;
+    float4 v[kActRegChunks];
+
+    template <class TokenRow>
+    __device__ __forceinline__ void load_pass(const float *__restrict__ x, int K, int m0, int mtc, int base,
+                                              TokenRow token_row) {
+        const int cpt = K / 4;
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k) {
+            const int c = base + (int)threadIdx.x + k * NT;
+            if (c < mtc * cpt) {
+                const int mm = c / cpt;
+                v[k] = reinterpret_cast<const float4 *>(x + (size_t)token_row(m0 + mm) * K)[c - mm * cpt];
+            }
+        }
+    }
+
+    template <class TokenRow>
+    __device__ __forceinline__ void load(const float *__restrict__ x, int K, int m0, int mtc, TokenRow token_row) {
+        load_pass(x, K, m0, mtc, 0, token_row);
+    }
+
+    template <class TokenRow>
+    __device__ __forceinline__ void store(uint8_t *lds, int K, int m0, int mtc, TokenRow token_row,
+                                          const ActSrc &src, bool publish) {
+        const int upr = K / U::weights;
+        const int cpt = K / 4;
+        const int total = mtc * cpt;
+        for (int base = 0; base < total; base += kActRegChunks * NT) {
+            if (base > 0) load_pass(src.x, K, m0, mtc, base, token_row);
+#pragma unroll
+            for (int k = 0; k < kActRegChunks; ++k) {
+                const int c = base + (int)threadIdx.x + k * NT;  // 8 consecutive lanes hold one 32-block
+                const bool valid = c < total;
+                float vals[4] = {0.f, 0.f, 0.f, 0.f};
+                if (valid) {
+                    vals[0] = v[k].x;
+                    vals[1] = v[k].y;
+                    vals[2] = v[k].z;
+                    vals[3] = v[k].w;
+                }
+                int8_t q[4];
+                float d;
+                int32_t s;
+                quantize_block_8lanes(vals, q, &d, &s);  // every lane takes part (shuffles)
+                if (valid) {
+                    const int mm = c / cpt;
+                    const int w = c - mm * cpt;
+                    const int blk = w >> 3, part = w & 7;
+                    const int u = blk / U::blocks, bi = blk - u * U::blocks;
+                    const uint32_t packed = (uint32_t)(uint8_t)q[0] | ((uint32_t)(uint8_t)q[1] << 8) |
+                                            ((uint32_t)(uint8_t)q[2] << 16) | ((uint32_t)(uint8_t)q[3] << 24);
+                    uint8_t *rec = lds + (size_t)(mm * upr + u) * REC;
+                    *reinterpret_cast<uint32_t *>(rec + 32 * bi + 4 * part) = packed;
+                    if (part == 0) {
+                        *reinterpret_cast<float *>(rec + U::weights + 4 * bi) = d;
+                        if constexpr (FMT == QG_FMT_Q4K)
+                            *reinterpret_cast<int32_t *>(rec + U::weights + 32 + 4 * bi) = s;
+                    }
+                    if (publish) {
+                        const size_t row = (size_t)token_row(m0 + mm);
+                        if (src.pqx) *reinterpret_cast<uint32_t *>(src.pqx + row * K + 32 * blk + 4 * part) = packed;
+                        if (part == 0) {
+                            if (src.pdx) src.pdx[row * (K / 32) + blk] = d;
+                            if (src.psx) src.psx[row * (K / 32) + blk] = s;
+                        }
+                    }
+                }
+            }
+        }
+    }
+};
+
 // ---------------------------------------------------------------- tile engine
 
 // Sum over the lpr lanes of a row with a fixed xor butterfly; every lane of
@@ -346,13 +442,13 @@ __device__ __forceinline__ void tile_to_unit(const TileRegs<U> &r, uint8_t *lw, 
 // tpw must be 1 (the tile stays in registers across chunks).  Every wave of
 // the workgroup must call this (it synchronizes).  PIPE = false limits tpw
 // to 1 and keeps only one tile register set; ONE = true is the M = 1 form
-// (no token loop, fewer live registers).
-template <int FMT, int NB, int WAVES, bool DEBUG_ISUM, bool PIPE, bool ONE, class TokenRow, class Out,
+// (no token loop, fewer live registers); F32 = true stages from the fp32
+// activation (quantizing it) instead of a Q8 activation.
+template <int FMT, int NB, int WAVES, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32, class TokenRow, class Out,
           class IsumOut>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, int N, int K, const TileGeom &tg,
-                                               int tile_base, int tpw, int ntiles, const int8_t *qx, const float *dx,
-                                               const int32_t *sx, int M, int mt, uint8_t *smem, TokenRow token_row,
-                                               Out out, IsumOut isum_out) {
+                                               int tile_base, int tpw, int ntiles, const ActSrc &src, int M, int mt,
+                                               uint8_t *smem, TokenRow token_row, Out out, IsumOut isum_out) {
     using U = Unit<FMT, NB>;
     constexpr int REC = U::rec_dwords * 4;
     const int wave = threadIdx.x / kWave;
@@ -382,14 +478,28 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
     TileRegs<U> ra, rb;
     UnitRegs<U> u;
     ActStage<FMT, U, WAVES> st;
+    ActStageF32<FMT, U, WAVES> stf;
+    const bool publish = F32 && blockIdx.x == 0 && blockIdx.y == 0;
+    auto act_load = [&](int m0, int mtc) {
+        if constexpr (F32)
+            stf.load(src.x, K, m0, mtc, token_row);
+        else
+            st.load(src.qx, src.dx, src.sx, K, m0, mtc, token_row);
+    };
+    auto act_store = [&](int m0, int mtc) {
+        if constexpr (F32)
+            stf.store(lact, K, m0, mtc, token_row, src, publish);
+        else
+            st.store(lact, K, mtc);
+    };
     if (ONE || M <= mt) {
         if (ONE) M = 1;
         // one chunk of tokens: activation reads first, then up to two tiles in
         // flight; tpw tiles in total
-        st.load(qx, dx, sx, K, 0, M, token_row);
+        act_load(0, M);
         if (tile0 < ntiles) load_tile<U>(W, N, tg, tile0, ra);
         if (PIPE && tpw > 1 && tile0 + 1 < ntiles) load_tile<U>(W, N, tg, tile0 + 1, rb);
-        st.store(lact, K, M);
+        act_store(0, M);
         __syncthreads();
         for (int i = 0; i < tpw; i += 2) {
             const int ta = tile0 + i, tb = tile0 + i + 1;
@@ -412,9 +522,9 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
         for (int m0 = 0; m0 < M; m0 += mt) {
             const int mtc = min(mt, M - m0);
             if (m0 > 0) __syncthreads();  // every wave is done with the previous chunk
-            st.load(qx, dx, sx, K, m0, mtc, token_row);
+            act_load(m0, mtc);
             if (m0 == 0 && tile0 < ntiles) load_tile<U>(W, N, tg, tile0, ra);
-            st.store(lact, K, mtc);
+            act_store(m0, mtc);
             __syncthreads();
             if (m0 == 0 && tile0 < ntiles) tile_to_unit<U>(ra, lw, r * tg.upr + g, v, u);
             if (tile0 < ntiles) compute(u, tile0, v, m0, mtc);

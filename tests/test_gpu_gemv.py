@@ -255,3 +255,60 @@ def test_gemv_errors_leave_outputs_untouched(qg):
     for fn, want in cases:
         assert fn() == want
     assert np.all(host(y) == 3.0)
+
+
+# ---------------------------------------------------------------- fused quantization
+
+@pytest.mark.parametrize("fmt,N,K,M", [(0, 4096, 8192, 1), (0, 300, 4096, 2), (1, 257, 4096, 1), (1, 70, 2048, 5),
+                                       (0, 33, 12288, 1), (0, 130, 1024, 9)])
+def test_fused_quantize_matches_two_step(qg, fmt, N, K, M):
+    """qgemv_*_f32 quantizes in the kernel: y equals quantize_act_q8 + qgemv_* bit for bit, and
+    the published Q8 activation equals quantize_act_q8's output."""
+    import torch
+    progress("fused fmt=%d N=%d K=%d M=%d" % (fmt, N, K, M))
+    g = np.random.default_rng(3000 + fmt + N + K + M)
+    W = dev(_weights(fmt, g, N, K))
+    x = synth.activations(g, M, K) * np.float32(3.0)
+    qx, dx, sx = gpu_quantize(qg, x)
+    ref = _run_gemv(qg, fmt, W, N, K, qx, dx, sx, M)
+    y = sentinel((M, N), torch.float32)
+    pq, pd, ps = sentinel((M, K), torch.int8, 5), sentinel((M, K // 32), torch.float32), \
+        sentinel((M, K // 32), torch.int32)
+    f = qg.qgemv_q8_0_f32 if fmt == 0 else qg.qgemv_q4k_f32
+    f(W, N, K, dev(x), M, y, pq, pd, ps)
+    assert np.array_equal(host(y).view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(host(pq), host(qx)) and np.array_equal(host(ps), host(sx))
+    assert np.array_equal(host(pd).view(np.uint32), host(dx).view(np.uint32))
+    y2 = sentinel((M, N), torch.float32)
+    f(W, N, K, dev(x), M, y2)  # without publishing
+    assert np.array_equal(host(y2).view(np.uint32), ref.view(np.uint32))
+
+
+def test_fused_paired(qg):
+    import torch
+    g = np.random.default_rng(3100)
+    K, N1, N2 = 4096, 1024, 512
+    for fmt in (0, 1):
+        W1, W2 = dev(_weights(fmt, g, N1, K)), dev(_weights(fmt, g, N2, K))
+        x = synth.activations(g, 2, K)
+        qx, dx, sx = gpu_quantize(qg, x)
+        for M in (1, 2):
+            y1, y2 = sentinel((M, N1), torch.float32), sentinel((M, N2), torch.float32)
+            pq, pd, ps = empty((M, K), torch.int8), empty((M, K // 32), torch.float32), \
+                empty((M, K // 32), torch.int32)
+            qg.qgemv_paired_f32(fmt, W1, N1, W2, N2, K, dev(x[:M].copy()), M, y1, y2, pq, pd, ps)
+            r1 = _run_gemv(qg, fmt, W1, N1, K, qx[:M], dx[:M], sx[:M], M)
+            r2 = _run_gemv(qg, fmt, W2, N2, K, qx[:M], dx[:M], sx[:M], M)
+            assert np.array_equal(host(y1), r1) and np.array_equal(host(y2), r2)
+            assert np.array_equal(host(pq), host(qx[:M])) and np.array_equal(host(ps), host(sx[:M]))
+
+
+def test_fused_errors(qg):
+    import torch
+    W = dev(synth.q8_0_weight(np.random.default_rng(1), 8, 512))
+    y = sentinel((1, 8), torch.float32, 2.0)
+    x = dev(np.zeros((1, 512), np.float32))
+    assert qg._c_q8_0_f32(W.data_ptr(), 8, 512, None, 1, y.data_ptr(), None, None, None, None) == -1
+    assert qg._c_q8_0_f32(W.data_ptr(), 8, 500, x.data_ptr(), 1, y.data_ptr(), None, None, None, None) == -2
+    assert qg._c_q8_0_f32(W.data_ptr(), 8, 512, x.data_ptr() + 4, 1, y.data_ptr(), None, None, None, None) == -3
+    assert np.all(host(y) == 2.0)
