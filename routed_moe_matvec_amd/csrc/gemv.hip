@@ -11,7 +11,7 @@
 
 namespace qg {
 
-constexpr int kGemvWaves = 8;
+constexpr int kGemvMaxWaves = 8;
 
 struct GemvArgs {
     const uint8_t *W0;
@@ -26,11 +26,12 @@ struct GemvArgs {
     int M;
     int mt;         // tokens staged in LDS per chunk
     int tpw;        // tiles per wave
+    int waves;      // waves per workgroup
     int32_t *isum;  // per-block sums of matrix 0 (test export), else unused
 };
 
 template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32>
-__global__ __launch_bounds__(kGemvWaves *kWave) void qgemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kGemvMaxWaves *kWave) void qgemv_kernel(GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // workgroups [0, nwg0) cover matrix 0, the rest matrix 1 (paired call)
     const bool second = (int)blockIdx.x >= a.nwg0;
@@ -41,8 +42,8 @@ __global__ __launch_bounds__(kGemvWaves *kWave) void qgemv_kernel(GemvArgs a) {
     const int nt = second ? a.nt1 : a.nt0;
     const int nb = a.K / 32;
     int32_t *isum = a.isum;
-    gemv_workgroup<FMT, NB, kGemvWaves, DEBUG_ISUM, PIPE, ONE, F32>(
-        W, N, a.K, a.tg, wg * kGemvWaves * a.tpw, a.tpw, nt, a.act, a.M, a.mt, smem,
+    gemv_workgroup<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>(
+        W, N, a.K, a.tg, wg * a.waves * a.tpw, a.tpw, nt, a.act, a.M, a.mt, smem,
         [](int m) { return m; }, [=](int m, int row, float v) { y[(size_t)m * N + row] = v; },
         [=](int m, int row, int unit, const int32_t *s) {
             int32_t *o = isum + ((size_t)m * N + row) * nb + unit * NB;
@@ -62,25 +63,34 @@ static int launch_kernel(const GemvArgs &a, int grid, size_t lds, hipStream_t st
             return QG_ERR_LAUNCH;
         attr_set = true;
     }
-    hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>), dim3(grid), dim3(kGemvWaves * kWave), lds, stream, a);
+    hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>), dim3(grid), dim3(a.waves * kWave), lds,
+                       stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
 template <int FMT, int NB, bool DEBUG_ISUM, bool F32>
 static int launch_gemv(GemvArgs &a, hipStream_t stream) {
     using U = Unit<FMT, NB>;
-    constexpr int threads = kGemvWaves * kWave;
     a.tg = make_tile_geom<U>(a.K);
     a.nt0 = (a.N0 + a.tg.rpt - 1) / a.tg.rpt;
     a.nt1 = a.W1 ? (a.N1 + a.tg.rpt - 1) / a.tg.rpt : 0;
+    const int cus = device_cu_count();
+    const int tiles = a.nt0 + a.nt1;
+    // waves per workgroup: 8 when there are tiles for 8-wave workgroups on
+    // every CU, else fewer so that the grid still spreads over the CUs
+    a.waves = kGemvMaxWaves;
+    while (a.waves > 1 && tiles < a.waves * cus) a.waves >>= 1;
+    const int threads = a.waves * kWave;
     a.mt = tokens_per_chunk<U>(a.K, a.M, threads, F32);
-    const size_t lds = gemv_lds_bytes<U>(kGemvWaves, a.K, a.mt);
+    const size_t lds = gemv_lds_bytes<U>(a.waves, a.K, a.mt);
     // about one round of resident waves (LDS bounds the workgroups per CU)
-    const int wg_per_cu = max(1, min(4, (int)((160 * 1024) / lds)));
-    // (the 8-block Q8_0 unit keeps one tile register set: two would spill)
-    a.tpw = tiles_per_wave(a.nt0 + a.nt1, device_cu_count() * wg_per_cu * kGemvWaves,
-                           a.M <= a.mt && !(FMT == QG_FMT_Q8_0 && NB == 8));
-    const int per_wg = kGemvWaves * a.tpw;
+    const int wg_per_cu = max(1, min(32 / a.waves, (int)(kLdsBytes / lds)));
+    // Two tiles per wave only pay when registers allow the extra set: for
+    // M = 1 more workgroups in staggered rounds measured faster, and the
+    // 8-block Q8_0 unit would spill.
+    a.tpw = tiles_per_wave(tiles, cus * wg_per_cu * a.waves,
+                           a.M > 1 && a.M <= a.mt && !(FMT == QG_FMT_Q8_0 && NB == 8));
+    const int per_wg = a.waves * a.tpw;
     a.nwg0 = (a.nt0 + per_wg - 1) / per_wg;
     const int grid = a.nwg0 + (a.nt1 + per_wg - 1) / per_wg;
     if (a.M == 1)

@@ -217,12 +217,13 @@ __host__ __device__ inline int act_lds_bytes_per_token(int K) {
 
 // Tokens staged at once: bounded by the LDS budget and by what the staging
 // registers of a workgroup of `threads` hold.
+// Tokens staged at once: bounded by the LDS budget, and preferably by what
+// one pass of the staging registers holds (larger rows take extra passes).
 template <class U>
 inline int tokens_per_chunk(int K, int M, int threads, bool f32_input = false) {
     const int budget = min(kActLdsBudget, kLdsBytes - (threads / kWave) * TileSize<U>::lds);
     int mt = budget / act_lds_bytes_per_token<U>(K);
     mt = min(mt, kActRegChunks * threads * (f32_input ? 4 : 16) / K);
-    mt = min(mt, threads * 128 / K);
     return max(1, min(mt, M));
 }
 
@@ -233,31 +234,37 @@ inline size_t gemv_lds_bytes(int waves, int K, int mt) {
 
 // Staging of one chunk of tokens [m0, m0 + mtc) of the Q8 activation into
 // padded per-unit LDS records, split in two halves: load() issues the global
-// reads into registers, store() writes the records.  Between the two the
-// caller issues its weight loads, which then stay in flight (the waits for
-// the activation registers only cover loads issued before them).
-// Needs mtc*K/16 <= kActRegChunks*threads and mtc*K/128 <= threads.
-template <int FMT, class U, int WAVES>
+// reads of the first slice into registers, store() writes the records (and
+// reads and writes whatever did not fit the registers in further passes).
+// Between the two the caller issues its weight loads, which then stay in
+// flight: the waits for the activation registers only cover loads issued
+// before them.
+template <int FMT, class U>
 struct ActStage {
-    static constexpr int NT = WAVES * kWave;
     static constexpr int REC = U::rec_dwords * 4;
     u32x4 q[kActRegChunks];
     u32x4 d, s;
 
     template <class TokenRow>
-    __device__ __forceinline__ void load(const int8_t *__restrict__ qx, const float *__restrict__ dx,
-                                         const int32_t *__restrict__ sx, int K, int m0, int mtc, TokenRow token_row) {
+    __device__ __forceinline__ void load_quants(const int8_t *__restrict__ qx, int K, int m0, int mtc, int base,
+                                                TokenRow token_row) {
+        const int NT = blockDim.x;
         const int cpt = K / 16;
 #pragma unroll
         for (int k = 0; k < kActRegChunks; ++k) {
-            const int c = (int)threadIdx.x + k * NT;
+            const int c = base + (int)threadIdx.x + k * NT;
             if (c < mtc * cpt) {
                 const int mm = c / cpt;
                 q[k] = reinterpret_cast<const u32x4 *>(qx + (size_t)token_row(m0 + mm) * K)[c - mm * cpt];
             }
         }
+    }
+
+    template <class TokenRow>
+    __device__ __forceinline__ void load_scales(const float *__restrict__ dx, const int32_t *__restrict__ sx, int K,
+                                                int m0, int mtc, int base, TokenRow token_row) {
         const int spt = K / 128;
-        const int c = threadIdx.x;
+        const int c = base + (int)threadIdx.x;
         if (c < mtc * spt) {
             const int mm = c / spt;
             const size_t src = (size_t)token_row(m0 + mm) * (K / 32) / 4 + (c - mm * spt);
@@ -266,30 +273,47 @@ struct ActStage {
         }
     }
 
-    __device__ __forceinline__ void store(uint8_t *lds, int K, int mtc) const {
+    template <class TokenRow>
+    __device__ __forceinline__ void load(const int8_t *__restrict__ qx, const float *__restrict__ dx,
+                                         const int32_t *__restrict__ sx, int K, int m0, int mtc, TokenRow token_row) {
+        load_quants(qx, K, m0, mtc, 0, token_row);
+        load_scales(dx, sx, K, m0, mtc, 0, token_row);
+    }
+
+    template <class TokenRow>
+    __device__ __forceinline__ void store(uint8_t *lds, const int8_t *__restrict__ qx, const float *__restrict__ dx,
+                                          const int32_t *__restrict__ sx, int K, int m0, int mtc,
+                                          TokenRow token_row) {
+        const int NT = blockDim.x;
         constexpr int QC = U::weights / 16;  // 16-byte chunks of quants per unit
         constexpr int SC = U::blocks / 4;    // 16-byte chunks of scales per unit
         const int upr = K / U::weights;
         const int cpt = K / 16;
+        for (int base = 0; base < mtc * cpt; base += kActRegChunks * NT) {
+            if (base > 0) load_quants(qx, K, m0, mtc, base, token_row);
 #pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k) {
-            const int c = (int)threadIdx.x + k * NT;
-            if (c < mtc * cpt) {
-                const int mm = c / cpt;
-                const int w = c - mm * cpt;
-                const int u = w / QC;
-                *reinterpret_cast<u32x4 *>(lds + (size_t)(mm * upr + u) * REC + (w - u * QC) * 16) = q[k];
+            for (int k = 0; k < kActRegChunks; ++k) {
+                const int c = base + (int)threadIdx.x + k * NT;
+                if (c < mtc * cpt) {
+                    const int mm = c / cpt;
+                    const int w = c - mm * cpt;
+                    const int u = w / QC;
+                    *reinterpret_cast<u32x4 *>(lds + (size_t)(mm * upr + u) * REC + (w - u * QC) * 16) = q[k];
+                }
             }
         }
         const int spt = K / 128;
-        const int c = threadIdx.x;
-        if (c < mtc * spt) {
-            const int mm = c / spt;
-            const int w = c - mm * spt;
-            const int u = w / SC;
-            uint8_t *rec = lds + (size_t)(mm * upr + u) * REC + U::weights + (w - u * SC) * 16;
-            *reinterpret_cast<u32x4 *>(rec) = d;
-            if constexpr (FMT == QG_FMT_Q4K) *reinterpret_cast<u32x4 *>(rec + 32) = s;
+        for (int base = 0; base < mtc * spt; base += NT) {
+            if (base > 0) load_scales(dx, sx, K, m0, mtc, base, token_row);
+            const int c = base + (int)threadIdx.x;
+            if (c < mtc * spt) {
+                const int mm = c / spt;
+                const int w = c - mm * spt;
+                const int u = w / SC;
+                uint8_t *rec = lds + (size_t)(mm * upr + u) * REC + U::weights + (w - u * SC) * 16;
+                *reinterpret_cast<u32x4 *>(rec) = d;
+                if constexpr (FMT == QG_FMT_Q4K) *reinterpret_cast<u32x4 *>(rec + 32) = s;
+            }
         }
     }
 };
@@ -313,15 +337,15 @@ struct ActSrc {
 // (4 values each) per thread into registers, store() quantizes each 32-block
 // on its 8 consecutive lanes and writes the records; chunks beyond what the
 // registers held are read and quantized in further passes inside store().
-template <int FMT, class U, int WAVES>
+template <int FMT, class U>
 struct ActStageF32 {
-    static constexpr int NT = WAVES * kWave;
     static constexpr int REC = U::rec_dwords * 4;
     float4 v[kActRegChunks];
 
     template <class TokenRow>
     __device__ __forceinline__ void load_pass(const float *__restrict__ x, int K, int m0, int mtc, int base,
                                               TokenRow token_row) {
+        const int NT = blockDim.x;
         const int cpt = K / 4;
 #pragma unroll
         for (int k = 0; k < kActRegChunks; ++k) {
@@ -341,6 +365,7 @@ struct ActStageF32 {
     template <class TokenRow>
     __device__ __forceinline__ void store(uint8_t *lds, int K, int m0, int mtc, TokenRow token_row,
                                           const ActSrc &src, bool publish) {
+        const int NT = blockDim.x;
         const int upr = K / U::weights;
         const int cpt = K / 4;
         const int total = mtc * cpt;
@@ -434,7 +459,7 @@ __device__ __forceinline__ void tile_to_unit(const TileRegs<U> &r, uint8_t *lw, 
     if (valid) read_unit<U>(lw + unit_index * U::bytes, u);
 }
 
-// The workgroup engine.  Wave w of the workgroup processes tiles
+// The workgroup engine (blockDim.x / 64 waves).  Wave w of the workgroup processes tiles
 // tile_base + w*tpw + i (i < tpw, tile < ntiles) of matrix W against M tokens.
 // token_row(m) gives the activation row of token m; out(m, row, v) stores one
 // result; isum_out(m, row, unit, sums) receives the exact block sums when
@@ -444,7 +469,7 @@ __device__ __forceinline__ void tile_to_unit(const TileRegs<U> &r, uint8_t *lw, 
 // to 1 and keeps only one tile register set; ONE = true is the M = 1 form
 // (no token loop, fewer live registers); F32 = true stages from the fp32
 // activation (quantizing it) instead of a Q8 activation.
-template <int FMT, int NB, int WAVES, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32, class TokenRow, class Out,
+template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32, class TokenRow, class Out,
           class IsumOut>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, int N, int K, const TileGeom &tg,
                                                int tile_base, int tpw, int ntiles, const ActSrc &src, int M, int mt,
@@ -454,7 +479,7 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     uint8_t *lw = smem + wave * TileSize<U>::lds;
-    uint8_t *lact = smem + WAVES * TileSize<U>::lds;
+    uint8_t *lact = smem + (blockDim.x / kWave) * TileSize<U>::lds;
     const int tile0 = tile_base + wave * tpw;
     const int r = lane >> tg.lsh;
     const int g = lane & (tg.lpr - 1);
@@ -477,8 +502,8 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
 
     TileRegs<U> ra, rb;
     UnitRegs<U> u;
-    ActStage<FMT, U, WAVES> st;
-    ActStageF32<FMT, U, WAVES> stf;
+    ActStage<FMT, U> st;
+    ActStageF32<FMT, U> stf;
     const bool publish = F32 && blockIdx.x == 0 && blockIdx.y == 0;
     auto act_load = [&](int m0, int mtc) {
         if constexpr (F32)
@@ -490,7 +515,7 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
         if constexpr (F32)
             stf.store(lact, K, m0, mtc, token_row, src, publish);
         else
-            st.store(lact, K, mtc);
+            st.store(lact, src.qx, src.dx, src.sx, K, m0, mtc, token_row);
     };
     if (ONE || M <= mt) {
         if (ONE) M = 1;

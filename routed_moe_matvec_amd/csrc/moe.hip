@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
     act.qx = a.qx;
     act.dx = a.dx;
     act.sx = a.sx;
-    gemv_workgroup<QG_FMT_Q4K, 8, kMoeWaves, false, false, false, false>(
+    gemv_workgroup<QG_FMT_Q4K, 8, false, false, false, false>(
         W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, cnt, a.mt, smem,
         [=](int m) { return pairs[m] / topk; },
         [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; },
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     act.qx = a.ws.hq;
     act.dx = a.ws.hd;
     act.sx = a.ws.hs;
-    gemv_workgroup<QG_FMT_Q4K, 8, kMoeWaves, false, false, false, false>(
+    gemv_workgroup<QG_FMT_Q4K, 8, false, false, false, false>(
         W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, act, cnt, a.mt, smem,
         [=](int m) { return pairs[m]; }, [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; },
         [](int, int, int, const int32_t *) {});
