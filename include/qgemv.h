@@ -250,6 +250,30 @@ int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t *sx, int T
  */
 int qgemm_prefill(int fmt, const void *W, int N, int K, const uint16_t *x_bf16, int M, float *y, void *stream);
 
+/*
+ * qgemm_prefill_workspace_bytes -- size of the device workspace that
+ * qgemm_prefill_ws needs for M tokens of K inputs (x as fp16 [M, K] and the
+ * per-32-input sums of x split into two fp16 halves [M, K/32] each, every
+ * region 256-byte aligned).  Returns 0 for an invalid shape (the rules of
+ * qgemm_prefill).
+ */
+size_t qgemm_prefill_workspace_bytes(int M, int K);
+
+/*
+ * qgemm_prefill_ws -- [PR621] the same product as qgemm_prefill, with the
+ * bf16 -> fp16 conversion of x and its 32-input sums done once by a separate
+ * pass into the caller's workspace, so that the GEMM reads them instead of
+ * converting x once per 128-row weight tile.  Results are bit-identical to
+ * qgemm_prefill.  ws is device memory owned by the caller (at least
+ * qgemm_prefill_workspace_bytes(M, K) bytes, 16-byte aligned); its contents on
+ * entry are ignored and on return are unspecified.  Calls that share a
+ * workspace must be ordered on one stream.
+ * Errors: as qgemm_prefill, plus QG_ERR_NULL for ws, QG_ERR_ALIGN for a
+ * misaligned ws and QG_ERR_WORKSPACE if ws_bytes is too small.
+ */
+int qgemm_prefill_ws(int fmt, const void *W, int N, int K, const uint16_t *x_bf16, int M, float *y, void *ws,
+                     size_t ws_bytes, void *stream);
+
 /* ---- diagnostics ------------------------------------------------------- */
 /* Human-readable text for a QG_* status or QG_DEV_* value (static storage). */
 const char *qg_status_string(int status);

@@ -18,7 +18,7 @@ __all__ = [
     "QGError", "FMT_Q8_0", "FMT_Q4K", "library_path", "quantize_act_q8", "qgemv_q8_0", "qgemv_q4k",
     "qgemv_paired", "moe_routed_workspace_bytes", "moe_routed_workspace_layout", "moe_routed_qgemv",
     "qgemm_prefill", "qg_status_string", "qgemv_debug_block_isums", "pointer_table", "WS_REGIONS",
-    "qgemv_q8_0_f32", "qgemv_q4k_f32", "qgemv_paired_f32",
+    "qgemv_q8_0_f32", "qgemv_q4k_f32", "qgemv_paired_f32", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
 ]
 
 FMT_Q8_0 = 0
@@ -58,17 +58,13 @@ _c_q8_0_f32 = _sig("qgemv_q8_0_f32", _i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp, _
 _c_q4k_f32 = _sig("qgemv_q4k_f32", _i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp])
 _c_paired_f32 = _sig("qgemv_paired_f32", _i, [_i, _vp, _i, _vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp])
 _c_status = _sig("qg_status_string", ctypes.c_char_p, [_i])
-try:
-    _c_ws_bytes = _sig("moe_routed_workspace_bytes", _sz, [_i, _i, _i, _i, _i])
-    _c_ws_layout = _sig("moe_routed_workspace_layout", _i, [_i, _i, _i, _i, _i, _vp])
-    _c_moe = _sig("moe_routed_qgemv", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                          _sz, _vp, _vp])
-except AttributeError:  # library built before the MoE sources existed
-    _c_ws_bytes = _c_ws_layout = _c_moe = None
-try:
-    _c_prefill = _sig("qgemm_prefill", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
-except AttributeError:
-    _c_prefill = None
+_c_ws_bytes = _sig("moe_routed_workspace_bytes", _sz, [_i, _i, _i, _i, _i])
+_c_ws_layout = _sig("moe_routed_workspace_layout", _i, [_i, _i, _i, _i, _i, _vp])
+_c_moe = _sig("moe_routed_qgemv", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _sz, _vp, _vp])
+_c_prefill = _sig("qgemm_prefill", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
+_c_prefill_ws_bytes = _sig("qgemm_prefill_workspace_bytes", _sz, [_i, _i])
+_c_prefill_ws = _sig("qgemm_prefill_ws", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp, _sz, _vp])
 
 
 class QGError(RuntimeError):
@@ -171,3 +167,12 @@ def moe_routed_qgemv(qx, dx, sx, T: int, D: int, F: int, E: int, topk: int, ids,
 
 def qgemm_prefill(fmt: int, W, N: int, K: int, x_bf16, M: int, y, stream=None) -> None:
     _ok(_c_prefill(fmt, _ptr(W), N, K, _ptr(x_bf16), M, _ptr(y), _stream(stream, W)), "qgemm_prefill")
+
+
+def qgemm_prefill_workspace_bytes(M: int, K: int) -> int:
+    return int(_c_prefill_ws_bytes(M, K))
+
+
+def qgemm_prefill_ws(fmt: int, W, N: int, K: int, x_bf16, M: int, y, ws, ws_bytes: int, stream=None) -> None:
+    _ok(_c_prefill_ws(fmt, _ptr(W), N, K, _ptr(x_bf16), M, _ptr(y), _ptr(ws), ws_bytes, _stream(stream, W)),
+        "qgemm_prefill_ws")

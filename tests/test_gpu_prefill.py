@@ -18,25 +18,98 @@ def qg():
     return qg
 
 
-def run_prefill(qg, W, N, K, xb, M):
+VARIANTS = ["plain", "ws"]
+
+
+def run_prefill(qg, W, N, K, xb, M, variant="plain"):
+    """qgemm_prefill (conversion inside the GEMM) or qgemm_prefill_ws (pre-pass
+    into a workspace, which starts filled with garbage)."""
     import torch
     y = sentinel((M, N), torch.float32, 99.0)
-    qg.qgemm_prefill(qg.FMT_Q4K, dev(W), N, K, dev(xb.view(np.int16)), M, y)
+    if variant == "plain":
+        qg.qgemm_prefill(qg.FMT_Q4K, dev(W), N, K, dev(xb.view(np.int16)), M, y)
+    else:
+        nb = qg.qgemm_prefill_workspace_bytes(M, K)
+        ws = sentinel((nb,), torch.uint8, 0xA5)
+        qg.qgemm_prefill_ws(qg.FMT_Q4K, dev(W), N, K, dev(xb.view(np.int16)), M, y, ws, nb)
     return host(y)
 
 
-@pytest.mark.parametrize("N,K,M", [(96, 512, 40), (130, 1280, 129), (256, 1024, 256), (1, 256, 1), (300, 2304, 7)])
-def test_prefill_parity_small(qg, orc, N, K, M):
-    progress("prefill N=%d K=%d M=%d" % (N, K, M))
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("N,K,M", [(96, 512, 40), (130, 1280, 129), (256, 1024, 256), (1, 256, 1), (300, 2304, 7),
+                                   (200, 2560, 300)])
+def test_prefill_parity_small(qg, orc, N, K, M, variant):
+    """Ragged N and M tails, K of 1..10 superblocks (partial min-term windows)."""
+    progress("prefill %s N=%d K=%d M=%d" % (variant, N, K, M))
     g = np.random.default_rng(500 + N + K + M)
     W = synth.q4k_weight(g, N, K)
     xb = synth.bf16_activations(g, M, K)
-    y = run_prefill(qg, W, N, K, xb, M)
+    y = run_prefill(qg, W, N, K, xb, M, variant)
     ref, bound = orc.prefill(orc.FMT_Q4K, W, N, K, xb, nthreads=oracle_threads())
-    assert_within_bound(y, ref, bound, what="prefill N=%d K=%d M=%d" % (N, K, M))
+    assert_within_bound(y, ref, bound, what="prefill %s N=%d K=%d M=%d" % (variant, N, K, M))
 
 
-def test_prefill_integer_weights_exact(qg):
+def scaled_bf16(xb, scale):
+    import torch
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).float() * scale
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+@pytest.mark.parametrize("scale", [2.0 ** 40, 2.0 ** -40, 1.0])
+def test_prefill_ws_activation_range(qg, orc, scale):
+    """The pre-pass scales each token by a power of two, so activations far outside
+    fp16's range (and rows mixing magnitudes 2^20 apart) stay within the bound."""
+    progress("prefill ws activation scale 2^%d" % int(np.log2(scale)))
+    g = np.random.default_rng(77)
+    N, K, M = 144, 1024, 20
+    W = synth.q4k_weight(g, N, K)
+    xb = synth.bf16_activations(g, M, K)
+    xb = scaled_bf16(xb, scale)
+    xb[3] = scaled_bf16(xb[3:4], 2.0 ** -20)[0]  # one quiet token
+    xb[5, :100] = scaled_bf16(xb[5:6, :100], 2.0 ** 10)[0]  # one token with loud early inputs
+    xb[7] = 0  # an all-zero token
+    y = run_prefill(qg, W, N, K, xb, M, "ws")
+    ref, bound = orc.prefill(orc.FMT_Q4K, W, N, K, xb, nthreads=oracle_threads())
+    assert_within_bound(y, ref, bound, what="prefill ws scale %g" % scale)
+    assert np.all(y[7] == 0.0)
+
+
+def set_scales(W, N, K, d, dmin):
+    """Overwrite the fp16 d and dmin of every superblock of a Q4_K matrix."""
+    sb = W.reshape(N, K // 256, 144)
+    sb[:, :, 0:2] = np.asarray(d, np.float16).view(np.uint8).reshape(N, K // 256, 2)
+    sb[:, :, 2:4] = np.asarray(dmin, np.float16).view(np.uint8).reshape(N, K // 256, 2)
+    return W
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("kind", ["large", "tiny", "mixed"])
+def test_prefill_scale_range(qg, orc, variant, kind):
+    """d and dmin across fp16's range: large (0.05 .. 60000), tiny (1e-7 .. 1e-6,
+    partly subnormal) and mixed (log-uniform over 6e-8 .. 65504 per superblock, so a
+    row's superblocks differ by up to 2^30): the min term's per-window power-of-two
+    scaling keeps every output within the bound."""
+    progress("prefill %s d/dmin %s" % (variant, kind))
+    g = np.random.default_rng(78)
+    N, K, M = 80, 2048, 24
+    W = synth.q4k_weight(g, N, K)
+    shape = (N, K // 256)
+    if kind == "large":
+        d, dmin = g.uniform(0.05, 60000, shape), g.uniform(0.05, 60000, shape)
+    elif kind == "tiny":
+        d, dmin = g.uniform(1e-7, 1e-6, shape), g.uniform(1e-7, 1e-6, shape)
+    else:
+        d = np.exp(g.uniform(np.log(6e-8), np.log(65504), shape))
+        dmin = np.exp(g.uniform(np.log(6e-8), np.log(65504), shape))
+    W = set_scales(W, N, K, d, dmin)
+    xb = synth.bf16_activations(g, M, K)
+    y = run_prefill(qg, W, N, K, xb, M, variant)
+    ref, bound = orc.prefill(orc.FMT_Q4K, W, N, K, xb, nthreads=oracle_threads())
+    assert_within_bound(y, ref, bound, what="prefill %s scales %s" % (variant, kind))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_prefill_integer_weights_exact(qg, variant):
     """d = 1, dmin = 0 and small-integer activations: every partial sum is an integer
     below 2^24, so Y equals the int64 matmul exactly."""
     import torch
@@ -49,26 +122,27 @@ def test_prefill_integer_weights_exact(qg):
     W = fh.pack_q4k_matrix(np.ones((N, S)), np.zeros((N, S)), sc, m, q)
     xi = g.integers(-4, 5, size=(M, K))
     xb = torch.from_numpy(xi.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    y = run_prefill(qg, W, N, K, xb, M)
+    y = run_prefill(qg, W, N, K, xb, M, variant)
     Wi = (sc[..., None] * q).reshape(N, K).astype(np.int64)
     assert np.array_equal(y.astype(np.float64), (xi @ Wi.T).astype(np.float64))
 
 
-def test_prefill_full_size_sampled_rows(qg, orc):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_prefill_full_size_sampled_rows(qg, orc, variant):
     """The 512-token prefill of the 4096 -> 8192 Q4_K projection; 96 sampled weight rows
     checked against the oracle for all 512 tokens."""
-    progress("prefill 512x8192x4096")
+    progress("prefill %s 512x8192x4096" % variant)
     w = synth.WORKLOADS["q4k_prefill_512x8192x4096"]
     g = synth.rng(w["seed"])
     N, K, M = w["N"], w["K"], w["M"]
     W = synth.q4k_weight(g, N, K)
     xb = synth.bf16_activations(g, M, K)
-    y = run_prefill(qg, W, N, K, xb, M)
+    y = run_prefill(qg, W, N, K, xb, M, variant)
     rows = np.sort(np.random.default_rng(9).choice(N, 96, replace=False))
     ref, bound = orc.prefill(orc.FMT_Q4K, W[rows], len(rows), K, xb, nthreads=oracle_threads())
     assert_within_bound(y[:, rows], ref, bound, what="prefill full")
     # deterministic and row-independent of the batch: token 77 alone gives the same row
-    y1 = run_prefill(qg, W, N, K, xb[77:78].copy(), 1)
+    y1 = run_prefill(qg, W, N, K, xb[77:78].copy(), 1, variant)
     assert np.array_equal(y1[0].view(np.uint32), y[77].view(np.uint32))
 
 
@@ -83,4 +157,21 @@ def test_prefill_errors(qg):
     assert c(1, W.data_ptr(), 8, 300, x.data_ptr(), 4, y.data_ptr(), None) == -2
     assert c(1, W.data_ptr(), 8, 512, x.data_ptr(), 0, y.data_ptr(), None) == -2
     assert c(1, W.data_ptr() + 4, 8, 512, x.data_ptr(), 4, y.data_ptr(), None) == -3
+    assert np.all(host(y) == 1.0)
+
+
+def test_prefill_ws_errors(qg):
+    import torch
+    W = dev(synth.q4k_weight(np.random.default_rng(1), 8, 512))
+    x = dev(np.zeros((4, 512), np.int16))
+    y = sentinel((4, 8), torch.float32, 1.0)
+    nb = qg.qgemm_prefill_workspace_bytes(4, 512)
+    ws = torch.zeros(nb + 64, dtype=torch.uint8, device=x.device)
+    c = qg._c_prefill_ws
+    assert c(1, W.data_ptr(), 8, 512, x.data_ptr(), 4, y.data_ptr(), None, nb, None) == -1
+    assert c(1, W.data_ptr(), 8, 512, x.data_ptr(), 4, y.data_ptr(), ws.data_ptr(), nb - 1, None) == -5
+    assert c(1, W.data_ptr(), 8, 512, x.data_ptr(), 4, y.data_ptr(), ws.data_ptr() + 8, nb, None) == -3
+    assert c(0, W.data_ptr(), 8, 512, x.data_ptr(), 4, y.data_ptr(), ws.data_ptr(), nb, None) == -4
+    assert c(1, W.data_ptr(), 8, 300, x.data_ptr(), 4, y.data_ptr(), ws.data_ptr(), nb, None) == -2
+    torch.cuda.synchronize()
     assert np.all(host(y) == 1.0)

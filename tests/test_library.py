@@ -71,6 +71,12 @@ def test_host_validation_without_gpu(lib):
     p = lib.qgemm_prefill
     p.argtypes = [ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp]
     assert p(0, fake, 8, 512, fake, 4, fake, None) == -4
+    pw = lib.qgemm_prefill_ws
+    pw.argtypes = [ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
+    assert pw(1, fake, 8, 512, fake, 4, fake, None, 1 << 20, None) == -1
+    assert pw(1, fake, 8, 512, fake, 4, fake, fake, 100, None) == -5
+    assert pw(1, fake, 8, 512, fake, 4, fake, vp((1 << 40) + 8), 1 << 20, None) == -3
+    assert pw(1, fake, 8, 768 + 1, fake, 4, fake, fake, 1 << 20, None) == -2
 
 
 def test_moe_workspace_sizing():
@@ -90,3 +96,13 @@ def test_moe_workspace_sizing():
     assert qg.moe_routed_workspace_bytes(2000, 6, 256, 4096, 2048) == 0  # more than 8192 pairs
     with pytest.raises(qg.QGError):
         qg.moe_routed_workspace_layout(0, 6, 256, 4096, 2048)
+
+
+def test_prefill_workspace_sizing():
+    import routed_moe_matvec_amd as qg
+    for M, K in [(1, 256), (7, 2304), (512, 4096), (300, 16384)]:
+        nb = qg.qgemm_prefill_workspace_bytes(M, K)
+        assert nb >= 2 * M * K + 2 * (2 * M * K // 32) + 4 * M, (M, K)
+        assert nb % 256 == 0 and nb <= 2 * M * K + 2 * (2 * M * K // 32) + 4 * M + 4 * 256
+    for M, K in [(0, 256), (4, 300), (4, 128), (4, 16384 + 256)]:
+        assert qg.qgemm_prefill_workspace_bytes(M, K) == 0, (M, K)
