@@ -21,6 +21,11 @@ MoE tokens/s, prefill) measured the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --summarize-rocprof DIR   (turn rocprofv3 csv output into a text summary)
+       python bench.py --probe {gemv,copy,prefill,prefill_ws} --steps K
+                 (eager launches of one kernel, for rocprofv3 --pmc counter runs)
+       python bench.py --summarize-pmc GEMV_FETCH GEMV_WRITE COPY_FETCH COPY_WRITE
+                 (HBM bytes per launch of the GEMV from FETCH_SIZE / WRITE_SIZE runs,
+                  scaled by the copy kernel's counters; writes profiles/pmc_traffic.json)
 """
 from __future__ import annotations
 
@@ -42,12 +47,17 @@ ROTATE_BYTES = 1 << 30  # > 2x the 256 MB Infinity Cache
 METRIC = "decode GEMV µs and achieved HBM GB/s (% of peak); routed-MoE tokens/s"
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources; profile summaries record it so stale counters are detected."""
+GEMV_SOURCES = ("csrc/gemv.hip", "csrc/gemv_device.h", "csrc/quantize_device.h", "csrc/common.h",
+                "../include/qgemv.h")
+
+
+def kernel_source_hash(files=GEMV_SOURCES) -> str:
+    """Hash of the sources the GEMV kernel is compiled from; counter summaries record it, so
+    counters taken on an older kernel are detected and not reported."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "routed_moe_matvec_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    pkg = os.path.join(ROOT, "routed_moe_matvec_amd")
+    for name in files:
+        with open(os.path.normpath(os.path.join(pkg, name)), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
@@ -196,9 +206,8 @@ def cpu_baseline(step: DecodeStep, budget_s: float = 12.0) -> dict:
 def load_traffic(kernel_key: str, src_hash: str):
     """Measured HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
-        with open(path) as f:
+        with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
@@ -372,6 +381,124 @@ def summarize_rocprof(path: str) -> str:
     return "\n".join(lines)
 
 
+
+# ----------------------------------------------------------------------------- counter runs
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_q8_0_4096x8192_hbm_traffic.json")
+COPY_PROBE_BYTES = 1 << 29  # 512 MiB read + 512 MiB written per copy launch
+
+
+def run_probe(name: str, steps: int, warmup: int, qg, torch) -> None:
+    """Eager launches (no graph, so counters attribute per dispatch) of one kernel,
+    rotating weights like the timed runs."""
+    import synth
+    stream = torch.cuda.current_stream()
+    if name == "gemv":
+        step = DecodeStep(qg, torch)
+        step.step(0)  # quantized activations for the projection
+        fn = step.out_gemv
+    elif name == "copy":
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+
+        def fn(i):
+            dst.copy_(src)
+    elif name in ("prefill", "prefill_ws"):
+        w = synth.WORKLOADS["q4k_prefill_512x8192x4096"]
+        g = synth.rng(w["seed"])
+        N, K, M = w["N"], w["K"], w["M"]
+        W_host = synth.q4k_weight(g, N, K)
+        R = rotation_count(W_host.nbytes)
+        base = torch.from_numpy(W_host).to("cuda")
+        copies = [base] + [base.clone() for _ in range(R - 1)]
+        xb = torch.from_numpy(synth.bf16_activations(g, M, K).view(np.int16)).to("cuda")
+        y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+        nb = qg.qgemm_prefill_workspace_bytes(M, K)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        if name == "prefill":
+            def fn(i):
+                qg.qgemm_prefill(qg.FMT_Q4K, copies[i % R], N, K, xb, M, y)
+        else:
+            def fn(i):
+                qg.qgemm_prefill_ws(qg.FMT_Q4K, copies[i % R], N, K, xb, M, y, ws, nb)
+    else:
+        raise SystemExit("unknown probe %r" % name)
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    print("probe %s: %d launches, %.3f us each (host clock, eager)" % (
+        name, steps, (time.perf_counter() - t0) / steps * 1e6), flush=True)
+    del stream
+
+
+def pmc_values(path: str) -> dict:
+    """{(kernel name, counter): mean value per dispatch} from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    acc = {}
+    for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (r.get("Kernel_Name", "?"), r.get("Counter_Name", "?"))
+                acc.setdefault(key, []).append(float(r.get("Counter_Value", "nan")))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def pick(vals: dict, counter: str, needle: str):
+    hits = [(k, v) for k, v in vals.items() if k[1] == counter and needle in k[0]]
+    if not hits:
+        raise SystemExit("no %s value for a kernel matching %r" % (counter, needle))
+    return max(hits, key=lambda kv: kv[1])
+
+
+def summarize_pmc(gf: str, gw: str, cf: str, cw: str) -> str:
+    """HBM traffic per GEMV launch: FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    the factor that makes the same counter read exactly the copy kernel's known bytes."""
+    (gk, g_fetch) = pick(pmc_values(gf), "FETCH_SIZE", "qgemv_kernel")
+    (_, g_write) = pick(pmc_values(gw), "WRITE_SIZE", "qgemv_kernel")
+    (ck, c_fetch) = pick(pmc_values(cf), "FETCH_SIZE", "")
+    (_, c_write) = pick(pmc_values(cw), "WRITE_SIZE", "")
+    known_kib = COPY_PROBE_BYTES / 1024.0
+    f_read, f_write = known_kib / c_fetch, known_kib / c_write
+    hbm = (g_fetch * f_read + g_write * f_write) * 1024.0
+    ent = {
+        "kernel": gk[0][:120], "source_hash": kernel_source_hash(),
+        "fetch_kib_per_dispatch": round(g_fetch, 1), "write_kib_per_dispatch": round(g_write, 1),
+        "copy_kernel": ck[0][:120], "copy_bytes": COPY_PROBE_BYTES,
+        "copy_fetch_kib": round(c_fetch, 1), "copy_write_kib": round(c_write, 1),
+        "read_scale": round(f_read, 4), "write_scale": round(f_write, 4),
+        "hbm_bytes_per_launch": int(round(hbm)),
+    }
+    pmc = "rocprofv3 --output-format csv --pmc %s -d %s -o run -- python3 -u bench.py --probe %s --steps %d --warmup %d"
+    ent["commands"] = [
+        pmc % ("FETCH_SIZE", gf, "gemv", 50, 5), pmc % ("WRITE_SIZE", gw, "gemv", 50, 5),
+        pmc % ("FETCH_SIZE", cf, "copy", 5, 1), pmc % ("WRITE_SIZE", cw, "copy", 5, 1),
+        "python3 bench.py --summarize-pmc %s %s %s %s" % (gf, gw, cf, cw)]
+    ent["note"] = ("FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is multiplied by the factor that makes "
+                   "the same counter equal the known bytes of a %d-byte device copy" % COPY_PROBE_BYTES)
+    pmc = "rocprofv3 --output-format csv --pmc %s -d %s -o run -- python3 -u bench.py --probe %s --steps %d --warmup %d"
+    ent["commands"] = [
+        pmc % ("FETCH_SIZE", gf, "gemv", 50, 5), pmc % ("WRITE_SIZE", gw, "gemv", 50, 5),
+        pmc % ("FETCH_SIZE", cf, "copy", 5, 1), pmc % ("WRITE_SIZE", cw, "copy", 5, 1),
+        "python3 bench.py --summarize-pmc %s %s %s %s" % (gf, gw, cf, cw)]
+    ent["note"] = ("FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is multiplied by the factor that makes "
+                   "the same counter equal the known bytes of a %d-byte device copy" % COPY_PROBE_BYTES)
+    path = TRAFFIC_FILE
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data["qgemv_q8_0_4096x8192"] = ent
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return json.dumps(ent, indent=1)
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -382,10 +509,15 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--summarize-rocprof", default=None)
+    ap.add_argument("--probe", default=None)
+    ap.add_argument("--summarize-pmc", nargs=4, default=None)
     args = ap.parse_args()
 
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof))
+        return 0
+    if args.summarize_pmc:
+        print(summarize_pmc(*args.summarize_pmc))
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the decode mat-vec would "
@@ -395,6 +527,9 @@ def main():
     import torch
     import routed_moe_matvec_amd as qg
 
+    if args.probe:
+        run_probe(args.probe, args.steps, args.warmup, qg, torch)
+        return 0
     torch.cuda.init()
     stream = torch.cuda.Stream()
     timer = Timer(stream)
