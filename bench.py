@@ -21,7 +21,7 @@ MoE tokens/s, prefill) measured the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --summarize-rocprof DIR   (turn rocprofv3 csv output into a text summary)
-       python bench.py --probe {gemv,copy,prefill,prefill_ws} --steps K
+       python bench.py --probe {gemv,copy,prefill,prefill_ws,moe_e256_t1,...} --steps K
                  (eager launches of one kernel, for rocprofv3 --pmc counter runs)
        python bench.py --summarize-pmc GEMV_FETCH GEMV_WRITE COPY_FETCH COPY_WRITE
                  (HBM bytes per launch of the GEMV from FETCH_SIZE / WRITE_SIZE runs,
@@ -299,7 +299,7 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
         out["moe_" + key.split("_", 1)[1]] = {
             "tokens_per_s": round(T / sec, 1), "us_per_call": round(sec * 1e6, 3), "mean_distinct_experts": float(uniq),
             "GB_s": round(byts / sec / 1e9, 1), "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4),
-            "includes": "quantize_act_q8 of the T tokens + moe_routed_qgemv (5 launches)"}
+            "includes": "quantize_act_q8 of the T tokens + moe_routed_qgemv (4 launches at T=1, else 5)"}
         del gr, pools, ws
         torch.cuda.empty_cache()
 
@@ -421,6 +421,34 @@ def run_probe(name: str, steps: int, warmup: int, qg, torch) -> None:
         else:
             def fn(i):
                 qg.qgemm_prefill_ws(qg.FMT_Q4K, copies[i % R], N, K, xb, M, y, ws, nb)
+    elif name.startswith("moe_"):
+        w = synth.WORKLOADS[name]
+        E, D, F, T, topk = w["E"], w["D"], w["F"], w["T"], w["topk"]
+        g = synth.rng(w["seed"])
+        pools = []
+        for _ in range(2):
+            pool = [[], [], []]
+            for e in range(E):
+                for lst, (n, k) in zip(pool, ((F, D), (F, D), (D, F))):
+                    lst.append(torch.from_numpy(synth.q4k_weight(g, n, k)).to("cuda"))
+            pools.append([qg.pointer_table(lst, "cuda") for lst in pool] + [pool])
+        draw = synth.moe_ids_zipf if w["ids"] == "zipf" else synth.moe_ids_uniform
+        ids_d = torch.from_numpy(draw(g, T, E, topk)).to("cuda")
+        rw = torch.from_numpy(synth.routing_weights(g, T, topk)).to("cuda")
+        x = torch.from_numpy(synth.activations(g, T, D)).to("cuda")
+        qx = torch.empty(T, D, dtype=torch.int8, device="cuda")
+        dx = torch.empty(T, D // 32, dtype=torch.float32, device="cuda")
+        sx = torch.empty(T, D // 32, dtype=torch.int32, device="cuda")
+        y = torch.empty(T, D, dtype=torch.float32, device="cuda")
+        nb = qg.moe_routed_workspace_bytes(T, topk, E, D, F)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        status = torch.empty(1, dtype=torch.int32, device="cuda")
+
+        def fn(i):
+            pool = pools[i % 2]
+            qg.quantize_act_q8(x, T, D, qx, dx, sx)
+            qg.moe_routed_qgemv(qx, dx, sx, T, D, F, E, topk, ids_d, rw, pool[0], pool[1], pool[2], y, ws, nb,
+                                status)
     else:
         raise SystemExit("unknown probe %r" % name)
     for i in range(warmup):

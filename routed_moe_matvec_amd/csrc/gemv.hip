@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kGemvMaxWaves *kWave) void qgemv_kernel(GemvArgs a)
     const int nt = second ? a.nt1 : a.nt0;
     const int nb = a.K / 32;
     int32_t *isum = a.isum;
-    gemv_workgroup<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>(
+    gemv_workgroup<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32 ? kSrcF32 : kSrcQ8>(
         W, N, a.K, a.tg, wg * a.waves * a.tpw, a.tpw, nt, a.act, a.M, a.mt, smem,
         [](int m) { return m; }, [=](int m, int row, float v) { y[(size_t)m * N + row] = v; },
         [=](int m, int row, int unit, const int32_t *s) {

@@ -331,19 +331,31 @@ struct ActSrc {
     int8_t *pqx;
     float *pdx;
     int32_t *psx;
+    const float *x2;  // kSrcGLU: the second input (x holds the gate outputs, x2 the up outputs)
+    float *ph;        // kSrcGLU: where the publishing workgroup writes h = silu(x) * x2
 };
+
+// What a workgroup stages: a Q8 activation, an fp32 activation it quantizes,
+// or the SwiGLU product h = silu(g) * v of two fp32 inputs, quantized.
+constexpr int kSrcQ8 = 0;
+constexpr int kSrcF32 = 1;
+constexpr int kSrcGLU = 2;
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Staging from fp32: load() reads the first kActRegChunks 16-byte chunks
 // (4 values each) per thread into registers, store() quantizes each 32-block
 // on its 8 consecutive lanes and writes the records; chunks beyond what the
 // registers held are read and quantized in further passes inside store().
-template <int FMT, class U>
+// GLU = true reads two inputs and stages h = silu(g) * v.
+template <int FMT, class U, bool GLU>
 struct ActStageF32 {
     static constexpr int REC = U::rec_dwords * 4;
     float4 v[kActRegChunks];
+    float4 v2[GLU ? kActRegChunks : 1];
 
     template <class TokenRow>
-    __device__ __forceinline__ void load_pass(const float *__restrict__ x, int K, int m0, int mtc, int base,
+    __device__ __forceinline__ void load_pass(const ActSrc &src, int K, int m0, int mtc, int base,
                                               TokenRow token_row) {
         const int NT = blockDim.x;
         const int cpt = K / 4;
@@ -352,14 +364,16 @@ struct ActStageF32 {
             const int c = base + (int)threadIdx.x + k * NT;
             if (c < mtc * cpt) {
                 const int mm = c / cpt;
-                v[k] = reinterpret_cast<const float4 *>(x + (size_t)token_row(m0 + mm) * K)[c - mm * cpt];
+                const size_t at = (size_t)token_row(m0 + mm) * K;
+                v[k] = reinterpret_cast<const float4 *>(src.x + at)[c - mm * cpt];
+                if constexpr (GLU) v2[k] = reinterpret_cast<const float4 *>(src.x2 + at)[c - mm * cpt];
             }
         }
     }
 
     template <class TokenRow>
-    __device__ __forceinline__ void load(const float *__restrict__ x, int K, int m0, int mtc, TokenRow token_row) {
-        load_pass(x, K, m0, mtc, 0, token_row);
+    __device__ __forceinline__ void load(const ActSrc &src, int K, int m0, int mtc, TokenRow token_row) {
+        load_pass(src, K, m0, mtc, 0, token_row);
     }
 
     template <class TokenRow>
@@ -370,7 +384,7 @@ struct ActStageF32 {
         const int cpt = K / 4;
         const int total = mtc * cpt;
         for (int base = 0; base < total; base += kActRegChunks * NT) {
-            if (base > 0) load_pass(src.x, K, m0, mtc, base, token_row);
+            if (base > 0) load_pass(src, K, m0, mtc, base, token_row);
 #pragma unroll
             for (int k = 0; k < kActRegChunks; ++k) {
                 const int c = base + (int)threadIdx.x + k * NT;  // 8 consecutive lanes hold one 32-block
@@ -381,6 +395,12 @@ struct ActStageF32 {
                     vals[1] = v[k].y;
                     vals[2] = v[k].z;
                     vals[3] = v[k].w;
+                    if constexpr (GLU) {
+                        vals[0] = silu(vals[0]) * v2[k].x;
+                        vals[1] = silu(vals[1]) * v2[k].y;
+                        vals[2] = silu(vals[2]) * v2[k].z;
+                        vals[3] = silu(vals[3]) * v2[k].w;
+                    }
                 }
                 int8_t q[4];
                 float d;
@@ -402,6 +422,9 @@ struct ActStageF32 {
                     }
                     if (publish) {
                         const size_t row = (size_t)token_row(m0 + mm);
+                        if (GLU && src.ph)
+                            *reinterpret_cast<float4 *>(src.ph + row * K + 4 * w) =
+                                make_float4(vals[0], vals[1], vals[2], vals[3]);
                         if (src.pqx) *reinterpret_cast<uint32_t *>(src.pqx + row * K + 32 * blk + 4 * part) = packed;
                         if (part == 0) {
                             if (src.pdx) src.pdx[row * (K / 32) + blk] = d;
@@ -467,9 +490,9 @@ __device__ __forceinline__ void tile_to_unit(const TileRegs<U> &r, uint8_t *lw, 
 // tpw must be 1 (the tile stays in registers across chunks).  Every wave of
 // the workgroup must call this (it synchronizes).  PIPE = false limits tpw
 // to 1 and keeps only one tile register set; ONE = true is the M = 1 form
-// (no token loop, fewer live registers); F32 = true stages from the fp32
-// activation (quantizing it) instead of a Q8 activation.
-template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32, class TokenRow, class Out,
+// (no token loop, fewer live registers); SRC picks what is staged (kSrcQ8,
+// kSrcF32 or kSrcGLU, see ActSrc).
+template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, int SRC, class TokenRow, class Out,
           class IsumOut>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, int N, int K, const TileGeom &tg,
                                                int tile_base, int tpw, int ntiles, const ActSrc &src, int M, int mt,
@@ -502,12 +525,15 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
 
     TileRegs<U> ra, rb;
     UnitRegs<U> u;
+    constexpr bool F32 = SRC != kSrcQ8;
     ActStage<FMT, U> st;
-    ActStageF32<FMT, U> stf;
-    const bool publish = F32 && blockIdx.x == 0 && blockIdx.y == 0;
+    ActStageF32<FMT, U, SRC == kSrcGLU> stf;
+    // fp32 input: workgroup (0, 0) publishes the Q8 activation; SwiGLU input:
+    // workgroup 0 of each blockIdx.y (one expert: its own pairs) publishes h
+    const bool publish = SRC == kSrcF32 ? (blockIdx.x == 0 && blockIdx.y == 0) : (SRC == kSrcGLU && blockIdx.x == 0);
     auto act_load = [&](int m0, int mtc) {
         if constexpr (F32)
-            stf.load(src.x, K, m0, mtc, token_row);
+            stf.load(src, K, m0, mtc, token_row);
         else
             st.load(src.qx, src.dx, src.sx, K, m0, mtc, token_row);
     };

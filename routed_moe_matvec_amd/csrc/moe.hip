@@ -8,15 +8,20 @@
 // weights (ROCm/ATOM "DeepSeek-V4 Usage Guide", opening paragraph and MoE
 // tips).  The experts are Q4_K (the "Q4KExperts" model of PR 623).
 //
-// Five launches on the caller's stream, none of which returns data to the host:
+// Launches on the caller's stream, none of which returns data to the host:
 //   1. table   : validate ids, distinct experts ascending, slots, CSR pair lists
+//                (one wave: bitmap of the selected experts, popcount ranks,
+//                ballot-based stable fill)
 //   2. gate/up : per distinct expert, gate and up rows against each of its
 //                pairs' tokens (weights streamed once per expert)
-//   3. h       : h = silu(g) * up, Q8-quantized per 32-block
-//   4. down    : per distinct expert, down rows against each pair's h
+//   3. h       : h = silu(g) * up, Q8-quantized per 32-block (T > 1 only)
+//   4. down    : per distinct expert, down rows against each pair's Q8 h
 //   5. combine : y[t] = sum_k rw[t,k] * o[t,k] in k order
 // Grids 2 and 4 are sized for the largest possible number of distinct experts,
-// min(T*topk, E); workgroups beyond the device-side count exit at once.
+// min(T*topk, E); workgroups beyond the device-side count exit at once.  With
+// one token every expert has one pair (or a few, if the token repeats an id):
+// then 2 and 4 use the single-token form of the engine, once per pair, and 4
+// computes and quantizes h itself while staging it, so 3 is not launched.
 #include "common.h"
 #include "gemv_device.h"
 #include "quantize_device.h"
@@ -24,7 +29,7 @@
 namespace qg {
 
 constexpr int kMoeWaves = 4;
-constexpr int kTableThreads = 1024;
+constexpr int kTableWords = QG_MAX_EXPERTS / 32;  // bitmap words over the expert ids
 
 struct MoeWs {
     int32_t *nuniq, *uniq, *slot, *pair_off, *pairs;
@@ -73,112 +78,125 @@ static size_t moe_layout(int T, int topk, int E, int D, int F, size_t off[QG_WS_
 
 // ---------------------------------------------------------------- 1. table
 
-// Exclusive scan of v[0..n) in place (n <= 4 * kTableThreads), whole block.
-// Returns the total.  tmp: kTableThreads ints of LDS.
-__device__ int block_exclusive_scan(int *v, int n, int *tmp) {
-    const int t = threadIdx.x;
-    int local[4];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = 4 * t + i;
-        local[i] = idx < n ? v[idx] : 0;
-        sum += local[i];
-    }
-    tmp[t] = sum;
-    __syncthreads();
-    for (int off = 1; off < kTableThreads; off <<= 1) {
-        const int add = t >= off ? tmp[t - off] : 0;
-        __syncthreads();
-        tmp[t] += add;
-        __syncthreads();
-    }
-    int run = tmp[t] - sum;  // exclusive prefix of this thread's 4 entries
-    const int total = tmp[kTableThreads - 1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = 4 * t + i;
-        if (idx < n) v[idx] = run;
-        run += local[i];
-    }
-    __syncthreads();
-    return total;
-}
-
 __device__ __forceinline__ bool bad_pointer(const void *p) { return p == nullptr || ((uintptr_t)p & 15) != 0; }
 
-__global__ __launch_bounds__(kTableThreads) void moe_table_kernel(const int32_t *__restrict__ ids, int P, int E,
-                                                                 const void *const *gate, const void *const *up,
-                                                                 const void *const *down, MoeWs ws,
-                                                                 int32_t *status) {
-    __shared__ int flag[QG_MAX_EXPERTS];  // selected and usable
-    __shared__ int rank[QG_MAX_EXPERTS];  // index in uniq
-    __shared__ int cnt[QG_MAX_EXPERTS];   // pairs per distinct expert, then running fill position
-    __shared__ int tmp[kTableThreads];
-    __shared__ int chunk_slot[kTableThreads];
-    const int t = threadIdx.x;
-    if (t == 0) atomicExch(status, QG_DEV_OK);
-    for (int e = t; e < E; e += kTableThreads) flag[e] = 0;
-    __threadfence();
+// Exclusive prefix sum over the 64 lanes of the wave; *total gets the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
+    const int lane = lane_id();
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    *total = __shfl(incl, kWave - 1, kWave);
+    return incl - v;
+}
+
+// One wave.  bm: bitmap of the selected usable experts; wpre[w]: number of set
+// bits in words below w, so rank(e) = wpre[e/32] + popcount of the bits of
+// word e/32 below e.
+__global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restrict__ ids, int P, int E,
+                                                         const void *const *gate, const void *const *up,
+                                                         const void *const *down, MoeWs ws, int32_t *status) {
+    __shared__ uint32_t bm[kTableWords];
+    __shared__ int wpre[kTableWords];
+    __shared__ int cur[QG_MAX_EXPERTS];  // pairs per distinct expert, then the next free position
+    const int l = threadIdx.x;
+    if (l == 0) atomicExch(status, QG_DEV_OK);
+    for (int w = l; w < kTableWords; w += kWave) bm[w] = 0u;
     __syncthreads();
-    for (int p = t; p < P; p += kTableThreads) {
+    for (int p = l; p < P; p += kWave) {
         const int e = ids[p];
         if (e < 0 || e >= E)
             atomicCAS(status, QG_DEV_OK, QG_DEV_BAD_EXPERT);
         else
-            flag[e] = 1;
+            atomicOr(&bm[e >> 5], 1u << (e & 31));
     }
     __syncthreads();
-    for (int e = t; e < E; e += kTableThreads) {
-        if (flag[e] && (bad_pointer(gate[e]) || bad_pointer(up[e]) || bad_pointer(down[e]))) {
-            flag[e] = 0;
+    // experts with a NULL or misaligned matrix are dropped (checked once per pair)
+    for (int p = l; p < P; p += kWave) {
+        const int e = ids[p];
+        if (e >= 0 && e < E && (bad_pointer(gate[e]) || bad_pointer(up[e]) || bad_pointer(down[e]))) {
+            atomicAnd(&bm[e >> 5], ~(1u << (e & 31)));
             atomicCAS(status, QG_DEV_OK, QG_DEV_NULL_EXPERT);
         }
-        rank[e] = flag[e];
     }
     __syncthreads();
-    const int U = block_exclusive_scan(rank, E, tmp);
-    for (int e = t; e < E; e += kTableThreads)
-        if (flag[e]) ws.uniq[rank[e]] = e;
-    if (t == 0) *ws.nuniq = U;
-    for (int u = t; u < U; u += kTableThreads) cnt[u] = 0;
+    // ranks: each lane owns kTableWords / 64 consecutive words
+    constexpr int WPL = kTableWords / kWave;
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) c += __popc(bm[WPL * l + i]);
+    int U;
+    int run = wave_exclusive_scan(c, &U);
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+        const int w = WPL * l + i;
+        uint32_t bits = bm[w];
+        wpre[w] = run;
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            ws.uniq[run++] = 32 * w + b;
+            bits &= bits - 1u;
+        }
+    }
+    if (l == 0) *ws.nuniq = U;
+    for (int u = l; u < U; u += kWave) cur[u] = 0;
     __syncthreads();
-    for (int p = t; p < P; p += kTableThreads) {
+    auto slot_of = [&](int p) -> int {
         const int e = ids[p];
-        const int s = (e >= 0 && e < E && flag[e]) ? rank[e] : -1;
+        if (e < 0 || e >= E) return -1;
+        const uint32_t word = bm[e >> 5], bit = 1u << (e & 31);
+        return (word & bit) ? wpre[e >> 5] + __popc(word & (bit - 1u)) : -1;
+    };
+    for (int p = l; p < P; p += kWave) {
+        const int s = slot_of(p);
         ws.slot[p] = s;
-        if (s >= 0) atomicAdd(&cnt[s], 1);
+        if (s >= 0) atomicAdd(&cur[s], 1);
     }
     __syncthreads();
-    const int npairs = block_exclusive_scan(cnt, U, tmp);  // cnt[u] = first position of expert u
-    for (int u = t; u < U; u += kTableThreads) ws.pair_off[u] = cnt[u];
-    if (t == 0) ws.pair_off[U] = npairs;
-    // stable fill: pairs of one expert keep ascending pair order
-    for (int c0 = 0; c0 < P; c0 += kTableThreads) {
-        const int p = c0 + t;
-        int s = -1;
-        if (p < P) {
-            const int e = ids[p];
-            s = (e >= 0 && e < E && flag[e]) ? rank[e] : -1;
-        }
-        chunk_slot[t] = s;
-        __syncthreads();
+    // CSR offsets: lane l scans experts [l*per, (l+1)*per)
+    const int per = (U + kWave - 1) / kWave;
+    const int lo = min(U, l * per), hi = min(U, lo + per);
+    int sum = 0;
+    for (int u = lo; u < hi; ++u) sum += cur[u];
+    int npairs;
+    int at = wave_exclusive_scan(sum, &npairs);
+    for (int u = lo; u < hi; ++u) {
+        const int n = cur[u];
+        ws.pair_off[u] = at;
+        cur[u] = at;
+        at += n;
+    }
+    if (l == 0) ws.pair_off[U] = npairs;
+    __syncthreads();
+    // stable fill, 64 pairs at a time: a pair's place among the chunk's pairs of
+    // the same expert comes from a ballot over each distinct slot in the chunk
+    const uint64_t below = (1ull << l) - 1ull;
+    for (int c0 = 0; c0 < P; c0 += kWave) {
+        const int p = c0 + l;
+        const int s = p < P ? slot_of(p) : -1;
+        uint64_t left = __ballot(s >= 0);
         int before = 0, same = 0;
-        if (s >= 0) {
-            for (int j = 0; j < kTableThreads && c0 + j < P; ++j) {
-                const int sj = chunk_slot[j];
-                same += sj == s;
-                before += (sj == s) & (j < t);
+        while (left) {
+            const int leader = __ffsll((unsigned long long)left) - 1;
+            const int v = __shfl(s, leader, kWave);
+            const uint64_t m = __ballot(s == v);
+            if (s == v) {
+                before = __popcll(m & below);
+                same = __popcll(m);
             }
-            ws.pairs[cnt[s] + before] = p;
+            left &= ~m;
         }
+        if (s >= 0) ws.pairs[cur[s] + before] = p;
         __syncthreads();
-        if (s >= 0 && before == 0) cnt[s] += same;  // one thread per expert present in the chunk
+        if (s >= 0 && before == 0) cur[s] += same;  // one lane per expert present in the chunk
         __syncthreads();
     }
 }
 
-// ---------------------------------------------------------------- 2./4. expert GEMVs
+// ---------------------------------------------------------------- 2./3. expert GEMVs
 
 struct MoeArgs {
     const int8_t *qx;
@@ -196,7 +214,9 @@ struct MoeArgs {
 using QU = Unit<QG_FMT_Q4K, 8>;
 
 // gate and up of expert uniq[blockIdx.y]: workgroups [0, nwg) take gate rows,
-// [nwg, 2 nwg) up rows; the tokens are the expert's pairs' tokens.
+// [nwg, 2 nwg) up rows; the tokens are the expert's pairs' tokens.  ONE: the
+// single-token engine, run once per pair.
+template <bool ONE>
 __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int u = blockIdx.y;
@@ -216,14 +236,27 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
     act.qx = a.qx;
     act.dx = a.dx;
     act.sx = a.sx;
-    gemv_workgroup<QG_FMT_Q4K, 8, false, false, false, false>(
-        W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, cnt, a.mt, smem,
-        [=](int m) { return pairs[m] / topk; },
-        [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; },
-        [](int, int, int, const int32_t *) {});
+    if constexpr (ONE) {
+        for (int m = 0; m < cnt; ++m) {
+            if (m > 0) __syncthreads();  // the previous pair's staged activation is no longer read
+            const int p = pairs[m];
+            gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8>(
+                W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p / topk; },
+                [=](int, int row, float v) { dst[(size_t)p * F + row] = v; }, [](int, int, int, const int32_t *) {});
+        }
+    } else {
+        gemv_workgroup<QG_FMT_Q4K, 8, false, false, false, kSrcQ8>(
+            W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, cnt, a.mt, smem, [=](int m) { return pairs[m] / topk; },
+            [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; },
+            [](int, int, int, const int32_t *) {});
+    }
 }
 
-// down of expert uniq[blockIdx.y] against the quantized h of each of its pairs
+// down of expert uniq[blockIdx.y] against the Q8 form of h = silu(g) * v of
+// each of its pairs.  ONE: h is computed and quantized while it is staged
+// (workgroup 0 of the expert stores h, hq, hd, hs of its pairs), once per
+// pair; otherwise moe_h_quant_kernel has stored hq/hd/hs before.
+template <bool ONE>
 __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int u = blockIdx.y;
@@ -237,20 +270,35 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     float *o = a.ws.o;
     const int D = a.D;
     ActSrc act{};
-    act.qx = a.ws.hq;
-    act.dx = a.ws.hd;
-    act.sx = a.ws.hs;
-    gemv_workgroup<QG_FMT_Q4K, 8, false, false, false, false>(
-        W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, act, cnt, a.mt, smem,
-        [=](int m) { return pairs[m]; }, [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; },
-        [](int, int, int, const int32_t *) {});
+    act.x = a.ws.g;
+    act.x2 = a.ws.v;
+    act.ph = a.ws.h;
+    act.pqx = a.ws.hq;
+    act.pdx = a.ws.hd;
+    act.psx = a.ws.hs;
+    if constexpr (ONE) {
+        for (int m = 0; m < cnt; ++m) {
+            if (m > 0) __syncthreads();
+            const int p = pairs[m];
+            gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcGLU>(
+                W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p; },
+                [=](int, int row, float v) { o[(size_t)p * D + row] = v; }, [](int, int, int, const int32_t *) {});
+        }
+    } else {
+        ActSrc hq{};
+        hq.qx = a.ws.hq;
+        hq.dx = a.ws.hd;
+        hq.sx = a.ws.hs;
+        gemv_workgroup<QG_FMT_Q4K, 8, false, false, false, kSrcQ8>(
+            W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, hq, cnt, a.mt, smem,
+            [=](int m) { return pairs[m]; }, [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; },
+            [](int, int, int, const int32_t *) {});
+    }
 }
 
-// ---------------------------------------------------------------- 3. h = silu(g) * v, Q8
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-// 8 lanes per 32-block of h, as in the activation quantizer.
+// h = silu(g) * v and its Q8 form for every valid pair, before the down
+// projection of more than one token: 8 lanes per 32-block, the quantizer of
+// the activation staging (so the records match the single-token form).
 __global__ __launch_bounds__(256) void moe_h_quant_kernel(MoeWs ws, int P, int F) {
     const int gid = blockIdx.x * blockDim.x + threadIdx.x;
     const int nblk = P * (F / 32);
@@ -283,7 +331,7 @@ __global__ __launch_bounds__(256) void moe_h_quant_kernel(MoeWs ws, int P, int F
     }
 }
 
-// ---------------------------------------------------------------- 5. combine
+// ---------------------------------------------------------------- 4. combine
 
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeWs ws, const float *__restrict__ rw, int T, int D,
                                                           int topk, float *__restrict__ y) {
@@ -363,8 +411,7 @@ extern "C" int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t
     const int Ucap = P < E ? P : E;
     MoeWs w = ws_pointers(ws, off);
 
-    hipLaunchKernelGGL(moe_table_kernel, dim3(1), dim3(kTableThreads), 0, st, ids, P, E, gate, up, down, w,
-                       d_status);
+    hipLaunchKernelGGL(moe_table_kernel, dim3(1), dim3(kWave), 0, st, ids, P, E, gate, up, down, w, d_status);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
 
     MoeArgs a{};
@@ -379,30 +426,42 @@ extern "C" int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t
     a.up = up;
     a.down = down;
     a.ws = w;
-
-    // gate/up: K = D
+    const bool one = T == 1;  // every expert then has a single pair (a few if the token repeats an id)
     constexpr int threads = kMoeWaves * kWave;
+    static bool lds_raised = false;  // idempotent: raise the dynamic-LDS limit once
+    if (!lds_raised)
+        lds_raised = raise_lds_limit(moe_gate_up_kernel<false>, kLdsBytes) &&
+                     raise_lds_limit(moe_gate_up_kernel<true>, kLdsBytes) &&
+                     raise_lds_limit(moe_down_kernel<false>, kLdsBytes) &&
+                     raise_lds_limit(moe_down_kernel<true>, kLdsBytes);
+
+    // gate/up: K = D, Q8 activation of the tokens
     a.tg = make_tile_geom<QU>(D);
-    a.mt = tokens_per_chunk<QU>(D, QG_MAX_MOE_PAIRS, threads);
+    a.mt = one ? 1 : tokens_per_chunk<QU>(D, QG_MAX_MOE_PAIRS, threads);
     size_t lds = gemv_lds_bytes<QU>(kMoeWaves, D, a.mt);
-    static bool lds_gu = false, lds_dn = false;  // idempotent: raise the dynamic-LDS limit once
-    const size_t lds_max = kLdsBytes;
-    if (!lds_gu) lds_gu = raise_lds_limit(moe_gate_up_kernel, lds_max);
     int nwg = ((F + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
-    hipLaunchKernelGGL(moe_gate_up_kernel, dim3(2 * nwg, Ucap), dim3(threads), lds, st, a);
+    if (one)
+        hipLaunchKernelGGL(moe_gate_up_kernel<true>, dim3(2 * nwg, Ucap), dim3(threads), lds, st, a);
+    else
+        hipLaunchKernelGGL(moe_gate_up_kernel<false>, dim3(2 * nwg, Ucap), dim3(threads), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
 
-    const long long hthreads = (long long)P * (F / 32) * 8;
-    hipLaunchKernelGGL(moe_h_quant_kernel, dim3((unsigned)((hthreads + 255) / 256)), dim3(256), 0, st, w, P, F);
-    if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
-
-    // down: K = F
+    // down: K = F.  One token: h = silu(g) * v staged from fp32 and quantized
+    // there; several: h quantized once per pair first (each expert's
+    // workgroups would otherwise all redo it for every pair)
+    if (!one) {
+        const long long hthreads = (long long)P * (F / 32) * 8;
+        hipLaunchKernelGGL(moe_h_quant_kernel, dim3((unsigned)((hthreads + 255) / 256)), dim3(256), 0, st, w, P, F);
+        if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
+    }
     a.tg = make_tile_geom<QU>(F);
-    a.mt = tokens_per_chunk<QU>(F, QG_MAX_MOE_PAIRS, threads);
+    a.mt = one ? 1 : tokens_per_chunk<QU>(F, QG_MAX_MOE_PAIRS, threads);
     lds = gemv_lds_bytes<QU>(kMoeWaves, F, a.mt);
-    if (!lds_dn) lds_dn = raise_lds_limit(moe_down_kernel, lds_max);
     nwg = ((D + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
-    hipLaunchKernelGGL(moe_down_kernel, dim3(nwg, Ucap), dim3(threads), lds, st, a);
+    if (one)
+        hipLaunchKernelGGL(moe_down_kernel<true>, dim3(nwg, Ucap), dim3(threads), lds, st, a);
+    else
+        hipLaunchKernelGGL(moe_down_kernel<false>, dim3(nwg, Ucap), dim3(threads), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
 
     const long long cthreads = (long long)T * (D / 4);
