@@ -25,7 +25,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extr
                  (eager launches of one kernel, for rocprofv3 --pmc counter runs)
        python bench.py --summarize-pmc GEMV_FETCH GEMV_WRITE COPY_FETCH COPY_WRITE
                  (HBM bytes per launch of the GEMV from FETCH_SIZE / WRITE_SIZE runs,
-                  scaled by the copy kernel's counters; writes profiles/pmc_traffic.json)
+                  scaled by the copy kernel's counters; writes profiles/qgemv_q8_0_4096x8192_hbm_traffic.json)
 """
 from __future__ import annotations
 
