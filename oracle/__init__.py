@@ -63,6 +63,8 @@ def _load():
     lib.oracle_quantize_act_q8.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.oracle_gemv.restype = ctypes.c_int
     lib.oracle_gemv.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp, i64, vp, vp, ctypes.c_int]
+    lib.oracle_gemv_fx.restype = ctypes.c_int
+    lib.oracle_gemv_fx.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, vp, vp, ctypes.c_int]
     lib.oracle_block_isums.restype = ctypes.c_int
     lib.oracle_block_isums.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, vp]
     lib.oracle_moe_table.restype = ctypes.c_int
@@ -144,6 +146,18 @@ def gemv(fmt: int, W: np.ndarray, N: int, K: int, qx: np.ndarray, dx: np.ndarray
     bound = np.empty((M, N), np.float64)
     _check(_load().oracle_gemv(fmt, _ptr(W), N, K, _ptr(qx), _ptr(dx), M, _ptr(y), _ptr(bound), nthreads),
            "gemv")
+    return y, bound
+
+
+def gemv_fx(fmt: int, W: np.ndarray, N: int, K: int, x: np.ndarray, nthreads: int = 1):
+    """(y, bound) float64 [M, N] of the weights against the fp32 activation x as given."""
+    W = _c(W, np.uint8)
+    x = _c(x, np.float32).reshape(-1, K)
+    M = x.shape[0]
+    assert W.size == N * row_bytes(fmt, K)
+    y = np.empty((M, N), np.float64)
+    bound = np.empty((M, N), np.float64)
+    _check(_load().oracle_gemv_fx(fmt, _ptr(W), N, K, _ptr(x), M, _ptr(y), _ptr(bound), nthreads), "gemv_fx")
     return y, bound
 
 

@@ -267,6 +267,40 @@ int oracle_gemv(int fmt, const uint8_t *W, int64_t N, int64_t K, const int8_t *q
 }
 
 /*
+ * The fp32-activation product kept as the exact-activation ("quality")
+ * comparator of the prequantized path (pull request 623, Summary: the shared-x
+ * fp32 path that prequantization replaced):
+ * y[m, n] = sum_k w[n, k] * x[m, k]   in fp64, x taken as the given fp32 values,
+ * bound[m, n] = sum_k |w[n, k] * x[m, k]|.  bound may be NULL.
+ */
+int oracle_gemv_fx(int fmt, const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M, double *y,
+                   double *bound, int nthreads) {
+    if (!fmt_ok(fmt, K) || N < 0 || M < 0) return ORACLE_ERR_ARG;
+    int64_t rb = oracle_row_bytes(fmt, K);
+    int64_t nb = K / 32;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *row = W + n * rb;
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, bnd = 0.0;
+            double w[32];
+            for (int64_t b = 0; b < nb; ++b) {
+                dequant_block(fmt, row, b, w);
+                for (int i = 0; i < 32; ++i) {
+                    double t = w[i] * (double)x[m * K + 32 * b + i];
+                    acc += t;
+                    bnd += fabs(t);
+                }
+            }
+            y[m * N + n] = acc;
+            if (bound) bound[m * N + n] = bnd;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
  * Per-block integer dot products of the raw quants with the activation quants:
  * isum[m, n, b] = sum_{i<32} q_w[n, b, i] * qx[m, 32b + i]
  * (Q8_0: q_w is the int8 quant; Q4_K: q_w is the 4-bit quant 0..15 of

@@ -200,6 +200,57 @@ def test_q8_0_general_vs_numpy_matmul(orc):
     assert np.allclose(bound, np.abs(a) @ np.abs(Wd).T, rtol=1e-13)
 
 
+def test_gemv_fx_integer_special_case_is_exact_int_matmul(orc):
+    """fp32 activation, no quantization: d = 1 and integer x (any magnitude that stays
+    exact) make the product an int64 matmul."""
+    g = np.random.default_rng(24)
+    N, K, M = 29, 512, 3
+    q = g.integers(-127, 128, size=(N, K // 32, 32)).astype(np.int8)
+    W = synth.q8_0_from_parts(np.ones((N, K // 32), np.float16), q)
+    xi = g.integers(-1000, 1001, size=(M, K))
+    y, bound = orc.gemv_fx(orc.FMT_Q8_0, W, N, K, xi.astype(np.float32))
+    Wi = q.reshape(N, K).astype(np.int64)
+    assert np.array_equal(y, (xi @ Wi.T).astype(np.float64))
+    assert np.array_equal(bound, (np.abs(xi) @ np.abs(Wi).T).astype(np.float64))
+
+
+def test_gemv_fx_hand_block(orc):
+    """N=1, K=32, d=0.5, q_i = i-16, x_i = 0.25*i -> y = 0.5*0.25*sum (i-16)*i = 0.125*2480 = 310."""
+    q = (np.arange(32) - 16).astype(np.int8).reshape(1, 1, 32)
+    W = synth.q8_0_from_parts(np.array([[0.5]], np.float16), q)
+    x = (0.25 * np.arange(32)).astype(np.float32).reshape(1, 32)
+    y, bound = orc.gemv_fx(orc.FMT_Q8_0, W, 1, 32, x)
+    assert y[0, 0] == 310.0
+    assert bound[0, 0] == 0.125 * float(np.sum(np.abs(np.arange(32) - 16) * np.arange(32)))
+
+
+def test_gemv_fx_equals_gemv_on_a_representable_activation(orc):
+    """x = dx*qx with power-of-two scales is exact in fp32, so the fp32-activation product
+    equals the Q8-activation product term for term (both fp64)."""
+    g = np.random.default_rng(25)
+    N, K, M = 31, 1024, 2
+    W = synth.q8_0_weight(g, N, K)
+    qx = g.integers(-127, 128, size=(M, K)).astype(np.int8)
+    dx = (2.0 ** g.integers(-6, 3, size=(M, K // 32))).astype(np.float32)
+    x = (dx.repeat(32, axis=1) * qx.astype(np.float32)).astype(np.float32)
+    y1, b1 = orc.gemv_fx(orc.FMT_Q8_0, W, N, K, x)
+    y2, b2 = orc.gemv(orc.FMT_Q8_0, W, N, K, qx, dx)
+    assert np.all(np.abs(y1 - y2) <= 1e-13 * b2)
+    assert np.allclose(b1, b2, rtol=1e-14, atol=0)
+
+
+def test_gemv_fx_general_vs_numpy_matmul(orc):
+    g = np.random.default_rng(26)
+    N, K, M = 40, 768, 3
+    W = synth.q8_0_weight(g, N, K)
+    x = synth.activations(g, M, K)
+    Wd = fh.numpy_dequant_q8_0(W, N, K)
+    y, bound = orc.gemv_fx(orc.FMT_Q8_0, W, N, K, x)
+    a = x.astype(np.float64)
+    assert np.all(np.abs(y - a @ Wd.T) <= 1e-12 * (np.abs(a) @ np.abs(Wd).T))
+    assert np.allclose(bound, np.abs(a) @ np.abs(Wd).T, rtol=1e-13)
+
+
 def test_gemv_threads_do_not_change_result(orc):
     g = np.random.default_rng(24)
     N, K = 64, 512
