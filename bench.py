@@ -233,15 +233,18 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
         qg.quantize_act_q8(x, M, K, qx, dx, sx)
         return qx, dx, sx
 
-    def gemv_rate(fmt, W_host, N, K, Ms, label):
+    def gemv_rate(fmt, W_host, N, K, Ms, label, G=1):
+        """G > 1: the grouped call, W_host holding G matrices of N rows on G input slices of K."""
         R = rotation_count(W_host.nbytes)
         base = torch.from_numpy(W_host).to(dev)
         copies = [base] + [base.clone() for _ in range(R - 1)]
         res = {}
         for M in Ms:
-            qx, dx, sx = quantized(K, M)
-            y = torch.empty(M, N, dtype=torch.float32, device=dev)
-            if fmt == 0:
+            qx, dx, sx = quantized(G * K, M)
+            y = torch.empty(M, G * N, dtype=torch.float32, device=dev)
+            if G > 1:
+                fn = lambda i: qg.qgemv_grouped(fmt, copies[i % R], G, N, K, qx, dx, sx, M, y)
+            elif fmt == 0:
                 fn = lambda i: qg.qgemv_q8_0(copies[i % R], N, K, qx, dx, M, y)
             else:
                 fn = lambda i: qg.qgemv_q4k(copies[i % R], N, K, qx, dx, sx, M, y)
@@ -249,7 +252,7 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
             g = capture(fn, n, stream)
             timer.run(g.replay)
             sec = timer.run(g.replay) / n
-            byts = W_host.nbytes + M * K + M * (K // 32) * (8 if fmt else 4) + M * N * 4
+            byts = W_host.nbytes + G * (M * K + M * (K // 32) * (8 if fmt else 4) + M * N * 4)
             res["M%d" % M] = {"us": round(sec * 1e6, 3), "GB_s": round(byts / sec / 1e9, 1),
                               "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4)}
             del g
@@ -335,6 +338,29 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
     g = synth.rng(0)
     w = synth.WORKLOADS["q8_0_512x1024"]
     gemv_rate(0, synth.q8_0_weight(g, w["N"], w["K"]), w["N"], w["K"], [1], "q8_0_512x1024")
+    # the fp32-activation comparator on the out-projection (no activation quantization)
+    w = synth.WORKLOADS["q8_0_out_4096x8192"]
+    gq = synth.rng(w["seed"])
+    Wq = synth.q8_0_weight(gq, w["N"], w["K"])
+    R = rotation_count(Wq.nbytes)
+    base = torch.from_numpy(Wq).to(dev)
+    copies = [base] + [base.clone() for _ in range(R - 1)]
+    xq = torch.from_numpy(synth.activations(gq, 1, w["K"])).to(dev)
+    yq = torch.empty(1, w["N"], dtype=torch.float32, device=dev)
+    n = max(R, 64)
+    gr = capture(lambda i: qg.qgemv_q8_0_quality(copies[i % R], w["N"], w["K"], xq, 1, yq), n, stream)
+    timer.run(gr.replay)
+    sec = timer.run(gr.replay) / n
+    byts = Wq.nbytes + w["K"] * 4 + w["N"] * 4
+    out["quality_q8_0_4096x8192"] = {"us": round(sec * 1e6, 3), "GB_s": round(byts / sec / 1e9, 1),
+                                     "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4),
+                                     "includes": "qgemv_q8_0_quality: fp32 activation, no quantization"}
+    del gr, copies, base
+    torch.cuda.empty_cache()
+    w = synth.WORKLOADS["q8_0_grouped_8x1024x4096"]
+    gw = synth.rng(w["seed"])
+    gemv_rate(0, np.concatenate([synth.q8_0_weight(gw, w["N"], w["K"]) for _ in range(w["G"])], axis=0), w["N"],
+              w["K"], [1], "q8_0_grouped_8x1024x4096", G=w["G"])
     w = synth.WORKLOADS["q4k_8192x4096"]
     gemv_rate(1, synth.q4k_weight(synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], [1], "q4k_8192x4096")
     w = synth.WORKLOADS["q8_0_16384x4096"]

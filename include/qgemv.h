@@ -20,6 +20,9 @@
  *          decode mat-vec plus the Q8 activation quantizer with a block sum.
  *  [ATOM]  ROCm/ATOM "DeepSeek-V4 Usage Guide" -- sigmoid routing of 6
  *          experts out of 256 or 384.
+ *  [LCPP]  llama.cpp pull request 24162 (DeepSeek V4 support) -- the grouped
+ *          attention-output tensor, 8 groups of 1024 x 4096 rather than one
+ *          4096 x 8192 matrix.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -148,6 +151,33 @@ int qgemv_q4k(const void *W, int N, int K, const int8_t *qx, const float *dx, co
  */
 int qgemv_paired(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const int8_t *qx, const float *dx,
                  const int32_t *sx, int M, float *y1, float *y2, void *stream);
+
+/*
+ * qgemv_grouped -- [PR623] Summary, the low-rank attention-output projection
+ * among the prequantized decode call sites; [LCPP] its tensor is G = 8 groups
+ * of N x K (1024 x 4096), each applied to its own K-wide slice of the input.
+ *   y[m, g, n] = sum_k w_g[n, k] * x[m, g*K + k]        (g < G, n < N)
+ * W: G matrices of format `fmt` [N, K] stored one after another (the [G, N, K]
+ * tensor); qx/dx/sx: the Q8 activation of the G*K-wide input [M, G*K] (its
+ * 32-blocks never straddle two slices); y fp32 [M, G*N].  Group g equals
+ * qgemv_q8_0 / qgemv_q4k of matrix g on slice g, bit for bit.  sx may be NULL
+ * for QG_FMT_Q8_0.
+ * Errors: QG_ERR_FORMAT; QG_ERR_SHAPE unless 1 <= G <= 65535; otherwise as
+ * qgemv_q8_0.
+ */
+int qgemv_grouped(int fmt, const void *W, int G, int N, int K, const int8_t *qx, const float *dx, const int32_t *sx,
+                  int M, float *y, void *stream);
+
+/*
+ * qgemv_q8_0_quality -- [PR623] Summary: the fp32-activation ("shared-x")
+ * Q8_0 product that prequantized decode replaced, kept as its exact-activation
+ * comparator (the quality mode).  No activation quantization:
+ *   y[m, n] = sum_b dw[n, b] * sum_{i<32} qw[n, b, i] * x[m, 32b + i]
+ * W: QG_FMT_Q8_0 [N, K]; x fp32 [M, K]; y fp32 [M, N].  fp32 arithmetic
+ * (error well under 1e-5 * sum |w * x| per output, x as given).
+ * Errors: as qgemv_q8_0.
+ */
+int qgemv_q8_0_quality(const void *W, int N, int K, const float *x, int M, float *y, void *stream);
 
 /*
  * qgemv_q8_0_f32, qgemv_q4k_f32, qgemv_paired_f32 -- the same products taking

@@ -19,6 +19,7 @@ __all__ = [
     "qgemv_paired", "moe_routed_workspace_bytes", "moe_routed_workspace_layout", "moe_routed_qgemv",
     "qgemm_prefill", "qg_status_string", "qgemv_debug_block_isums", "pointer_table", "WS_REGIONS",
     "qgemv_q8_0_f32", "qgemv_q4k_f32", "qgemv_paired_f32", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
+    "qgemv_grouped", "qgemv_q8_0_quality",
 ]
 
 FMT_Q8_0 = 0
@@ -53,6 +54,8 @@ _c_quantize = _sig("quantize_act_q8", _i, [_vp, _i, _i, _vp, _vp, _vp, _vp])
 _c_q8_0 = _sig("qgemv_q8_0", _i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp])
 _c_q4k = _sig("qgemv_q4k", _i, [_vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp])
 _c_paired = _sig("qgemv_paired", _i, [_i, _vp, _i, _vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp])
+_c_grouped = _sig("qgemv_grouped", _i, [_i, _vp, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp])
+_c_quality = _sig("qgemv_q8_0_quality", _i, [_vp, _i, _i, _vp, _i, _vp, _vp])
 _c_isums = _sig("qgemv_debug_block_isums", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
 _c_q8_0_f32 = _sig("qgemv_q8_0_f32", _i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp])
 _c_q4k_f32 = _sig("qgemv_q4k_f32", _i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp])
@@ -120,6 +123,15 @@ def qgemv_q4k(W, N: int, K: int, qx, dx, sx, M: int, y, stream=None) -> None:
 def qgemv_paired(fmt: int, W1, N1: int, W2, N2: int, K: int, qx, dx, sx, M: int, y1, y2, stream=None) -> None:
     _ok(_c_paired(fmt, _ptr(W1), N1, _ptr(W2), N2, K, _ptr(qx), _ptr(dx), _ptr(sx), M, _ptr(y1), _ptr(y2),
                   _stream(stream, W1)), "qgemv_paired")
+
+
+def qgemv_grouped(fmt: int, W, G: int, N: int, K: int, qx, dx, sx, M: int, y, stream=None) -> None:
+    _ok(_c_grouped(fmt, _ptr(W), G, N, K, _ptr(qx), _ptr(dx), _ptr(sx), M, _ptr(y), _stream(stream, W)),
+        "qgemv_grouped")
+
+
+def qgemv_q8_0_quality(W, N: int, K: int, x, M: int, y, stream=None) -> None:
+    _ok(_c_quality(_ptr(W), N, K, _ptr(x), M, _ptr(y), _stream(stream, W)), "qgemv_q8_0_quality")
 
 
 def qgemv_q8_0_f32(W, N: int, K: int, x, M: int, y, qx=None, dx=None, sx=None, stream=None) -> None:

@@ -28,6 +28,7 @@ struct GemvArgs {
     int tpw;        // tiles per wave
     int waves;      // waves per workgroup
     int32_t *isum;  // per-block sums of matrix 0 (test export), else unused
+    int G;          // groups (blockIdx.y): matrix g of W0 against input slice g, 1 otherwise
 };
 
 template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32>
@@ -42,9 +43,13 @@ __global__ __launch_bounds__(kGemvMaxWaves *kWave) void qgemv_kernel(GemvArgs a)
     const int nt = second ? a.nt1 : a.nt0;
     const int nb = a.K / 32;
     int32_t *isum = a.isum;
+    // grouped call: group g = blockIdx.y takes matrix g and slice g of every
+    // token's activation (row m*G + g of the [M*G, K] view), writing y[m, g, :]
+    const int G = a.G, g = blockIdx.y;
+    W += (size_t)g * N * a.tg.row_bytes;
     gemv_workgroup<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32 ? kSrcF32 : kSrcQ8>(
         W, N, a.K, a.tg, wg * a.waves * a.tpw, a.tpw, nt, a.act, a.M, a.mt, smem,
-        [](int m) { return m; }, [=](int m, int row, float v) { y[(size_t)m * N + row] = v; },
+        [=](int m) { return m * G + g; }, [=](int m, int row, float v) { y[((size_t)m * G + g) * N + row] = v; },
         [=](int m, int row, int unit, const int32_t *s) {
             int32_t *o = isum + ((size_t)m * N + row) * nb + unit * NB;
 #pragma unroll
@@ -63,8 +68,8 @@ static int launch_kernel(const GemvArgs &a, int grid, size_t lds, hipStream_t st
             return QG_ERR_LAUNCH;
         attr_set = true;
     }
-    hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>), dim3(grid), dim3(a.waves * kWave), lds,
-                       stream, a);
+    hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>), dim3(grid, a.G), dim3(a.waves * kWave),
+                       lds, stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
@@ -75,7 +80,7 @@ static int launch_gemv(GemvArgs &a, hipStream_t stream) {
     a.nt0 = (a.N0 + a.tg.rpt - 1) / a.tg.rpt;
     a.nt1 = a.W1 ? (a.N1 + a.tg.rpt - 1) / a.tg.rpt : 0;
     const int cus = device_cu_count();
-    const int tiles = a.nt0 + a.nt1;
+    const int tiles = (a.nt0 + a.nt1) * a.G;
     // waves per workgroup: 8 when there are tiles for 8-wave workgroups on
     // every CU, else fewer so that the grid still spreads over the CUs
     a.waves = kGemvMaxWaves;
@@ -117,7 +122,7 @@ static int check_common(int N, int K, int M) {
 // given: (qx, dx[, sx]) or the fp32 x (then pqx/pdx/psx optionally receive
 // the Q8 activation).
 static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const ActSrc &act, int M,
-                         float *y1, float *y2, int32_t *isum, hipStream_t stream) {
+                         float *y1, float *y2, int32_t *isum, hipStream_t stream, int G = 1) {
     if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4K) return QG_ERR_FORMAT;
     const bool f32 = act.x != nullptr;
     if (!W1 || (!y1 && !isum)) return QG_ERR_NULL;
@@ -126,6 +131,7 @@ static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2
     int rc = check_common(N1, K, M);
     if (rc) return rc;
     if (W2 && N2 < 1) return QG_ERR_SHAPE;
+    if (G < 1 || G > 65535 || (G > 1 && (W2 || isum))) return QG_ERR_SHAPE;
     if (misaligned(W1) || misaligned(act.qx) || misaligned(act.dx) || misaligned(act.sx) || misaligned(act.x) ||
         misaligned(act.pqx) || misaligned(act.pdx) || misaligned(act.psx) || (y1 && misaligned(y1)) ||
         misaligned(W2) || misaligned(y2) || misaligned(isum))
@@ -143,6 +149,7 @@ static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2
     a.act = act;
     a.M = M;
     a.isum = isum;
+    a.G = G;
     if (isum) return launch_fmt<true, false>(fmt, a, stream);
     return f32 ? launch_fmt<false, true>(fmt, a, stream) : launch_fmt<false, false>(fmt, a, stream);
 }
@@ -186,6 +193,14 @@ extern "C" int qgemv_paired(int fmt, const void *W1, int N1, const void *W2, int
     if (!W2 || !y2 || !y1 || !qx || !dx) return QG_ERR_NULL;
     return qg::gemv_dispatch(fmt, W1, N1, W2, N2, K, qg::q8_src(qx, dx, sx), M, y1, y2, nullptr,
                              (hipStream_t)stream);
+}
+
+extern "C" int qgemv_grouped(int fmt, const void *W, int G, int N, int K, const int8_t *qx, const float *dx,
+                             const int32_t *sx, int M, float *y, void *stream) {
+    if (fmt != QG_FMT_Q8_0 && fmt != QG_FMT_Q4K) return QG_ERR_FORMAT;
+    if (!qx || !dx || (fmt == QG_FMT_Q4K && !sx)) return QG_ERR_NULL;
+    return qg::gemv_dispatch(fmt, W, N, nullptr, 0, K, qg::q8_src(qx, dx, sx), M, y, nullptr, nullptr,
+                             (hipStream_t)stream, G);
 }
 
 extern "C" int qgemv_q8_0_f32(const void *W, int N, int K, const float *x, int M, float *y, int8_t *qx, float *dx,

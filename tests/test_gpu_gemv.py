@@ -312,3 +312,65 @@ def test_fused_errors(qg):
     assert qg._c_q8_0_f32(W.data_ptr(), 8, 500, x.data_ptr(), 1, y.data_ptr(), None, None, None, None) == -2
     assert qg._c_q8_0_f32(W.data_ptr(), 8, 512, x.data_ptr() + 4, 1, y.data_ptr(), None, None, None, None) == -3
     assert np.all(host(y) == 2.0)
+
+
+# ---------------------------------------------------------------- grouped (attention output, low rank)
+
+@pytest.mark.parametrize("fmt,G,N,K,M", [(0, 8, 1024, 4096, 1), (0, 3, 130, 512, 3), (1, 2, 70, 1024, 2),
+                                         (0, 1, 96, 256, 5), (1, 5, 33, 256, 1)])
+def test_grouped_parity(qg, orc, fmt, G, N, K, M):
+    """Group g against the oracle on matrix g and input slice g; ragged N, G = 1, several tokens."""
+    import torch
+    progress("grouped fmt=%d G=%d N=%d K=%d M=%d" % (fmt, G, N, K, M))
+    g_ = np.random.default_rng(900 + G * 7 + N + K + M + fmt)
+    make = synth.q8_0_weight if fmt == 0 else synth.q4k_weight
+    Ws = [make(g_, N, K) for _ in range(G)]
+    x = synth.activations(g_, M, G * K)
+    qx, dx, sx = orc.quantize_act_q8(x)
+    y = sentinel((M, G * N), torch.float32, 99.0)
+    qg.qgemv_grouped(fmt, dev(np.concatenate(Ws, axis=0)), G, N, K, dev(qx), dev(dx), dev(sx), M, y)
+    yh = host(y).reshape(M, G, N)
+    nt = oracle_threads()
+    for g in range(G):
+        sl = slice(g * K, (g + 1) * K)
+        ref, bound = orc.gemv(fmt, Ws[g], N, K, qx[:, sl].copy(), dx[:, g * K // 32:(g + 1) * K // 32].copy(),
+                              nthreads=nt)
+        assert_within_bound(yh[:, g], ref, bound, what="grouped g=%d" % g)
+
+
+def test_grouped_equals_single_calls(qg):
+    """Each group equals the single-matrix call on its slice, bit for bit."""
+    import torch
+    g_ = np.random.default_rng(31)
+    G, N, K, M = 4, 200, 1024, 2
+    Ws = [synth.q8_0_weight(g_, N, K) for _ in range(G)]
+    x = dev(synth.activations(g_, M, G * K))
+    qx = torch.empty(M, G * K, dtype=torch.int8, device=x.device)
+    dx = torch.empty(M, G * K // 32, dtype=torch.float32, device=x.device)
+    sx = torch.empty(M, G * K // 32, dtype=torch.int32, device=x.device)
+    qg.quantize_act_q8(x, M, G * K, qx, dx, sx)
+    y = sentinel((M, G * N), torch.float32, 99.0)
+    qg.qgemv_grouped(0, dev(np.concatenate(Ws, axis=0)), G, N, K, qx, dx, sx, M, y)
+    yh = host(y).reshape(M, G, N)
+    for g in range(G):
+        qs = qx[:, g * K:(g + 1) * K].contiguous()
+        ds = dx[:, g * K // 32:(g + 1) * K // 32].contiguous()
+        y1 = sentinel((M, N), torch.float32, 99.0)
+        qg.qgemv_q8_0(dev(Ws[g]), N, K, qs, ds, M, y1)
+        assert np.array_equal(host(y1).view(np.uint32), np.ascontiguousarray(yh[:, g]).view(np.uint32)), g
+
+
+def test_grouped_errors(qg):
+    import torch
+    W = dev(synth.q8_0_weight(np.random.default_rng(1), 16, 512))
+    qx = dev(np.zeros((1, 1024), np.int8))
+    dx = dev(np.ones((1, 32), np.float32))
+    y = sentinel((1, 16), torch.float32, 1.0)
+    c = qg._c_grouped
+    assert c(0, W.data_ptr(), 0, 8, 512, qx.data_ptr(), dx.data_ptr(), None, 1, y.data_ptr(), None) == -2
+    assert c(0, W.data_ptr(), 70000, 8, 512, qx.data_ptr(), dx.data_ptr(), None, 1, y.data_ptr(), None) == -2
+    assert c(1, W.data_ptr(), 2, 8, 512, qx.data_ptr(), dx.data_ptr(), None, 1, y.data_ptr(), None) == -1
+    assert c(3, W.data_ptr(), 2, 8, 512, qx.data_ptr(), dx.data_ptr(), None, 1, y.data_ptr(), None) == -4
+    assert c(0, W.data_ptr() + 4, 2, 8, 512, qx.data_ptr(), dx.data_ptr(), None, 1, y.data_ptr(), None) == -3
+    torch.cuda.synchronize()
+    assert np.all(host(y) == 1.0)
