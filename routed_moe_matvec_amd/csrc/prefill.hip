@@ -36,6 +36,8 @@
 // |x| < 2^-17).  qgemm_prefill_ws first runs a pass, one workgroup per token,
 // that finds e, writes x*2^e as fp16 and the hi/lo sums to a caller workspace;
 // the GEMM then reads them instead of converting once per weight tile.
+#include <type_traits>
+
 #include "common.h"
 
 namespace qg {
@@ -377,6 +379,387 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
         }
 }
 
+// ------------------------------------------------------------------ GEMM, workspace form
+
+// 128 tokens x 128 weight rows per workgroup of eight waves (two per SIMD, so
+// one wave's copies and dequantization overlap the other's MFMAs), each wave
+// 64 tokens x 32 rows.  K advances 128 per step.
+//
+// Every global read of a step is a global -> LDS copy (global_load_lds), six
+// per thread, into one of three rotating LDS stages, issued two steps ahead:
+//   * the 128 x 128 fp16 activations (from the pre-pass): rows of 16 chunks
+//     of 16 bytes, chunk c of row r stored at r*16 + (c ^ (r & 15)), so the
+//     16 lanes reading one operand column hit 16 different bank groups;
+//   * the 128 weight rows' 64 nibble bytes of this half superblock: rows of
+//     four 16-byte units, unit u of row r stored at r*4 + (u ^ ((r >> 2) & 3)),
+//     so the 8-byte operand reads are conflict-free;
+//   * the 128 superblock headers (d, dmin, scale fields).
+// No vector register is the destination of a prefetch, so nothing makes the
+// compiler wait early; the explicit waits below are the only ones on them.
+// From LDS each lane takes the 8 nibble bytes of its B operand (column =
+// lane % 16, k = 8 * (lane / 16) .. +8 of a sub-block: low nibbles give one
+// sub-block, high nibbles the next) and dequantizes them in registers
+// straight into the MFMA operand.  One barrier per step.
+constexpr int kPf3Threads = 512;
+constexpr int kPf3ChunkUnits = 16;    // 16-byte chunks per 128-half activation row
+constexpr int kPf3Stages = 3;         // LDS stages: compute one, two in flight
+constexpr int kPf3LoadsPerStep = 6;   // per thread: 4 activation + 1 nibble + 1 header copy
+
+struct __attribute__((aligned(16))) Prefill3Stage {
+    _Float16 a[kPfBM * kPfKS];   // 32 KiB activations, swizzled
+    uint8_t nib[kPfBN * 64];     // 8 KiB nibbles, swizzled
+    uint32_t hdr[kPfBN * 4];     // 2 KiB headers
+};
+
+// The 8 weights of B operand (kk, lane) from 8 nibble bytes: low nibbles
+// (even sub-block) when hi == 0, else high nibbles; times sc, exactly.
+__device__ __forceinline__ half8 b_operand(uint2 nib, int hi, half2v sc2, half2v off2) {
+    const uint32_t a = hi ? (nib.x >> 4) : nib.x;
+    const uint32_t b = hi ? (nib.y >> 4) : nib.y;
+    uint32_t o[4];
+    nibbles_to_half(a & 0x0F0F0F0Fu, sc2, off2, o[0], o[1]);
+    nibbles_to_half(b & 0x0F0F0F0Fu, sc2, off2, o[2], o[3]);
+    return __builtin_bit_cast(half8, u32x4p{o[0], o[1], o[2], o[3]});
+}
+
+// s_waitcnt vmcnt(n), expcnt / lgkmcnt untouched (gfx9 encoding)
+template <int n>
+__device__ __forceinline__ void wait_vmem_at_most() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+__device__ __forceinline__ void global_to_lds4(const void *gsrc, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds_base, 4, 0, 0);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release
+// would wait for every copy still in flight).  Every LDS write of the kernel
+// that uses it is a global -> LDS copy waited for explicitly before the
+// barrier, and every LDS read completes inside its own block; the empty asm
+// statements keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void barrier_no_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// LDS reads issued together and completed inside one asm block, from one base
+// address and immediate offsets.  Written this way because the compiler,
+// unable to place the global -> LDS copies in flight into the other stages,
+// would otherwise wait for all of them before any LDS read; the copies are
+// ordered against these reads by the explicit wait and barrier at the end of
+// every step instead.
+template <int O1, int O2, int O3>
+__device__ __forceinline__ void lds_read4_b128(uint32_t base, u32x4p &r0, u32x4p &r1, u32x4p &r2, u32x4p &r3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:%5\n\t"
+        "ds_read_b128 %2, %4 offset:%6\n\t"
+        "ds_read_b128 %3, %4 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(base), "i"(O1), "i"(O2), "i"(O3)
+        : "memory");
+}
+
+// one k-slice: four 16-byte A fragments (base a, rows 16 apart) and two
+// 8-byte nibble groups (base n, rows 16 apart)
+__device__ __forceinline__ void lds_read_slice(uint32_t a, uint32_t n, u32x4p &r0, u32x4p &r1, u32x4p &r2, u32x4p &r3,
+                                               uint2 &q0, uint2 &q1) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:4096\n\t"
+        "ds_read_b128 %2, %6 offset:8192\n\t"
+        "ds_read_b128 %3, %6 offset:12288\n\t"
+        "ds_read_b64 %4, %7\n\t"
+        "ds_read_b64 %5, %7 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(q0), "=&v"(q1)
+        : "v"(a), "v"(n)
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_read2_b128_256(uint32_t base, u32x4p &r0, u32x4p &r1) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:256\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1)
+        : "v"(base)
+        : "memory");
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0): also every LDS write of this wave is done
+template <int n>
+__device__ __forceinline__ void wait_vmem_lgkm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14));
+}
+
+
+// Steps run six at a time, so that a step's stage (g % 3) and half superblock
+// (g % 2) are compile-time constants of the unrolled body: the compiler then
+// sees that a step's LDS reads and the copies in flight into the other stages
+// are disjoint and waits for nothing early.  Up to five remaining steps run
+// in a guarded tail with the same property.  Copies past the last step
+// re-read the last step's data, so every step issues the same copies.
+__global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
+    const uint8_t *__restrict__ W, int N, int K, int M, const _Float16 *__restrict__ X16,
+    const _Float16 *__restrict__ S_hi, const _Float16 *__restrict__ S_lo, const int32_t *__restrict__ E_x,
+    float *__restrict__ Y) {
+    // three stages as three LDS objects: the compiler tells a stage's reads
+    // from the copies in flight into another stage by object, not by offset
+    __shared__ Prefill3Stage st0, st1, st2;
+    // sums of the 32-input blocks of the current min-term window, S * 2^(e-6)
+    // split into fp16 hi + lo: [row][8 * (superblock in window) + sub-block]
+    __shared__ __attribute__((aligned(16))) _Float16 wsum_hi[kPfBM * 32], wsum_lo[kPfBM * 32];
+    auto stage_ref = [&](auto sc) -> Prefill3Stage & {
+        constexpr int i = decltype(sc)::value;
+        if constexpr (i == 0)
+            return st0;
+        else if constexpr (i == 1)
+            return st1;
+        else
+            return st2;
+    };
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;  // 64 tokens x 32 rows
+    const int n0 = blockIdx.x * kPfBN, m0 = blockIdx.y * kPfBM;
+    const int nsb = K / 256;
+    const int nsteps = 2 * nsb;
+    const size_t row_bytes = (size_t)nsb * 144;
+    const int quad = lane >> 4, l16 = lane & 15;
+
+    // copy roles of this thread (fixed over the steps)
+    const int nib_row = 16 * wave + (lane >> 2);                      // weight row whose nibbles it copies
+    const int nib_unit = (lane & 3) ^ ((nib_row >> 2) & 3);           // logical 16-byte unit it fetches
+    const uint8_t *nib_src = W + (size_t)min(n0 + nib_row, N - 1) * row_bytes + 16 + 16 * nib_unit;
+    const int hdr_row = tid >> 2;                                     // header dword tid % 4 of row tid / 4
+    const uint8_t *hdr_src = W + (size_t)min(n0 + hdr_row, N - 1) * row_bytes + 4 * (tid & 3);
+
+    auto issue = [&](int g, auto stage) {
+        const int gl = min(g, nsteps - 1);
+        const int k0 = 128 * gl;
+        Prefill3Stage &S = stage_ref(stage);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int seg = 4 * wave + i;
+            const int r = 4 * seg + quad;
+            const int c = l16 ^ (r & 15);  // logical chunk held by physical slot l16
+            global_to_lds16(X16 + (size_t)min(m0 + r, M - 1) * K + k0 + 8 * c, S.a + seg * 64 * 8);
+        }
+        const int s = gl >> 1, h = gl & 1;
+        global_to_lds16(nib_src + (size_t)s * 144 + 64 * h, S.nib + wave * 1024);
+        global_to_lds4(hdr_src + (size_t)s * 144, S.hdr + wave * 64);
+    };
+
+    f32x4 acc[4][2], cs[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = cs[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // this lane's B rows inside the tile
+    int brow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) brow[j] = 32 * wn + 16 * j + l16;
+
+    u32x4p mhd[2] = {u32x4p{0, 0, 0, 0}, u32x4p{0, 0, 0, 0}};  // min-term headers of this lane's slot
+
+    // Step g = g6 + k (g6 a multiple of 6): issue step g+2 into stage
+    // (k+2) % 3, compute step g from stage k % 3, wait for step g+1's copies,
+    // barrier.  The min-term window closes after every fourth superblock and
+    // after the last one.
+    auto step = [&](auto kc, int g6) {
+        constexpr int k = decltype(kc)::value;
+        constexpr int h = k & 1;
+        constexpr int stage = k % kPf3Stages;
+        const int g = g6 + k;
+        const int s = g >> 1;
+        const bool window_end = h == 1 && ((s & (kPfWin - 1)) == kPfWin - 1 || s == nsb - 1);
+        // min-term bookkeeping: superblocks sb_start .. s of the window; slot =
+        // lane / 16 is the superblock whose header this lane keeps
+        const int sb_start = s - (s & (kPfWin - 1));
+        const bool mlive = sb_start + quad <= s;
+        issue(g + 2, std::integral_constant<int, (k + 2) % kPf3Stages>{});
+        const Prefill3Stage &S = stage_ref(std::integral_constant<int, stage>{});
+        {
+            // this step's 32-input block sums: thread t sums sub-block t % 4 of
+            // row t / 4 (16 fp16 pairs, dot2 against ones into fp32, in order)
+            // (the sub-block's four chunks form one 64-byte group of the swizzled
+            // row, summed in stored order: a fixed order for every row)
+            const int r = tid >> 2, jb = tid & 3;
+            u32x4p v[4];
+            lds_read4_b128<16, 32, 48>(lds_addr(S.a + r * kPf3ChunkUnits * 8 + 32 * (jb ^ ((r & 15) >> 2))), v[0], v[1],
+                                       v[2], v[3]);
+            const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
+            float sum = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                // elements go through scalars: this compiler reads element 0 for a
+                // bit cast taken straight from a vector element
+                const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w[e]), one2, sum, false);
+            }
+            const int at = r * 32 + 8 * (s & (kPfWin - 1)) + 4 * h + jb;
+            split_half(ldexpf(sum, -kPfSumShift), wsum_hi[at], wsum_lo[at]);
+        }
+        // headers of this lane's two columns; scales of this step's four
+        // sub-blocks (fields 4h .. 4h+3), zero for a padding step
+        u32x4p hd[2];
+        lds_read2_b128_256(lds_addr(S.hdr + 4 * brow[0]), hd[0], hd[1]);  // rows brow[0], brow[0] + 16
+        uint32_t bits[2];  // the four 6-bit scale fields 4h .. 4h+3 of each column
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bits[j] = h ? ((hd[j].y >> 24) | (hd[j].z << 8)) : hd[j].y;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            half8 af[4], bf[2];
+            // A rows 64 wm + 16 i + l16 (i = 0..3 at +4096 bytes), chunk
+            // (4 kk + quad) ^ l16; B rows brow[j] (j = 1 at +1024 bytes), 8 bytes at
+            // byte 32 * pair + 8 * quad of the row's 64: unit 2 pair + quad / 2,
+            // swizzled by (row >> 2) & 3 = (l16 >> 2) & 3
+            const int ra = 64 * wm + l16;
+            const uint32_t aa = lds_addr(S.a + (ra * kPf3ChunkUnits + ((4 * kk + quad) ^ l16)) * 8);
+            const int u = (2 * (kk >> 1) + (quad >> 1)) ^ ((l16 >> 2) & 3);
+            const uint32_t na = lds_addr(S.nib + brow[0] * 64 + 16 * u + 8 * (quad & 1));
+            u32x4p ar[4];
+            uint2 nb[2];
+            lds_read_slice(aa, na, ar[0], ar[1], ar[2], ar[3], nb[0], nb[1]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(half8, ar[i]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const _Float16 v = (_Float16)(float)((bits[j] >> (6 * kk)) & 63u);
+                const _Float16 o = (_Float16)(-1024.0f * (float)v);
+                bf[j] = b_operand(nb[j], kk & 1, half2v{v, v}, half2v{o, o});
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    cs[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], cs[i][j], 0, 0, 0);
+        }
+        if constexpr (h == 1) {
+            // superblock done: acc += d * cs, d of this lane's column; the lanes
+            // of this superblock's slot keep its headers for the min term
+            const bool keep = quad == (s & (kPfWin - 1));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mhd[j] = keep ? hd[j] : mhd[j];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float d = half_lo(hd[j].x);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf_exact(d, cs[i][j][e], acc[i][j][e]);
+                    cs[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+        if (window_end) {
+            // min term of the window; slot = lane / 16 is its superblock.  Every
+            // wave's block sums of this step are written first.
+            wait_vmem_lgkm<kPf3LoadsPerStep>();
+            barrier_no_fence();
+            // slots past the window's last superblock hold finite leftovers
+            // (the arrays start zeroed) and meet zero weights below
+            u32x4p t[8];
+            {
+                const int row = 64 * wm + l16;  // rows 16 apart: +1024 bytes
+                lds_read4_b128<1024, 2048, 3072>(lds_addr(wsum_hi + row * 32 + 8 * quad), t[0], t[1], t[2], t[3]);
+                lds_read4_b128<1024, 2048, 3072>(lds_addr(wsum_lo + row * 32 + 8 * quad), t[4], t[5], t[6], t[7]);
+            }
+            half8 mh[2], ml[2];
+            float fac[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float dmin = mlive ? half_hi(mhd[j].x) : 0.0f;
+                float dmax = dmin;
+                dmax = fmaxf(dmax, __shfl_xor(dmax, 16, kWave));
+                dmax = fmaxf(dmax, __shfl_xor(dmax, 32, kWave));
+                const int E = row_exponent(dmax) - 6;
+                fac[j] = -ldexpf(1.0f, kPfSumShift - E);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float mv = ldexpf(dmin * (float)field6(mhd[j].y, mhd[j].z, mhd[j].w, 8 + e), E);
+                    _Float16 hi, lo;
+                    split_half(mv, hi, lo);
+                    mh[j][e] = hi;
+                    ml[j][e] = lo;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const half8 shi = __builtin_bit_cast(half8, t[i]), slo = __builtin_bit_cast(half8, t[4 + i]);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi, mh[j], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi, ml[j], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(slo, mh[j], c, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf_exact(fac[j], c[e], acc[i][j][e]);
+                }
+        }
+        // step g+1's copies have landed (this wave's; the barrier makes it every
+        // wave's) while step g+2's stay in flight; the block sums are written;
+        // after the barrier every wave is also done with stage g % 3, which step
+        // g+3 refills, and with the window's sums before the next window's
+        wait_vmem_lgkm<kPf3LoadsPerStep>();
+        barrier_no_fence();
+    };
+
+    for (int i = tid; i < kPfBM * 32 / 8; i += kPf3Threads) {
+        reinterpret_cast<u32x4p *>(wsum_hi)[i] = u32x4p{0, 0, 0, 0};
+        reinterpret_cast<u32x4p *>(wsum_lo)[i] = u32x4p{0, 0, 0, 0};
+    }
+    issue(0, std::integral_constant<int, 0>{});
+    issue(1, std::integral_constant<int, 1>{});
+    wait_vmem_lgkm<kPf3LoadsPerStep>();  // step 0's copies and the zeroed sums are in LDS
+    barrier_no_fence();
+    const int nbody = nsteps - nsteps % 6;
+    int g6 = 0;
+    for (; g6 < nbody; g6 += 6) {
+        step(std::integral_constant<int, 0>{}, g6);
+        step(std::integral_constant<int, 1>{}, g6);
+        step(std::integral_constant<int, 2>{}, g6);
+        step(std::integral_constant<int, 3>{}, g6);
+        step(std::integral_constant<int, 4>{}, g6);
+        step(std::integral_constant<int, 5>{}, g6);
+    }
+    // tail: nsteps is even, so 0, 2 or 4 steps remain
+    if (g6 < nsteps) {
+        step(std::integral_constant<int, 0>{}, g6);
+        step(std::integral_constant<int, 1>{}, g6);
+    }
+    if (g6 + 2 < nsteps) {
+        step(std::integral_constant<int, 2>{}, g6);
+        step(std::integral_constant<int, 3>{}, g6);
+    }
+    wait_vmem_at_most<0>();  // no copy into LDS may still be in flight when the workgroup ends
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = m0 + 64 * wm + 16 * i + 4 * quad + e;
+            if (m >= M) continue;
+            const int ex = E_x[m];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int n = n0 + 32 * wn + 16 * j + l16;
+                if (n < N) Y[(size_t)m * N + n] = ldexpf(acc[i][j][e], -ex);
+            }
+        }
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct PrefillWs {
@@ -437,7 +820,7 @@ extern "C" int qgemm_prefill_ws(int fmt, const void *W, int N, int K, const uint
                        K, x16, s_hi, s_lo, ex);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
     dim3 grid((N + qg::kPfBN - 1) / qg::kPfBN, (M + qg::kPfBM - 1) / qg::kPfBM);
-    hipLaunchKernelGGL(qg::qgemm_prefill_q4k_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream,
-                       reinterpret_cast<const uint8_t *>(W), N, K, x_bf16, M, x16, s_hi, s_lo, ex, y);
+    hipLaunchKernelGGL(qg::qgemm_prefill_q4k_ws_kernel, grid, dim3(qg::kPf3Threads), 0, (hipStream_t)stream,
+                       reinterpret_cast<const uint8_t *>(W), N, K, M, x16, s_hi, s_lo, ex, y);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
