@@ -273,7 +273,10 @@ int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t *sx, int T
  * reports).
  *   Y[m, n] = sum_k w[n, k] * x[m, k],  w from QG_FMT_Q4K W [N, K],
  *   x bf16 [M, K] (raw bits), Y fp32 [M, N], fp32 accumulation on matrix
- *   cores (error well under 1e-5 * sum |w * x| per output).
+ *   cores (error well under 1e-5 * sum |w * x| per output).  x is converted
+ *   to fp16 as it is: |x| must not exceed 65504, and |x| below 2^-17 loses
+ *   low bits (qgemm_prefill_ws has no such limit).  d and dmin may take any
+ *   fp16 value.
  * Errors: QG_ERR_FORMAT (only QG_FMT_Q4K); QG_ERR_NULL; QG_ERR_SHAPE unless
  * M >= 1, N >= 1, K % 256 == 0, 256 <= K <= QG_MAX_K; QG_ERR_ALIGN;
  * QG_ERR_LAUNCH.
@@ -282,19 +285,20 @@ int qgemm_prefill(int fmt, const void *W, int N, int K, const uint16_t *x_bf16, 
 
 /*
  * qgemm_prefill_workspace_bytes -- size of the device workspace that
- * qgemm_prefill_ws needs for M tokens of K inputs (x as fp16 [M, K] and the
- * per-32-input sums of x split into two fp16 halves [M, K/32] each, every
- * region 256-byte aligned).  Returns 0 for an invalid shape (the rules of
+ * qgemm_prefill_ws needs for M tokens of K inputs: x scaled by a power of two
+ * per token as fp16 [M, K], then the int32 exponents [M], each region
+ * 256-byte aligned.  Returns 0 for an invalid shape (the rules of
  * qgemm_prefill).
  */
 size_t qgemm_prefill_workspace_bytes(int M, int K);
 
 /*
  * qgemm_prefill_ws -- [PR621] the same product as qgemm_prefill, with the
- * bf16 -> fp16 conversion of x and its 32-input sums done once by a separate
- * pass into the caller's workspace, so that the GEMM reads them instead of
- * converting x once per 128-row weight tile.  Results are bit-identical to
- * qgemm_prefill.  ws is device memory owned by the caller (at least
+ * bf16 -> fp16 conversion of x done once by a separate pass into the caller's
+ * workspace, each token scaled by a power of two so that any finite bf16
+ * activation converts exactly (qgemm_prefill needs |x| <= 65504), and a
+ * faster GEMM that reads it.  Results agree with qgemm_prefill to rounding
+ * (the same error bound).  ws is device memory owned by the caller (at least
  * qgemm_prefill_workspace_bytes(M, K) bytes, 16-byte aligned); its contents on
  * entry are ignored and on return are unspecified.  Calls that share a
  * workspace must be ordered on one stream.

@@ -507,18 +507,10 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
     const int r = lane >> tg.lsh;
     const int g = lane & (tg.lpr - 1);
 
-    auto compute = [&](const UnitRegs<U> &u0, int tile, bool valid, int m0, int mtc) {
+    auto compute = [&](const UnitRegs<U> &u, int tile, bool valid, int m0, int mtc) {
         const int row = tile * tg.rpt + r;
         if (ONE) mtc = 1;
-        UnitRegs<U> u = u0;
         for (int mm = 0; mm < mtc; ++mm) {
-            // the Q4_K unit's decode (nibble masks, scale and min fields) stays
-            // inside the token loop: hoisted, it holds far more registers than
-            // the packed unit and costs occupancy (for Q8_0 hoisting is cheaper)
-            if (!ONE && FMT == QG_FMT_Q4K) {
-#pragma unroll
-                for (int i = 0; i < U::dwords; ++i) asm volatile("" : "+v"(u.w[i]));
-            }
             float p = 0.0f;
             if (valid) {
                 int32_t isum_tmp[U::blocks];

@@ -20,22 +20,19 @@
 // power of two and is undone exactly.  Plain bf16 or fp16 dequantization of w
 // would not meet 1e-5 * sum |w x|.
 //
-// Tiling (gfx950, wave64): 128 tokens x 128 weight rows per workgroup, four
-// waves of 64 x 64, v_mfma_f32_16x16x32_f16 (A: lane l holds row l%16, k
-// 8*(l/16)..+8; B: column l%16, same k; C: rows 4*(l/16)+i, column l%16).
-// K advances 128 (half a superblock) per step.  Each step the workgroup
-// dequantizes its 128 x 128 weight slice once into LDS as fp16 sc*q (nibbles
-// are widened with byte permutes into fp16 1024+q, and one packed fp16 fma per
-// pair, (1024+q)*sc - 1024*sc, gives sc*q exactly) and stages the activations
-// as fp16, both with padded row strides so the 16-byte operand reads are
-// bank-conflict free.  The global reads of the next step are issued before
-// the current step's MFMAs, so they overlap.
-//
-// Two forms.  qgemm_prefill converts bf16 -> fp16 and forms the sub-block sums
-// inside the GEMM, with e = 0 (so it needs |x| <= 65504 and loses low bits of
-// |x| < 2^-17).  qgemm_prefill_ws first runs a pass, one workgroup per token,
-// that finds e, writes x*2^e as fp16 and the hi/lo sums to a caller workspace;
-// the GEMM then reads them instead of converting once per weight tile.
+// Two forms.
+//   qgemm_prefill: 128 tokens x 128 weight rows per workgroup, four waves of
+//   64 x 64, v_mfma_f32_16x16x32_f16 (A: lane l holds row l%16, k 8*(l/16)..+8;
+//   B: column l%16, same k; C: rows 4*(l/16)+i, column l%16), K steps of 128.
+//   Each step the workgroup dequantizes its 128 x 128 weight slice once into
+//   LDS as fp16 sc*q (nibbles are widened with byte permutes into fp16 1024+q,
+//   and one packed fp16 fma per pair, (1024+q)*sc - 1024*sc, gives sc*q
+//   exactly) and converts the activations bf16 -> fp16 into LDS (e = 0, so it
+//   needs |x| <= 65504 and loses low bits of |x| < 2^-17), with padded rows.
+//   qgemm_prefill_ws: a pre-pass (one workgroup per token) finds e and writes
+//   x * 2^e as fp16 to a caller workspace; the GEMM (eight waves, operands
+//   through pipelined global -> LDS copies, weights dequantized in registers;
+//   described at the kernel) reads it from there.
 #include <type_traits>
 
 #include "common.h"
@@ -113,13 +110,9 @@ __device__ __forceinline__ int row_exponent(float amax) {
 
 // ------------------------------------------------------------------ pre-pass
 
-// One workgroup per token m: e[m], X16[m] = x*2^e (fp16), and the sums of each
-// 32-block split as S*2^(e-6) = hi + lo (fp16).  Lane group of 8 per block,
-// four values per lane.
+// One workgroup per token m: e[m] and X16[m] = x * 2^e (fp16).
 __global__ __launch_bounds__(kPfPreThreads) void prefill_prepass_kernel(const uint16_t *__restrict__ X, int K,
                                                                         _Float16 *__restrict__ X16,
-                                                                        _Float16 *__restrict__ s_hi,
-                                                                        _Float16 *__restrict__ s_lo,
                                                                         int32_t *__restrict__ e_out) {
     __shared__ float red[kPfPreThreads / kWave];
     const int m = blockIdx.x, tid = threadIdx.x;
@@ -136,23 +129,12 @@ __global__ __launch_bounds__(kPfPreThreads) void prefill_prepass_kernel(const ui
     for (int i = 1; i < kPfPreThreads / kWave; ++i) amax = fmaxf(amax, red[i]);
     const int e = row_exponent(amax);
     if (tid == 0) e_out[m] = e;
-
     for (int k = 4 * tid; k < K; k += 4 * kPfPreThreads) {
         const uint2 w = *reinterpret_cast<const uint2 *>(xr + k);
-        const float v0 = bf_lo(w.x), v1 = bf_hi(w.x), v2 = bf_lo(w.y), v3 = bf_hi(w.y);
-        const half2v h0 = {(_Float16)ldexpf(v0, e), (_Float16)ldexpf(v1, e)};
-        const half2v h1 = {(_Float16)ldexpf(v2, e), (_Float16)ldexpf(v3, e)};
+        const half2v h0 = {(_Float16)ldexpf(bf_lo(w.x), e), (_Float16)ldexpf(bf_hi(w.x), e)};
+        const half2v h1 = {(_Float16)ldexpf(bf_lo(w.y), e), (_Float16)ldexpf(bf_hi(w.y), e)};
         *reinterpret_cast<uint2 *>(X16 + (size_t)m * K + k) =
             make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
-        // block sum: lanes 8b .. 8b+7 hold block b's four-value partial sums in order
-        float s = quad_sum(v0, v1, v2, v3);
-        s += __shfl_xor(s, 1, kWave);
-        s += __shfl_xor(s, 2, kWave);
-        s += __shfl_xor(s, 4, kWave);
-        if ((tid & 7) == 0) {
-            const size_t blk = (size_t)m * (K / 32) + (size_t)(k / 32);
-            split_half(ldexpf(s, e - kPfSumShift), s_hi[blk], s_lo[blk]);
-        }
     }
 }
 
@@ -165,13 +147,8 @@ struct PfRegs {
     u32x4p q[2];  // 32 bytes of nibbles
 };
 
-template <bool XPRE>
 __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *__restrict__ W, int N, int K,
                                                                 const uint16_t *__restrict__ X, int M,
-                                                                const _Float16 *__restrict__ X16,
-                                                                const _Float16 *__restrict__ S_hi,
-                                                                const _Float16 *__restrict__ S_lo,
-                                                                const int32_t *__restrict__ E_x,
                                                                 float *__restrict__ Y) {
     __shared__ PrefillLds L;
     const int tid = threadIdx.x;
@@ -199,8 +176,7 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
         const int s = g >> 1, h = g & 1;
         const size_t k0 = (size_t)s * 256 + 128 * h + 64 * part;
         if (xrow_ok) {
-            const u32x4p *src = XPRE ? reinterpret_cast<const u32x4p *>(X16 + (size_t)(m0 + r) * K + k0)
-                                     : reinterpret_cast<const u32x4p *>(X + (size_t)(m0 + r) * K + k0);
+            const u32x4p *src = reinterpret_cast<const u32x4p *>(X + (size_t)(m0 + r) * K + k0);
 #pragma unroll
             for (int c = 0; c < 8; ++c) pr.x[c] = src[c];
         } else {
@@ -248,25 +224,20 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
             if (h == 0 && part == 0) L.d[r] = half_lo(pr.hdr.x);
 
             _Float16 *arow = L.a + r * kPfLd + 64 * part;
-            if (XPRE) {
+            // bf16 -> fp16, and the two sub-block sums (fixed order)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4p *>(arow + 8 * c) = pr.x[c];
-            } else {
-                // bf16 -> fp16, and the two sub-block sums (the pre-pass's order)
+            for (int j = 0; j < 2; ++j) {
+                float t[8];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float t[8];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const u32x4p v = pr.x[4 * j + c];
-                        *reinterpret_cast<u32x4p *>(arow + 32 * j + 8 * c) =
-                            u32x4p{bf16x2_to_half2(v.x), bf16x2_to_half2(v.y), bf16x2_to_half2(v.z), bf16x2_to_half2(v.w)};
-                        t[2 * c] = quad_sum(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
-                        t[2 * c + 1] = quad_sum(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
-                    }
-                    const int idx = r * kPfSLd + 8 * q + 4 * h + 2 * part + j;
-                    split_half(ldexpf(sub_block_sum(t), -kPfSumShift), L.s_hi[idx], L.s_lo[idx]);
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4p v = pr.x[4 * j + c];
+                    *reinterpret_cast<u32x4p *>(arow + 32 * j + 8 * c) =
+                        u32x4p{bf16x2_to_half2(v.x), bf16x2_to_half2(v.y), bf16x2_to_half2(v.z), bf16x2_to_half2(v.w)};
+                    t[2 * c] = quad_sum(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
+                    t[2 * c + 1] = quad_sum(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
                 }
+                const int idx = r * kPfSLd + 8 * q + 4 * h + 2 * part + j;
+                split_half(ldexpf(sub_block_sum(t), -kPfSumShift), L.s_hi[idx], L.s_lo[idx]);
             }
         }
         __syncthreads();
@@ -317,10 +288,6 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
                     const int mr = 64 * wm + 16 * i + (lane & 15);
                     if (!live) {
                         sh[i] = sl[i] = zero;
-                    } else if (XPRE) {
-                        const size_t o = (size_t)min(m0 + mr, M - 1) * (K / 32) + (size_t)(sb0 + slot) * 8;
-                        sh[i] = *reinterpret_cast<const half8 *>(S_hi + o);
-                        sl[i] = *reinterpret_cast<const half8 *>(S_lo + o);
                     } else {
                         sh[i] = *reinterpret_cast<const half8 *>(L.s_hi + mr * kPfSLd + 8 * slot);
                         sl[i] = *reinterpret_cast<const half8 *>(L.s_lo + mr * kPfSLd + 8 * slot);
@@ -370,11 +337,10 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
         for (int e = 0; e < 4; ++e) {
             const int m = m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + e;
             if (m >= M) continue;
-            const int ex = XPRE ? E_x[m] : 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = n0 + 64 * wn + 16 * j + (lane & 15);
-                if (n < N) Y[(size_t)m * N + n] = XPRE ? ldexpf(acc[i][j][e], -ex) : acc[i][j][e];
+                if (n < N) Y[(size_t)m * N + n] = acc[i][j][e];
             }
         }
 }
@@ -467,6 +433,43 @@ __device__ __forceinline__ void lds_read4_b128(uint32_t base, u32x4p &r0, u32x4p
         : "memory");
 }
 
+__device__ __forceinline__ void lds_read4_b128_addr(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4p &r0,
+                                                    u32x4p &r1, u32x4p &r2, u32x4p &r3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+
+// two k-slices: for each, four 16-byte A fragments (rows 16 apart) and two
+// 8-byte nibble groups (rows 16 apart)
+__device__ __forceinline__ void lds_read_slice2(uint32_t a, uint32_t n, uint32_t a2, uint32_t n2, u32x4p (&r)[8],
+                                                uint2 (&q)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %12 offset:4096\n\t"
+        "ds_read_b128 %2, %12 offset:8192\n\t"
+        "ds_read_b128 %3, %12 offset:12288\n\t"
+        "ds_read_b64 %8, %13\n\t"
+        "ds_read_b64 %9, %13 offset:1024\n\t"
+        "ds_read_b128 %4, %14\n\t"
+        "ds_read_b128 %5, %14 offset:4096\n\t"
+        "ds_read_b128 %6, %14 offset:8192\n\t"
+        "ds_read_b128 %7, %14 offset:12288\n\t"
+        "ds_read_b64 %10, %15\n\t"
+        "ds_read_b64 %11, %15 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3])
+        : "v"(a), "v"(n), "v"(a2), "v"(n2)
+        : "memory");
+}
+
 // one k-slice: four 16-byte A fragments (base a, rows 16 apart) and two
 // 8-byte nibble groups (base n, rows 16 apart)
 __device__ __forceinline__ void lds_read_slice(uint32_t a, uint32_t n, u32x4p &r0, u32x4p &r1, u32x4p &r2, u32x4p &r3,
@@ -510,8 +513,7 @@ __device__ __forceinline__ void wait_vmem_lgkm() {
 // re-read the last step's data, so every step issues the same copies.
 __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
     const uint8_t *__restrict__ W, int N, int K, int M, const _Float16 *__restrict__ X16,
-    const _Float16 *__restrict__ S_hi, const _Float16 *__restrict__ S_lo, const int32_t *__restrict__ E_x,
-    float *__restrict__ Y) {
+    const int32_t *__restrict__ E_x, float *__restrict__ Y) {
     // three stages as three LDS objects: the compiler tells a stage's reads
     // from the copies in flight into another stage by object, not by offset
     __shared__ Prefill3Stage st0, st1, st2;
@@ -594,10 +596,15 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
             // row t / 4 (16 fp16 pairs, dot2 against ones into fp32, in order)
             // (the sub-block's four chunks form one 64-byte group of the swizzled
             // row, summed in stored order: a fixed order for every row)
+            // (read in an order rotated by the row, so the 16 lanes of a read hit
+            // 16 different bank groups)
             const int r = tid >> 2, jb = tid & 3;
             u32x4p v[4];
-            lds_read4_b128<16, 32, 48>(lds_addr(S.a + r * kPf3ChunkUnits * 8 + 32 * (jb ^ ((r & 15) >> 2))), v[0], v[1],
-                                       v[2], v[3]);
+            const _Float16 *grp = S.a + r * kPf3ChunkUnits * 8 + 32 * (jb ^ ((r & 15) >> 2));
+            uint32_t ad[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) ad[c] = lds_addr(grp + 8 * ((c + r) & 3));
+            lds_read4_b128_addr(ad[0], ad[1], ad[2], ad[3], v[0], v[1], v[2], v[3]);
             const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
             float sum = 0.0f;
 #pragma unroll
@@ -619,32 +626,41 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j) bits[j] = h ? ((hd[j].y >> 24) | (hd[j].z << 8)) : hd[j].y;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            half8 af[4], bf[2];
+        for (int kp = 0; kp < 4; kp += 2) {
             // A rows 64 wm + 16 i + l16 (i = 0..3 at +4096 bytes), chunk
             // (4 kk + quad) ^ l16; B rows brow[j] (j = 1 at +1024 bytes), 8 bytes at
             // byte 32 * pair + 8 * quad of the row's 64: unit 2 pair + quad / 2,
             // swizzled by (row >> 2) & 3 = (l16 >> 2) & 3
-            const int ra = 64 * wm + l16;
-            const uint32_t aa = lds_addr(S.a + (ra * kPf3ChunkUnits + ((4 * kk + quad) ^ l16)) * 8);
-            const int u = (2 * (kk >> 1) + (quad >> 1)) ^ ((l16 >> 2) & 3);
-            const uint32_t na = lds_addr(S.nib + brow[0] * 64 + 16 * u + 8 * (quad & 1));
-            u32x4p ar[4];
-            uint2 nb[2];
-            lds_read_slice(aa, na, ar[0], ar[1], ar[2], ar[3], nb[0], nb[1]);
+            uint32_t aa[2], na[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(half8, ar[i]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const _Float16 v = (_Float16)(float)((bits[j] >> (6 * kk)) & 63u);
-                const _Float16 o = (_Float16)(-1024.0f * (float)v);
-                bf[j] = b_operand(nb[j], kk & 1, half2v{v, v}, half2v{o, o});
+            for (int t = 0; t < 2; ++t) {
+                const int kk = kp + t;
+                const int ra = 64 * wm + l16;
+                aa[t] = lds_addr(S.a + (ra * kPf3ChunkUnits + ((4 * kk + quad) ^ l16)) * 8);
+                const int u = (2 * (kk >> 1) + (quad >> 1)) ^ ((l16 >> 2) & 3);
+                na[t] = lds_addr(S.nib + brow[0] * 64 + 16 * u + 8 * (quad & 1));
             }
+            u32x4p ar[8];
+            uint2 nb[4];
+            lds_read_slice2(aa[0], na[0], aa[1], na[1], ar, nb);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int t = 0; t < 2; ++t) {
+                const int kk = kp + t;
+                half8 af[4], bf[2];
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    cs[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], cs[i][j], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(half8, ar[4 * t + i]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const _Float16 v = (_Float16)(float)((bits[j] >> (6 * kk)) & 63u);
+                    const _Float16 o = (_Float16)(-1024.0f * (float)v);
+                    bf[j] = b_operand(nb[2 * t + j], kk & 1, half2v{v, v}, half2v{o, o});
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        cs[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], cs[i][j], 0, 0, 0);
+            }
         }
         if constexpr (h == 1) {
             // superblock done: acc += d * cs, d of this lane's column; the lanes
@@ -763,16 +779,12 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct PrefillWs {
-    size_t off_shi, off_slo, off_e, total;
+    size_t off_e, total;
 };
 
 static PrefillWs prefill_ws_layout(int M, int K) {
     PrefillWs w;
-    const size_t x16 = align256((size_t)M * K * 2);
-    const size_t s = align256((size_t)M * (K / 32) * 2);
-    w.off_shi = x16;
-    w.off_slo = x16 + s;
-    w.off_e = x16 + 2 * s;
+    w.off_e = align256((size_t)M * K * 2);
     w.total = w.off_e + align256((size_t)M * 4);
     return w;
 }
@@ -793,8 +805,8 @@ extern "C" int qgemm_prefill(int fmt, const void *W, int N, int K, const uint16_
     const int rc = qg::prefill_check(fmt, W, N, K, x_bf16, M, y);
     if (rc) return rc;
     dim3 grid((N + qg::kPfBN - 1) / qg::kPfBN, (M + qg::kPfBM - 1) / qg::kPfBM);
-    hipLaunchKernelGGL(qg::qgemm_prefill_q4k_kernel<false>, grid, dim3(256), 0, (hipStream_t)stream,
-                       reinterpret_cast<const uint8_t *>(W), N, K, x_bf16, M, nullptr, nullptr, nullptr, nullptr, y);
+    hipLaunchKernelGGL(qg::qgemm_prefill_q4k_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<const uint8_t *>(W), N, K, x_bf16, M, y);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
@@ -813,14 +825,12 @@ extern "C" int qgemm_prefill_ws(int fmt, const void *W, int N, int K, const uint
     if (ws_bytes < lay.total) return QG_ERR_WORKSPACE;
     uint8_t *b = reinterpret_cast<uint8_t *>(ws);
     _Float16 *x16 = reinterpret_cast<_Float16 *>(b);
-    _Float16 *s_hi = reinterpret_cast<_Float16 *>(b + lay.off_shi);
-    _Float16 *s_lo = reinterpret_cast<_Float16 *>(b + lay.off_slo);
     int32_t *ex = reinterpret_cast<int32_t *>(b + lay.off_e);
     hipLaunchKernelGGL(qg::prefill_prepass_kernel, dim3(M), dim3(qg::kPfPreThreads), 0, (hipStream_t)stream, x_bf16,
-                       K, x16, s_hi, s_lo, ex);
+                       K, x16, ex);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
     dim3 grid((N + qg::kPfBN - 1) / qg::kPfBN, (M + qg::kPfBM - 1) / qg::kPfBM);
     hipLaunchKernelGGL(qg::qgemm_prefill_q4k_ws_kernel, grid, dim3(qg::kPf3Threads), 0, (hipStream_t)stream,
-                       reinterpret_cast<const uint8_t *>(W), N, K, M, x16, s_hi, s_lo, ex, y);
+                       reinterpret_cast<const uint8_t *>(W), N, K, M, x16, ex, y);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
