@@ -423,6 +423,24 @@ def run_probe(name: str, steps: int, warmup: int, qg, torch) -> None:
         step = DecodeStep(qg, torch)
         step.step(0)  # quantized activations for the projection
         fn = step.out_gemv
+    elif name == "gemv_batch":
+        # the batched Q8_0 sweep's largest batch: 16384 x 4096, 32 tokens
+        w = synth.WORKLOADS["q8_0_16384x4096"]
+        g = synth.rng(w["seed"])
+        N, K, M = w["N"], w["K"], max(w["Ms"])
+        W_host = synth.q8_0_weight(g, N, K)
+        R = rotation_count(W_host.nbytes)
+        base = torch.from_numpy(W_host).to("cuda")
+        copies = [base] + [base.clone() for _ in range(R - 1)]
+        x = torch.from_numpy(synth.activations(g, M, K)).to("cuda")
+        qx = torch.empty(M, K, dtype=torch.int8, device="cuda")
+        dx = torch.empty(M, K // 32, dtype=torch.float32, device="cuda")
+        sx = torch.empty(M, K // 32, dtype=torch.int32, device="cuda")
+        qg.quantize_act_q8(x, M, K, qx, dx, sx)
+        y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+
+        def fn(i):
+            qg.qgemv_q8_0(copies[i % R], N, K, qx, dx, M, y)
     elif name == "copy":
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

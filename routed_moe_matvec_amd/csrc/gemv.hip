@@ -12,6 +12,8 @@
 namespace qg {
 
 constexpr int kGemvMaxWaves = 8;
+// smallest Q8_0 token batch served by the matrix-core form
+constexpr int kMmMinTokens = 4;
 
 struct GemvArgs {
     const uint8_t *W0;
@@ -150,6 +152,10 @@ static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2
     a.M = M;
     a.isum = isum;
     a.G = G;
+    // batches of kMmMinTokens or more Q8_0 tokens go to the matrix cores
+    // (same results bit for bit)
+    if (fmt == QG_FMT_Q8_0 && !f32 && !isum && M >= kMmMinTokens)
+        return gemv_mm_q8_0(a.W0, N1, y1, a.W1, N2, y2, K, act.qx, act.dx, M, G, stream);
     if (isum) return launch_fmt<true, false>(fmt, a, stream);
     return f32 ? launch_fmt<false, true>(fmt, a, stream) : launch_fmt<false, false>(fmt, a, stream);
 }

@@ -1,0 +1,410 @@
+// Batched decode mat-vec on the matrix cores: Q8_0 weights x Q8 activation
+// for a batch of tokens ("ROCm: restore DeepSeek V4 Flash decode performance
+// and Q4 SSD streaming", antirez/ds4 PR 623: the Q8_0 projections on a
+// prequantized activation; the page's kernels take one token per call, this
+// form serves the batched calls of the same projections).
+//
+// Numerics are those of the one-token engine, so a batched call reproduces
+// the one-token call bit for bit on every token:
+//   * a v_mfma_i32_32x32x32_i8 per 32-block gives the exact integer block sum
+//     isum[n, m, b] for 32 rows x 32 tokens;
+//   * s = fp32(dw[n, b] * dx[m, b]) and acc = fma(isum, s, acc) in block
+//     order inside each unit of NB blocks (the one-token engine's per-lane
+//     unit), starting from +0;
+//   * the units of a row are summed by the same pairwise tree over the next
+//     power of two of units (the one-token engine's xor butterfly, padded
+//     with zeros).
+//
+// Work split: a workgroup owns 32 rows of one matrix; its KS waves take
+// consecutive, power-of-two-aligned slices of the row's 256-weight groups, so
+// each slice is a subtree of the unit tree.  A wave streams its 32 rows'
+// groups through registers into a private LDS stage (the next group's loads
+// stay in flight while the current one is multiplied), builds a small table of
+// the stage's fp16 block scales, and keeps one partial sum per tree level.  The
+// slices' subtree sums meet in LDS and are added in tree order.
+//
+// MFMA roles: A = weights (row i = lane % 32, 16 of the block's 32 quants per
+// lane half), B = activation (token j = lane % 32).  The 32x32 i32 result puts
+// token lane % 32 and rows 8q + 4 (lane / 32) + t (q, t < 4) in a lane's 16
+// registers, so one activation scale and 16 weight scales scale a lane's sums.
+#include <type_traits>
+
+#include "common.h"
+#include "gemv_device.h"
+
+namespace qg {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+constexpr int kMmRows = 32;                             // weight rows of a workgroup
+constexpr int kMmParts = 17;                            // 16-byte parts of a row's 272-byte group
+constexpr int kMmStageBytes = kMmParts * kMmRows * 16;  // one group of 32 rows: [part][row] x 16 B
+constexpr int kMmScaleBytes = 8 * kMmRows * 2;          // fp16 scales of a group: [block][lane half][16]
+// LDS of a wave: the stage, the scale table and the pending tree levels 1
+// and 2 (slices of four or eight groups)
+constexpr int mm_wave_lds(int gps) { return kMmStageBytes + kMmScaleBytes + (gps >= 8 ? 2 : gps >= 4 ? 1 : 0) * 16 * 64 * 4; }
+constexpr int kMmMaxSlices = 8;       // waves of a workgroup
+constexpr int kMmMaxGroups = 8;       // groups of a slice (three stored tree levels)
+constexpr int kMmTargetWaves = 2048;  // about two waves per SIMD over the chip
+
+struct MmArgs {
+    const uint8_t *W0, *W1;
+    float *y0, *y1;
+    int N0, N1;
+    int nt0;  // workgroups (32-row tiles) of matrix 0; matrix 1's follow
+    const int8_t *qx;
+    const float *dx;
+    int K, M, G;
+    int row_bytes;
+    int groups;  // 256-weight groups per row
+    int gps;     // groups per slice (power of two)
+    int KS;      // slices = waves per workgroup
+};
+
+template <int NB, int GPS>
+__global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    // the wave index is uniform over the wave: keep it (and every slice bound) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const bool second = (int)blockIdx.x >= a.nt0;
+    const int tile = second ? (int)blockIdx.x - a.nt0 : (int)blockIdx.x;
+    const int N = second ? a.N1 : a.N0;
+    const int g = blockIdx.y;  // grouped call: matrix g against activation slice g
+    const uint8_t *W = (second ? a.W1 : a.W0) + (size_t)g * N * a.row_bytes;
+    float *y = second ? a.y1 : a.y0;
+    const int row0 = tile * kMmRows;
+    constexpr int kWaveLds = mm_wave_lds(GPS);
+    uint8_t *stage = smem + wave * kWaveLds;
+    uint8_t *stab = stage + kMmStageBytes;
+
+    const int grp0 = wave * a.gps;
+    const int ngroups = min(max(a.groups - grp0, 0), a.gps);
+
+    // Group loads: instruction i < 8 reads part 4 (i / 2) + lane % 4 of row
+    // 16 (i % 2) + lane / 4 (a quad of lanes reads 64 consecutive bytes of one
+    // row), instruction 8 part 16 of row lane % 32 (lanes 32..63 repeat it and
+    // do not store).  Rows past N re-read row N - 1.
+    const int rl = lane >> 2, pq = lane & 3, r32 = lane & 31;
+    const uint8_t *wr0 = W + (size_t)min(row0 + rl, N - 1) * a.row_bytes + 16 * pq;
+    const uint8_t *wr1 = W + (size_t)min(row0 + 16 + rl, N - 1) * a.row_bytes + 16 * pq;
+    const uint8_t *wr8 = W + (size_t)min(row0 + r32, N - 1) * a.row_bytes + 256;
+    // activation: token lane % 32 (tokens past M re-read token M - 1; their
+    // columns are not stored), 16 quants of each block per lane half
+    const int half = lane >> 5;
+    const size_t arow = (size_t)min(r32, a.M - 1) * a.G + g;
+    const int8_t *xp = a.qx + arow * a.K + 16 * half;
+    const float *dp = a.dx + arow * (a.K / 32);
+
+    auto load_w = [&](int gi, u32x4 (&w)[9]) __attribute__((always_inline)) {
+        const size_t off = (size_t)gi * 272;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            w[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(((i & 1) ? wr1 : wr0) + off + 64 * (i >> 1)));
+        w[8] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr8 + off));
+    };
+    auto load_dx = [&](int gi, float4 (&d)[2]) __attribute__((always_inline)) {
+        d[0] = reinterpret_cast<const float4 *>(dp + 8 * gi)[0];
+        d[1] = reinterpret_cast<const float4 *>(dp + 8 * gi)[1];
+    };
+    auto load_act = [&](int gi, int b) __attribute__((always_inline)) { return *reinterpret_cast<const i32x4 *>(xp + (size_t)gi * 256 + 32 * b); };
+
+    // Stage layout: part p of row r at 16 (32 p + (r ^ 2 (p % 4))).  The xor
+    // puts the four parts a quad writes and the rows that eight lanes read
+    // at one part in eight different 16-byte bank groups.
+    auto chunk = [&](int p, int r) __attribute__((always_inline)) { return 16 * (32 * p + (r ^ (2 * (p & 3)))); };
+    auto store_w = [&](const u32x4 (&w)[9]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<u32x4 *>(stage + chunk(4 * (i >> 1) + pq, 16 * (i & 1) + rl)) = w[i];
+        if (lane < 32) *reinterpret_cast<u32x4 *>(stage + chunk(16, lane)) = w[8];
+    };
+    // A-operand reads: part p0 + half of row lane % 32 sits at
+    // stage + 512 p0 + abase[p0 % 4]
+    int abase[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) abase[j] = 512 * half + 16 * (r32 ^ (2 * ((j + half) & 3)));
+    // fp16 scales of the stage, arranged so that a lane half reads the 16 rows
+    // 8q + 4 half + t of its MFMA result as 32 consecutive bytes
+    const int slot = ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
+    auto build_scales = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int bb = 4 * half + j;
+            const int off = 34 * bb;
+            const uint16_t v = *reinterpret_cast<const uint16_t *>(stage + chunk(off >> 4, r32) + (off & 15));
+            *reinterpret_cast<uint16_t *>(stab + 2 * (bb * 32 + slot)) = v;
+        }
+    };
+
+    // Tree levels of the slice: st0 (registers) holds a pending group node;
+    // a pending pair (level 1) and quad (level 2) wait in the wave's LDS level
+    // area (16 floats per lane, lane-interleaved); top receives the slice's
+    // full subtree.  Group i of the slice enters with a static index (the step
+    // loop is unrolled), so every carry is fixed code.
+    float st0[16], top[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st0[e] = top[e] = 0.0f;
+    float *lvl = reinterpret_cast<float *>(stage + kMmStageBytes + kMmScaleBytes);  // [level - 1][16][64]
+    auto lvl_store = [&](int k, const float (&v)[16]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) lvl[((k - 1) * 16 + e) * kWave + lane] = v[e];
+    };
+    auto lvl_add = [&](int k, float (&v)[16]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = lvl[((k - 1) * 16 + e) * kWave + lane] + v[e];
+    };
+    auto push = [&](float (&v)[16], auto index) __attribute__((always_inline)) {
+        constexpr int i = decltype(index)::value;
+        if constexpr (GPS == 1) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) top[e] = v[e];
+        } else if constexpr (!(i & 1)) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st0[e] = v[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = st0[e] + v[e];
+            if constexpr (GPS == 2) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) top[e] = v[e];
+            } else if constexpr (!(i & 2)) {
+                lvl_store(1, v);
+            } else {
+                lvl_add(1, v);
+                if constexpr (GPS == 4) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) top[e] = v[e];
+                } else if constexpr (!(i & 4)) {
+                    lvl_store(2, v);
+                } else {
+                    lvl_add(2, v);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) top[e] = v[e];
+                }
+            }
+        }
+    };
+
+    // Group j of the slice, clamped to the slice's last group (and to the
+    // row's last group for an empty slice): loads past the slice's end re-read
+    // a valid group and are not used.
+    auto gclamp = [&](int j) __attribute__((always_inline)) {
+        return min(grp0 + min(j, max(ngroups - 1, 0)), a.groups - 1);
+    };
+    // Weights are requested two groups ahead (two register sets), activations
+    // and their scales one group ahead.
+    u32x4 wreg[2][9];
+    float4 dxv[2];
+    i32x4 act[8];
+    load_w(gclamp(0), wreg[0]);
+    if constexpr (GPS > 1) load_w(gclamp(1), wreg[1]);
+    load_dx(gclamp(0), dxv);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) act[b] = load_act(gclamp(0), b);
+
+    // Step s multiplies group grp0 + s.
+    auto step = [&](auto index) __attribute__((always_inline)) {
+        constexpr int s = decltype(index)::value;
+        constexpr bool PF = s + 1 < GPS;   // activation of the next group
+        constexpr bool PF2 = s + 2 < GPS;  // weights of the group after it
+        const int gnext = gclamp(s + 1);
+        // steps are not interleaved by the scheduler (registers)
+        __builtin_amdgcn_sched_barrier(0);
+        store_w(wreg[s & 1]);
+        build_scales();
+        float4 dxn[2];
+        if constexpr (PF2) load_w(gclamp(s + 2), wreg[s & 1]);
+        if constexpr (PF) load_dx(gnext, dxn);
+        // block b's integer sums: A operand = quants 16 half .. 16 half + 15 of
+        // block b of row lane % 32, realigned from the stage; then the next
+        // group's activation for block b is requested
+        auto block_sums = [&](auto bi) __attribute__((always_inline)) {
+            constexpr int b = decltype(bi)::value;
+            constexpr int o = 34 * b + 2;
+            constexpr int p0 = o >> 4, sh = o & 15, wd = sh >> 2, bs = sh & 3;
+            const u32x4 c0 = *reinterpret_cast<const u32x4 *>(stage + 512 * p0 + abase[p0 & 3]);
+            u32x4 c1 = c0;
+            if constexpr (sh != 0) c1 = *reinterpret_cast<const u32x4 *>(stage + 512 * (p0 + 1) + abase[(p0 + 1) & 3]);
+            const uint32_t D[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            i32x4 A;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) A[k] = (int)(bs ? align_bytes(D[wd + k + 1], D[wd + k], bs) : D[wd + k]);
+            const i32x16 zero = {};
+            const i32x16 is = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, act[b], zero, 0, 0, 0);
+            if constexpr (PF) act[b] = load_act(gnext, b);
+            return is;
+        };
+        float acc[16], acc2[16];
+        // scale and accumulate block b (the next block's product is already issued)
+        auto block_scale = [&](auto bi, const i32x16 &is) __attribute__((always_inline)) {
+            constexpr int b = decltype(bi)::value;
+            const u32x4 s0 = *reinterpret_cast<const u32x4 *>(stab + 64 * b + 32 * half);
+            const u32x4 s1 = *reinterpret_cast<const u32x4 *>(stab + 64 * b + 32 * half + 16);
+            const uint32_t S[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            const float dxb = b < 4 ? dxv[0][b & 3] : dxv[1][b & 3];
+            float *ac = (NB == 4 && b >= 4) ? acc2 : acc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t pair = S[e >> 1];
+                const half2v h = __builtin_bit_cast(half2v, pair);
+                const float dw = (float)((e & 1) ? h.y : h.x);
+                // fp32 product dw * dx (the +0 addend lets it issue as one
+                // mixed-precision fma; a -0 product would become +0, which
+                // no later sum can tell apart, since no sum starts at -0)
+                const float sc = __builtin_fmaf(dw, dxb, 0.0f);
+                const float prev = (b % NB == 0) ? 0.0f : ac[e];
+                ac[e] = fmaf_exact((float)is[e], sc, prev);
+            }
+        };
+        using I = std::integral_constant<int, 0>;
+        i32x16 cur = block_sums(I{});
+        auto body = [&](auto bi) __attribute__((always_inline)) {
+            constexpr int b = decltype(bi)::value;
+            i32x16 nxt;
+            if constexpr (b < 7) nxt = block_sums(std::integral_constant<int, b + 1>{});
+            __builtin_amdgcn_sched_barrier(0);
+            block_scale(bi, cur);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (b < 7) cur = nxt;
+        };
+        body(std::integral_constant<int, 0>{});
+        body(std::integral_constant<int, 1>{});
+        body(std::integral_constant<int, 2>{});
+        body(std::integral_constant<int, 3>{});
+        body(std::integral_constant<int, 4>{});
+        body(std::integral_constant<int, 5>{});
+        body(std::integral_constant<int, 6>{});
+        body(std::integral_constant<int, 7>{});
+        if constexpr (NB == 4) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = acc[e] + acc2[e];
+        }
+        push(acc, index);
+        if constexpr (PF) {
+            dxv[0] = dxn[0];
+            dxv[1] = dxn[1];
+        }
+    };
+    static_assert(GPS == 1 || GPS == 2 || GPS == 4 || GPS == 8, "groups per slice");
+    if (ngroups > 0) step(std::integral_constant<int, 0>{});
+    if constexpr (GPS > 1) {
+        if (ngroups > 1) step(std::integral_constant<int, 1>{});
+    }
+    if constexpr (GPS > 2) {
+        if (ngroups > 2) step(std::integral_constant<int, 2>{});
+        if (ngroups > 3) step(std::integral_constant<int, 3>{});
+    }
+    if constexpr (GPS > 4) {
+        if (ngroups > 4) step(std::integral_constant<int, 4>{});
+        if (ngroups > 5) step(std::integral_constant<int, 5>{});
+        if (ngroups > 6) step(std::integral_constant<int, 6>{});
+        if (ngroups > 7) step(std::integral_constant<int, 7>{});
+    }
+
+    // The slice's subtree: top for a full slice; else the pending levels of
+    // the set bits of ngroups, lowest first (the zero-padded leaves add nothing).
+    float r[16];
+    if (ngroups == GPS) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) r[e] = top[e];
+    } else {
+        const bool b0 = ngroups & 1, b1 = ngroups & 2, b2 = ngroups & 4;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float t = b0 ? st0[e] : 0.0f;
+            if (GPS > 2 && b1) {
+                const float l1 = lvl[e * kWave + lane];
+                t = b0 ? l1 + t : l1;
+            }
+            if (GPS > 4 && b2) {
+                const float l2 = lvl[(16 + e) * kWave + lane];
+                t = (b0 || b1) ? l2 + t : l2;
+            }
+            r[e] = t;
+        }
+    }
+    // slices meet in LDS (each wave overwrites only its own stage)
+    float *comb = reinterpret_cast<float *>(stage);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) comb[e * 64 + lane] = r[e];
+    __syncthreads();
+    const int KS = a.KS;
+    for (int idx = threadIdx.x; idx < 16 * 64; idx += KS * kWave) {
+        float v[kMmMaxSlices];
+#pragma unroll
+        for (int s = 0; s < kMmMaxSlices; ++s)
+            v[s] = s < KS ? reinterpret_cast<const float *>(smem + s * kWaveLds)[idx] : 0.0f;
+#pragma unroll
+        for (int w = 1; w < kMmMaxSlices; w <<= 1)
+#pragma unroll
+            for (int s = 0; s + w < kMmMaxSlices; s += 2 * w)
+                if (s + w < KS) v[s] = v[s] + v[s + w];
+        const int e = idx >> 6, l = idx & 63;
+        const int token = l & 31;
+        const int row = row0 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+        if (token < a.M && row < N) y[((size_t)token * a.G + g) * N + row] = v[0];
+    }
+}
+
+template <int NB, int GPS>
+static int launch_mm_gps(const MmArgs &a, int nt1, hipStream_t stream) {
+    static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_mm_q8_0_kernel<NB, GPS>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kMmMaxSlices * mm_wave_lds(GPS)) != hipSuccess)
+            return QG_ERR_LAUNCH;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((qgemv_mm_q8_0_kernel<NB, GPS>), dim3(a.nt0 + nt1, a.G), dim3(a.KS * kWave),
+                       (size_t)a.KS * mm_wave_lds(GPS), stream, a);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+// Slices per workgroup: at most eight groups per slice, at most eight slices,
+// and more slices while the grid has fewer than about two waves per SIMD.
+template <int NB>
+static int launch_mm(MmArgs &a, hipStream_t stream) {
+    a.row_bytes = a.K / 32 * 34;
+    a.groups = a.K / 256;
+    int gpow2 = 1;
+    while (gpow2 < a.groups) gpow2 <<= 1;
+    const int nt1 = a.W1 ? (a.N1 + kMmRows - 1) / kMmRows : 0;
+    a.nt0 = (a.N0 + kMmRows - 1) / kMmRows;
+    const long tiles = (long)(a.nt0 + nt1) * a.G;
+    int ks = gpow2 > kMmMaxGroups ? gpow2 / kMmMaxGroups : 1;
+    const int ks_max = gpow2 < kMmMaxSlices ? gpow2 : kMmMaxSlices;
+    while (ks < ks_max && tiles * ks < kMmTargetWaves) ks <<= 1;
+    a.KS = ks;
+    a.gps = gpow2 / ks;
+    switch (a.gps) {
+        case 1: return launch_mm_gps<NB, 1>(a, nt1, stream);
+        case 2: return launch_mm_gps<NB, 2>(a, nt1, stream);
+        case 4: return launch_mm_gps<NB, 4>(a, nt1, stream);
+        case 8: return launch_mm_gps<NB, 8>(a, nt1, stream);
+        default: return QG_ERR_SHAPE;
+    }
+}
+
+int gemv_mm_q8_0(const uint8_t *W0, int N0, float *y0, const uint8_t *W1, int N1, float *y1, int K, const int8_t *qx,
+                 const float *dx, int M, int G, hipStream_t stream) {
+    MmArgs a{};
+    a.W0 = W0;
+    a.N0 = N0;
+    a.y0 = y0;
+    a.W1 = W1;
+    a.N1 = N1;
+    a.y1 = y1;
+    a.K = K;
+    a.qx = qx;
+    a.dx = dx;
+    a.M = M;
+    a.G = G;
+    // the unit of the one-token engine: 4 blocks up to K = 8192, else 8
+    if (K <= 8192) return launch_mm<4>(a, stream);
+    return launch_mm<8>(a, stream);
+}
+
+}  // namespace qg

@@ -172,10 +172,10 @@ def test_paired_equals_two_singles_and_oracle(qg, orc):
     K, N1, N2 = w["K"], w["N1"], w["N2"]
     for fmt in (0, 1):
         W1, W2 = _weights(fmt, g, N1, K), _weights(fmt, g, N2, K)
-        x = synth.activations(g, 2, K)
+        x = synth.activations(g, 8, K)
         qx, dx, sx = gpu_quantize(qg, x)
         import torch
-        for M in (1, 2):
+        for M in (1, 2, 8):
             y1, y2 = sentinel((M, N1), torch.float32), sentinel((M, N2), torch.float32)
             qg.qgemv_paired(fmt, dev(W1), N1, dev(W2), N2, K, qx[:M], dx[:M], sx[:M], M, y1, y2)
             s1 = _run_gemv(qg, fmt, dev(W1), N1, K, qx[:M], dx[:M], sx[:M], M)
@@ -185,6 +185,45 @@ def test_paired_equals_two_singles_and_oracle(qg, orc):
             r2, b2 = orc.gemv(fmt, W2, N2, K, host(qx[:M]), host(dx[:M]))
             assert_within_bound(host(y1), r1, b1, what="paired y1")
             assert_within_bound(host(y2), r2, b2, what="paired y2")
+
+
+# ---------------------------------------------------------------- Q8_0 batches on the matrix cores
+
+MM_CASES = [
+    # N, K, M: one group per row; empty K slices; partial slices of two, four
+    # and eight groups (K = 1280, 2304: groups per row not a power of two, with
+    # enough rows that a workgroup takes few slices); the 8-block unit (K > 8192)
+    # with a partial slice; the largest K; ragged row tiles; 4..32 tokens
+    (37, 256, 4),
+    (100, 1280, 5),
+    (16384, 1280, 8),
+    (32768, 1280, 6),
+    (32768, 2304, 5),
+    (333, 2048, 9),
+    (70, 7168, 17),
+    (9, 8448, 7),
+    (9, 12288, 32),
+    (64, 16384, 16),
+    (4096, 4096, 32),
+]
+
+
+@pytest.mark.parametrize("N,K,M", MM_CASES)
+def test_q8_0_batch_rows_equal_single_token_calls(qg, orc, N, K, M):
+    """A batch of M Q8_0 tokens: every row equals the one-token call on that token, bit for
+    bit, and sampled rows match the oracle."""
+    progress("q8_0 batch N=%d K=%d M=%d" % (N, K, M))
+    g = np.random.default_rng(4000 + N + K + M)
+    W = synth.q8_0_weight(g, N, K)
+    Wd = dev(W)
+    qx, dx, sx = gpu_quantize(qg, synth.activations(g, M, K))
+    y = _run_gemv(qg, 0, Wd, N, K, qx, dx, sx, M)
+    for t in range(M):
+        single = _run_gemv(qg, 0, Wd, N, K, qx[t:t + 1], dx[t:t + 1], sx[t:t + 1], 1)
+        assert np.array_equal(y[t].view(np.uint32), single[0].view(np.uint32)), "token %d" % t
+    rows = np.arange(N) if N <= 512 else np.sort(g.choice(N, 256, replace=False))
+    ref, bound = orc.gemv(0, W[rows], len(rows), K, host(qx), host(dx), nthreads=oracle_threads())
+    assert_within_bound(y[:, rows], ref, bound, what="q8_0 batch N=%d K=%d M=%d" % (N, K, M))
 
 
 @pytest.mark.parametrize("fmt,N,K,M", [(0, 45, 1024, 2), (0, 8, 12288, 1), (1, 33, 2048, 3), (1, 5, 256, 1)])
@@ -317,7 +356,7 @@ def test_fused_errors(qg):
 # ---------------------------------------------------------------- grouped (attention output, low rank)
 
 @pytest.mark.parametrize("fmt,G,N,K,M", [(0, 8, 1024, 4096, 1), (0, 3, 130, 512, 3), (1, 2, 70, 1024, 2),
-                                         (0, 1, 96, 256, 5), (1, 5, 33, 256, 1)])
+                                         (0, 1, 96, 256, 5), (1, 5, 33, 256, 1), (0, 8, 1024, 4096, 12)])
 def test_grouped_parity(qg, orc, fmt, G, N, K, M):
     """Group g against the oracle on matrix g and input slice g; ragged N, G = 1, several tokens."""
     import torch
@@ -340,9 +379,13 @@ def test_grouped_parity(qg, orc, fmt, G, N, K, M):
 
 def test_grouped_equals_single_calls(qg):
     """Each group equals the single-matrix call on its slice, bit for bit."""
-    import torch
     g_ = np.random.default_rng(31)
-    G, N, K, M = 4, 200, 1024, 2
+    for G, N, K, M in ((4, 200, 1024, 2), (3, 100, 2048, 9)):
+        _grouped_equals_singles(qg, g_, G, N, K, M)
+
+
+def _grouped_equals_singles(qg, g_, G, N, K, M):
+    import torch
     Ws = [synth.q8_0_weight(g_, N, K) for _ in range(G)]
     x = dev(synth.activations(g_, M, G * K))
     qx = torch.empty(M, G * K, dtype=torch.int8, device=x.device)
