@@ -23,6 +23,8 @@ import numpy as np
 
 FMT_Q8_0 = 0
 FMT_Q4K = 1
+FMT_FP8_B128 = 2  # FP8 E4M3 codes, UE8M0 scale per 128 x 128 block
+FMT_FP4_MX = 3    # FP4 E2M1 codes (two per byte, low nibble first), UE8M0 scale per 1 x 32
 BAD_EXPERT = 1  # status code for an expert id outside [0, E)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,8 +57,16 @@ def _load():
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_double.restype = dbl
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_e4m3_to_double.restype = dbl
+    lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_to_double.restype = dbl
+    lib.oracle_e2m1_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_ue8m0_to_double.restype = dbl
+    lib.oracle_ue8m0_to_double.argtypes = [ctypes.c_uint8]
     lib.oracle_row_bytes.restype = i64
     lib.oracle_row_bytes.argtypes = [ctypes.c_int, i64]
+    lib.oracle_matrix_bytes.restype = i64
+    lib.oracle_matrix_bytes.argtypes = [ctypes.c_int, i64, i64]
     lib.oracle_dequant.restype = ctypes.c_int
     lib.oracle_dequant.argtypes = [ctypes.c_int, vp, i64, i64, vp]
     lib.oracle_quantize_act_q8.restype = None
@@ -74,6 +84,9 @@ def _load():
     lib.oracle_moe_routed.restype = ctypes.c_int
     lib.oracle_moe_routed.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_int]
+    lib.oracle_moe_routed_fmt.restype = ctypes.c_int
+    lib.oracle_moe_routed_fmt.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, ctypes.c_int]
     lib.oracle_prefill.restype = ctypes.c_int
     lib.oracle_prefill.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, vp, vp, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -108,14 +121,32 @@ def bf16_to_double(bits: int) -> float:
     return _load().oracle_bf16_to_double(int(bits) & 0xFFFF)
 
 
+def e4m3_to_double(code: int) -> float:
+    return _load().oracle_e4m3_to_double(int(code) & 0xFF)
+
+
+def e2m1_to_double(code: int) -> float:
+    return _load().oracle_e2m1_to_double(int(code) & 0x0F)
+
+
+def ue8m0_to_double(code: int) -> float:
+    return _load().oracle_ue8m0_to_double(int(code) & 0xFF)
+
+
 def row_bytes(fmt: int, K: int) -> int:
+    """Bytes of one row (for FP8 / FP4: of its codes only)."""
     return int(_load().oracle_row_bytes(fmt, K))
+
+
+def matrix_bytes(fmt: int, N: int, K: int) -> int:
+    """Bytes of a whole N x K matrix, scales included."""
+    return int(_load().oracle_matrix_bytes(fmt, N, K))
 
 
 def dequant(fmt: int, W: np.ndarray, N: int, K: int) -> np.ndarray:
     """Dequantized [N, K] float64 matrix."""
     W = _c(W, np.uint8)
-    assert W.size == N * row_bytes(fmt, K)
+    assert W.size == matrix_bytes(fmt, N, K)
     out = np.empty((N, K), np.float64)
     _check(_load().oracle_dequant(fmt, _ptr(W), N, K, _ptr(out)), "dequant")
     return out
@@ -141,7 +172,7 @@ def gemv(fmt: int, W: np.ndarray, N: int, K: int, qx: np.ndarray, dx: np.ndarray
     qx = _c(qx, np.int8).reshape(-1, K)
     M = qx.shape[0]
     dx = _c(dx, np.float32).reshape(M, K // 32)
-    assert W.size == N * row_bytes(fmt, K)
+    assert W.size == matrix_bytes(fmt, N, K)
     y = np.empty((M, N), np.float64)
     bound = np.empty((M, N), np.float64)
     _check(_load().oracle_gemv(fmt, _ptr(W), N, K, _ptr(qx), _ptr(dx), M, _ptr(y), _ptr(bound), nthreads),
@@ -154,7 +185,7 @@ def gemv_fx(fmt: int, W: np.ndarray, N: int, K: int, x: np.ndarray, nthreads: in
     W = _c(W, np.uint8)
     x = _c(x, np.float32).reshape(-1, K)
     M = x.shape[0]
-    assert W.size == N * row_bytes(fmt, K)
+    assert W.size == matrix_bytes(fmt, N, K)
     y = np.empty((M, N), np.float64)
     bound = np.empty((M, N), np.float64)
     _check(_load().oracle_gemv_fx(fmt, _ptr(W), N, K, _ptr(x), M, _ptr(y), _ptr(bound), nthreads), "gemv_fx")
@@ -195,8 +226,8 @@ def silu(z: float) -> float:
     return _load().oracle_silu(float(z))
 
 
-def moe_routed(qx, dx, ids, rw, gate, up, down, D: int, F: int, nthreads: int = 1):
-    """End-to-end routed MoE from scratch.  gate/up/down: lists of E uint8 arrays.
+def moe_routed(qx, dx, ids, rw, gate, up, down, D: int, F: int, nthreads: int = 1, fmt: int = FMT_Q4K):
+    """End-to-end routed MoE from scratch.  gate/up/down: lists of E uint8 arrays in format fmt.
 
     Returns (y, bound, status) with y, bound float64 [T, D].
     """
@@ -215,7 +246,7 @@ def moe_routed(qx, dx, ids, rw, gate, up, down, D: int, F: int, nthreads: int = 
     y = np.empty((T, D), np.float64)
     bound = np.empty((T, D), np.float64)
     status = np.zeros(1, np.int32)
-    _check(_load().oracle_moe_routed(_ptr(qx), _ptr(dx), T, D, F, E, topk, _ptr(ids), _ptr(rw),
+    _check(_load().oracle_moe_routed_fmt(fmt, _ptr(qx), _ptr(dx), T, D, F, E, topk, _ptr(ids), _ptr(rw),
                                      ctypes.cast(ptr_arrays[0], ctypes.c_void_p),
                                      ctypes.cast(ptr_arrays[1], ctypes.c_void_p),
                                      ctypes.cast(ptr_arrays[2], ctypes.c_void_p),

@@ -59,6 +59,22 @@
  *     weight (j, i) = d * sc[j] * q - dmin * m[j]
  *   A row of K weights is K/256 consecutive superblocks.
  *
+ *   FP8 E4M3 with 128 x 128 block scales, and FP4 E2M1 with 1 x 32
+ *   microscaling, both with UE8M0 scales (the routed-expert formats of
+ *   ROCm/ATOM "DeepSeek-V4 Usage Guide", section "FP8 on MI308 / gfx942":
+ *   its quantization-config table and the V4-Pro MoE backend note).  One
+ *   matrix of N rows and K columns is one buffer: the codes, then, from the
+ *   first multiple of 256 bytes after them, the scale bytes.
+ *     FP8: codes uint8 [N][K]; scales [ceil(N/128)][K/128];
+ *          weight (n, k) = e4m3(code) * 2^(S[n/128][k/128] - 127).
+ *     FP4: codes uint8 [N][K/2], element 2i in the low nibble of byte i and
+ *          element 2i+1 in the high nibble; scales [N][K/32];
+ *          weight (n, k) = e2m1(nibble) * 2^(S[n][k/32] - 127).
+ *   E4M3 (OCP 8-bit float, no infinities): sign, 4 exponent bits (bias 7),
+ *   3 mantissa bits; exponent 0 is subnormal; S.1111.111 is NaN.  E2M1 (OCP
+ *   4-bit float): sign, 2 exponent bits (bias 1), 1 mantissa bit.  UE8M0:
+ *   an unsigned 8-bit exponent, 2^(s - 127), 255 being NaN.
+ *
  *   Q8 activation (per row of K fp32 values, per block b of 32):
  *     qx int8[K], dx fp32[K/32] (the block scale), sx int32[K/32] (sum of
  *     the block's quants).
@@ -74,6 +90,8 @@
 
 #define ORACLE_FMT_Q8_0 0
 #define ORACLE_FMT_Q4K 1
+#define ORACLE_FMT_FP8_B128 2
+#define ORACLE_FMT_FP4_MX 3
 
 #define ORACLE_OK 0
 #define ORACLE_ERR_ARG -1
@@ -110,6 +128,27 @@ double oracle_bf16_to_double(uint16_t b) {
     return (double)f;
 }
 
+/* OCP FP8 E4M3: sign, exponent e (4 bits, bias 7), mantissa m (3 bits).
+ * e == 0: (m / 8) * 2^-6;  otherwise (1 + m / 8) * 2^(e - 7);  e == 15 with
+ * m == 7 is NaN (the format has no infinities). */
+double oracle_e4m3_to_double(uint8_t c) {
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return sign ? -v : v;
+}
+
+/* OCP FP4 E2M1 (the low 4 bits of c): sign, exponent e (2 bits, bias 1),
+ * mantissa m (1 bit).  e == 0: m / 2;  otherwise (1 + m / 2) * 2^(e - 1). */
+double oracle_e2m1_to_double(uint8_t c) {
+    int sign = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = (e == 0) ? 0.5 * (double)m : ldexp((double)(2 + m), e - 2);
+    return sign ? -v : v;
+}
+
+/* UE8M0 scale: 2^(s - 127); s == 255 is NaN. */
+double oracle_ue8m0_to_double(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
 static uint16_t load_u16_le(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
 /* field f (0..15) of the 96-bit little-endian string held in bytes[0..11] */
@@ -126,7 +165,24 @@ static int q4k_field(const uint8_t *bytes, int f) {
 int64_t oracle_row_bytes(int fmt, int64_t K) {
     if (fmt == ORACLE_FMT_Q8_0) return (K / 32) * 34;
     if (fmt == ORACLE_FMT_Q4K) return (K / 256) * 144;
+    if (fmt == ORACLE_FMT_FP8_B128) return K; /* codes only */
+    if (fmt == ORACLE_FMT_FP4_MX) return K / 2;
     return -1;
+}
+
+static int is_scaled_fmt(int fmt) { return fmt == ORACLE_FMT_FP8_B128 || fmt == ORACLE_FMT_FP4_MX; }
+
+/* Byte offset of the scales of an FP8 / FP4 matrix: the codes rounded up to 256. */
+static int64_t scale_offset(int fmt, int64_t N, int64_t K) {
+    int64_t codes = N * oracle_row_bytes(fmt, K);
+    return (codes + 255) / 256 * 256;
+}
+
+/* Bytes of a whole N x K matrix in format fmt (codes and, for FP8 / FP4, scales). */
+int64_t oracle_matrix_bytes(int fmt, int64_t N, int64_t K) {
+    if (fmt == ORACLE_FMT_FP8_B128) return scale_offset(fmt, N, K) + (N + 127) / 128 * (K / 128);
+    if (fmt == ORACLE_FMT_FP4_MX) return scale_offset(fmt, N, K) + N * (K / 32);
+    return N * oracle_row_bytes(fmt, K);
 }
 
 /* Dequantize the 32 weights of block b (0 .. K/32-1) of one row into w[32]. */
@@ -151,6 +207,25 @@ static void dequant_block(int fmt, const uint8_t *row, int64_t b, double *w) {
     }
 }
 
+/* Block b (32 weights) of row n of matrix W (N x K), any format, into w[32]. */
+static void dequant_row_block(int fmt, const uint8_t *W, int64_t N, int64_t K, int64_t n, int64_t b, double *w) {
+    if (fmt == ORACLE_FMT_FP8_B128) {
+        const uint8_t *codes = W + n * K + 32 * b;
+        double scale = oracle_ue8m0_to_double(W[scale_offset(fmt, N, K) + (n / 128) * (K / 128) + (32 * b) / 128]);
+        for (int i = 0; i < 32; ++i) w[i] = oracle_e4m3_to_double(codes[i]) * scale;
+    } else if (fmt == ORACLE_FMT_FP4_MX) {
+        const uint8_t *codes = W + n * (K / 2) + 16 * b;
+        double scale = oracle_ue8m0_to_double(W[scale_offset(fmt, N, K) + n * (K / 32) + b]);
+        for (int i = 0; i < 32; ++i) {
+            uint8_t byte = codes[i / 2];
+            uint8_t nib = (i % 2 == 0) ? (byte & 0x0f) : (byte >> 4);
+            w[i] = oracle_e2m1_to_double(nib) * scale;
+        }
+    } else {
+        dequant_block(fmt, W + n * oracle_row_bytes(fmt, K), b, w);
+    }
+}
+
 /* Raw integer quant of block b, element i (int8 for Q8_0, nibble 0..15 for Q4_K). */
 static int raw_quant(int fmt, const uint8_t *row, int64_t b, int i) {
     if (fmt == ORACLE_FMT_Q8_0) return (int8_t)row[34 * b + 2 + i];
@@ -163,15 +238,16 @@ static int raw_quant(int fmt, const uint8_t *row, int64_t b, int i) {
 static int fmt_ok(int fmt, int64_t K) {
     if (fmt == ORACLE_FMT_Q8_0) return K > 0 && K % 32 == 0;
     if (fmt == ORACLE_FMT_Q4K) return K > 0 && K % 256 == 0;
+    if (fmt == ORACLE_FMT_FP8_B128) return K > 0 && K % 128 == 0;
+    if (fmt == ORACLE_FMT_FP4_MX) return K > 0 && K % 32 == 0;
     return 0;
 }
 
 /* Full dequantized matrix, out[N*K] row-major. */
 int oracle_dequant(int fmt, const uint8_t *W, int64_t N, int64_t K, double *out) {
     if (!fmt_ok(fmt, K) || N < 0) return ORACLE_ERR_ARG;
-    int64_t rb = oracle_row_bytes(fmt, K);
     for (int64_t n = 0; n < N; ++n)
-        for (int64_t b = 0; b < K / 32; ++b) dequant_block(fmt, W + n * rb, b, out + n * K + 32 * b);
+        for (int64_t b = 0; b < K / 32; ++b) dequant_row_block(fmt, W, N, K, n, b, out + n * K + 32 * b);
     return ORACLE_OK;
 }
 
@@ -226,7 +302,6 @@ void oracle_quantize_act_q8(const float *x, int64_t M, int64_t K, int8_t *qx, fl
 int oracle_gemv(int fmt, const uint8_t *W, int64_t N, int64_t K, const int8_t *qx, const float *dx, int64_t M,
                 double *y, double *bound, int nthreads) {
     if (!fmt_ok(fmt, K) || N < 0 || M < 0) return ORACLE_ERR_ARG;
-    int64_t rb = oracle_row_bytes(fmt, K);
     int64_t nb = K / 32;
     int err = 0;
     if (nthreads < 1) nthreads = 1;
@@ -240,11 +315,10 @@ int oracle_gemv(int fmt, const uint8_t *W, int64_t N, int64_t K, const int8_t *q
             double *bnd = acc + (M > 0 ? M : 1);
 #pragma omp for schedule(static)
             for (int64_t n = 0; n < N; ++n) {
-                const uint8_t *row = W + n * rb;
                 double w[32];
                 for (int64_t m = 0; m < M; ++m) acc[m] = bnd[m] = 0.0;
                 for (int64_t b = 0; b < nb; ++b) {
-                    dequant_block(fmt, row, b, w);
+                    dequant_row_block(fmt, W, N, K, n, b, w);
                     for (int64_t m = 0; m < M; ++m) {
                         double scale = (double)dx[m * nb + b];
                         const int8_t *q = qx + m * K + 32 * b;
@@ -276,17 +350,15 @@ int oracle_gemv(int fmt, const uint8_t *W, int64_t N, int64_t K, const int8_t *q
 int oracle_gemv_fx(int fmt, const uint8_t *W, int64_t N, int64_t K, const float *x, int64_t M, double *y,
                    double *bound, int nthreads) {
     if (!fmt_ok(fmt, K) || N < 0 || M < 0) return ORACLE_ERR_ARG;
-    int64_t rb = oracle_row_bytes(fmt, K);
     int64_t nb = K / 32;
     if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for schedule(static) num_threads(nthreads)
     for (int64_t n = 0; n < N; ++n) {
-        const uint8_t *row = W + n * rb;
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0, bnd = 0.0;
             double w[32];
             for (int64_t b = 0; b < nb; ++b) {
-                dequant_block(fmt, row, b, w);
+                dequant_row_block(fmt, W, N, K, n, b, w);
                 for (int i = 0; i < 32; ++i) {
                     double t = w[i] * (double)x[m * K + 32 * b + i];
                     acc += t;
@@ -307,7 +379,7 @@ int oracle_gemv_fx(int fmt, const uint8_t *W, int64_t N, int64_t K, const float 
  * sub-block b).  Exact in int32: |isum| <= 32*127*127 (Q8_0), 32*15*127 (Q4_K).
  */
 int oracle_block_isums(int fmt, const uint8_t *W, int64_t N, int64_t K, const int8_t *qx, int64_t M, int32_t *isum) {
-    if (!fmt_ok(fmt, K) || N < 0 || M < 0) return ORACLE_ERR_ARG;
+    if (!fmt_ok(fmt, K) || is_scaled_fmt(fmt) || N < 0 || M < 0) return ORACLE_ERR_ARG;
     int64_t rb = oracle_row_bytes(fmt, K);
     int64_t nb = K / 32;
     for (int64_t m = 0; m < M; ++m)
@@ -391,13 +463,17 @@ double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
  *                                                   other projection)
  *     o = down_e . h_q                             (fp64)
  *     y_t += rw[t, k] * o,  bound_t += |rw[t, k]| * bound(o)
- * Gate/up are F x D, down is D x F, all Q4_K.  Pairs with an invalid id add
- * nothing and set *status.  y, bound are [T, D].
+ * Gate/up are F x D, down is D x F, all in format fmt (Q4_K for the
+ * distributed model; FP8 E4M3 128 x 128 or FP4 E2M1 1 x 32 for the ATOM
+ * expert formats).  Pairs with an invalid id add nothing and set *status.
+ * y, bound are [T, D].
  */
-int oracle_moe_routed(const int8_t *qx, const float *dx, int64_t T, int64_t D, int64_t F, int64_t E, int64_t topk,
-                      const int32_t *ids, const float *rw, const uint8_t *const *gate, const uint8_t *const *up,
-                      const uint8_t *const *down, double *y, double *bound, int32_t *status, int nthreads) {
+int oracle_moe_routed_fmt(int fmt, const int8_t *qx, const float *dx, int64_t T, int64_t D, int64_t F, int64_t E,
+                          int64_t topk, const int32_t *ids, const float *rw, const uint8_t *const *gate,
+                          const uint8_t *const *up, const uint8_t *const *down, double *y, double *bound,
+                          int32_t *status, int nthreads) {
     if (T < 0 || D % 256 || F % 256 || D <= 0 || F <= 0 || E < 1 || topk < 1) return ORACLE_ERR_ARG;
+    if (fmt != ORACLE_FMT_Q4K && !is_scaled_fmt(fmt)) return ORACLE_ERR_ARG;
     double *g = (double *)malloc(sizeof(double) * (size_t)F);
     double *v = (double *)malloc(sizeof(double) * (size_t)F);
     float *hf = (float *)malloc(sizeof(float) * (size_t)F);
@@ -420,11 +496,11 @@ int oracle_moe_routed(const int8_t *qx, const float *dx, int64_t T, int64_t D, i
                 *status = ORACLE_BAD_EXPERT;
                 continue;
             }
-            oracle_gemv(ORACLE_FMT_Q4K, gate[e], F, D, qx + t * D, dx + t * (D / 32), 1, g, NULL, nthreads);
-            oracle_gemv(ORACLE_FMT_Q4K, up[e], F, D, qx + t * D, dx + t * (D / 32), 1, v, NULL, nthreads);
+            oracle_gemv(fmt, gate[e], F, D, qx + t * D, dx + t * (D / 32), 1, g, NULL, nthreads);
+            oracle_gemv(fmt, up[e], F, D, qx + t * D, dx + t * (D / 32), 1, v, NULL, nthreads);
             for (int64_t f = 0; f < F; ++f) hf[f] = (float)(oracle_silu(g[f]) * v[f]);
             oracle_quantize_act_q8(hf, 1, F, hq, hd, hs);
-            oracle_gemv(ORACLE_FMT_Q4K, down[e], D, F, hq, hd, 1, o, ob, nthreads);
+            oracle_gemv(fmt, down[e], D, F, hq, hd, 1, o, ob, nthreads);
             double r = (double)rw[t * topk + k];
             for (int64_t n = 0; n < D; ++n) {
                 y[t * D + n] += r * o[n];
@@ -444,6 +520,14 @@ done:
     return rc;
 }
 
+/* The distributed model's routed MoE: every expert matrix Q4_K. */
+int oracle_moe_routed(const int8_t *qx, const float *dx, int64_t T, int64_t D, int64_t F, int64_t E, int64_t topk,
+                      const int32_t *ids, const float *rw, const uint8_t *const *gate, const uint8_t *const *up,
+                      const uint8_t *const *down, double *y, double *bound, int32_t *status, int nthreads) {
+    return oracle_moe_routed_fmt(ORACLE_FMT_Q4K, qx, dx, T, D, F, E, topk, ids, rw, gate, up, down, y, bound, status,
+                                 nthreads);
+}
+
 /* ------------------------------------------------------------------ */
 /* prefill                                                              */
 /* ------------------------------------------------------------------ */
@@ -454,7 +538,7 @@ done:
  */
 int oracle_prefill(int fmt, const uint8_t *W, int64_t N, int64_t K, const uint16_t *xbf16, int64_t M, double *Y,
                    double *bound, int nthreads) {
-    if (!fmt_ok(fmt, K) || N < 0 || M < 0) return ORACLE_ERR_ARG;
+    if (!fmt_ok(fmt, K) || is_scaled_fmt(fmt) || N < 0 || M < 0) return ORACLE_ERR_ARG;
     int64_t rb = oracle_row_bytes(fmt, K);
     int64_t nb = K / 32;
     if (nthreads < 1) nthreads = 1;

@@ -76,6 +76,73 @@ def q4k_weight(g: np.random.Generator, N: int, K: int, lo: float = 1e-4, hi: flo
     return sb.reshape(N, ns * Q4K_BLOCK_BYTES)
 
 
+# FP8 E4M3 (128 x 128 block scales) and FP4 E2M1 (1 x 32 scales) expert
+# matrices, UE8M0 scales.  One buffer per matrix: the codes, then the scale
+# bytes from the next multiple of 256 bytes.
+FMT_FP8_B128 = 2
+FMT_FP4_MX = 3
+E4M3_NAN_CODES = (0x7F, 0xFF)
+
+
+def _align256(x: int) -> int:
+    return (x + 255) // 256 * 256
+
+
+def scaled_matrix_bytes(fmt: int, N: int, K: int) -> int:
+    """Bytes of an FP8 / FP4 matrix buffer: codes, padding to 256, scales."""
+    if fmt == FMT_FP8_B128:
+        return _align256(N * K) + (N + 127) // 128 * (K // 128)
+    if fmt == FMT_FP4_MX:
+        return _align256(N * K // 2) + N * (K // 32)
+    raise ValueError(fmt)
+
+
+def fp8_from_parts(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Place E4M3 codes uint8 [N, K] and UE8M0 scales uint8 [ceil(N/128), K/128] into one buffer."""
+    N, K = codes.shape
+    assert scales.shape == ((N + 127) // 128, K // 128)
+    buf = np.zeros(scaled_matrix_bytes(FMT_FP8_B128, N, K), np.uint8)
+    buf[:N * K] = codes.reshape(-1)
+    buf[_align256(N * K):] = scales.reshape(-1)
+    return buf
+
+
+def fp4_from_parts(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Place packed E2M1 codes uint8 [N, K/2] (element 2i in the low nibble of byte i) and
+    UE8M0 scales uint8 [N, K/32] into one buffer."""
+    N, half = codes.shape
+    K = 2 * half
+    assert scales.shape == (N, K // 32)
+    buf = np.zeros(scaled_matrix_bytes(FMT_FP4_MX, N, K), np.uint8)
+    buf[:N * half] = codes.reshape(-1)
+    buf[_align256(N * half):] = scales.reshape(-1)
+    return buf
+
+
+def fp8_weight(g: np.random.Generator, N: int, K: int, s_lo: int = 118, s_hi: int = 122) -> np.ndarray:
+    """FP8 E4M3 matrix buffer: codes uniform over the 254 non-NaN codes, scales uniform
+    integers in [s_lo, s_hi] (2^-9 .. 2^-5 for the defaults)."""
+    assert K % 128 == 0
+    valid = np.setdiff1d(np.arange(256), E4M3_NAN_CODES).astype(np.uint8)
+    codes = valid[g.integers(0, valid.size, size=(N, K))]
+    scales = g.integers(s_lo, s_hi + 1, size=((N + 127) // 128, K // 128)).astype(np.uint8)
+    return fp8_from_parts(codes, scales)
+
+
+def fp4_weight(g: np.random.Generator, N: int, K: int, s_lo: int = 120, s_hi: int = 124) -> np.ndarray:
+    """FP4 E2M1 matrix buffer: uniform random nibbles (all 16 codes are values), scales
+    uniform integers in [s_lo, s_hi]."""
+    assert K % 32 == 0
+    codes = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = g.integers(s_lo, s_hi + 1, size=(N, K // 32)).astype(np.uint8)
+    return fp4_from_parts(codes, scales)
+
+
+def weight(fmt: int, g: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """A synthetic matrix of any format (0 Q8_0, 1 Q4_K, 2 FP8 E4M3 B128, 3 FP4 E2M1 MX)."""
+    return [q8_0_weight, q4k_weight, fp8_weight, fp4_weight][fmt](g, N, K)
+
+
 def activations(g: np.random.Generator, M: int, K: int) -> np.ndarray:
     """fp32 [M, K] drawn N(0, 1)."""
     return g.standard_normal((M, K), dtype=np.float64).astype(np.float32)
@@ -111,13 +178,13 @@ def routing_weights(g: np.random.Generator, T: int, topk: int) -> np.ndarray:
     return (s / s.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
-def moe_experts(g: np.random.Generator, E: int, D: int, F: int):
-    """Lists (gate, up, down) of E Q4_K matrices: gate/up [F, D], down [D, F]."""
+def moe_experts(g: np.random.Generator, E: int, D: int, F: int, fmt: int = 1):
+    """Lists (gate, up, down) of E matrices in format fmt (Q4_K by default): gate/up [F, D], down [D, F]."""
     gate, up, down = [], [], []
     for _ in range(E):
-        gate.append(q4k_weight(g, F, D))
-        up.append(q4k_weight(g, F, D))
-        down.append(q4k_weight(g, D, F))
+        gate.append(weight(fmt, g, F, D))
+        up.append(weight(fmt, g, F, D))
+        down.append(weight(fmt, g, D, F))
     return gate, up, down
 
 
@@ -144,4 +211,8 @@ WORKLOADS = {
     "q8_0_16384x4096": dict(fmt="q8_0", N=16384, K=4096, Ms=(1, 2, 4, 8, 16, 32), seed=4),
     # routed MoE with reuse: 384 experts, top-6, 64 tokens, Zipf(1.1)
     "moe_e384_t64_zipf": dict(E=384, D=4096, F=2048, topk=6, T=64, ids="zipf", seed=4),
+    # the ATOM expert formats on the routed path, one token: FP8 E4M3 with
+    # 128 x 128 block scales over 256 experts, FP4 E2M1 with 1 x 32 scales over 384
+    "moe_fp8_e256_t1": dict(E=256, D=4096, F=2048, topk=6, T=1, ids="uniform", fmt=FMT_FP8_B128, seed=6),
+    "moe_fp4_e384_t1": dict(E=384, D=4096, F=2048, topk=6, T=1, ids="uniform", fmt=FMT_FP4_MX, seed=7),
 }

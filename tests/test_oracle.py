@@ -518,3 +518,169 @@ def test_golden_expert_id_range(orc):
         assert orc.moe_table(np.array([[bad, 0]], np.int32), E)["status"] == orc.BAD_EXPERT
     for ok in fact["valid_ids"]:
         assert orc.moe_table(np.array([[ok, 0]], np.int32), E)["status"] == 0
+
+
+# ---------------------------------------------------------------- FP8 E4M3 / FP4 E2M1 expert formats
+
+def _ocp():
+    with open(os.path.join(GOLDEN, "ocp_fp8_fp4_values.json")) as f:
+        return json.load(f)
+
+
+def test_e4m3_all_codes_match_torch(orc):
+    """Every E4M3 code decodes to what torch's float8_e4m3fn conversion gives (signed zeros too)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([orc.e4m3_to_double(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3_and_ue8m0_landmarks_golden(orc):
+    o = _ocp()
+    for k, v in o["e4m3_landmarks"].items():
+        assert orc.e4m3_to_double(int(k, 16)) == v, k
+    for k in o["e4m3_nan_codes"]:
+        assert math.isnan(orc.e4m3_to_double(int(k, 16)))
+    for k, v in o["ue8m0_landmarks"].items():
+        assert orc.ue8m0_to_double(int(k, 16)) == v, k
+    for k in o["ue8m0_nan_codes"]:
+        assert math.isnan(orc.ue8m0_to_double(int(k, 16)))
+
+
+def test_e2m1_table_golden(orc):
+    """The sixteen E2M1 codes decode to the MX specification's element values."""
+    ref = _ocp()["e2m1_values_by_code"]
+    for c in range(16):
+        got = orc.e2m1_to_double(c)
+        assert got == ref[c] and math.copysign(1.0, got) == math.copysign(1.0, ref[c]), c
+    # only the low nibble is read
+    assert orc.e2m1_to_double(0xF7) == 6.0
+
+
+def test_ue8m0_all_codes_match_torch(orc):
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([orc.ue8m0_to_double(int(c)) for c in codes])
+    assert np.array_equal(got, ref, equal_nan=True)
+
+
+def _torch_decode_fp8(W, N, K):
+    """Test-side decode of an FP8 E4M3 / 128 x 128 buffer through torch's float8 dtypes."""
+    import torch
+    codes = W[:N * K].reshape(N, K)
+    off = (N * K + 255) // 256 * 256
+    sc = W[off:off + (N + 127) // 128 * (K // 128)].reshape((N + 127) // 128, K // 128)
+    v = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    s = torch.from_numpy(sc.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    return v * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)[:N]
+
+
+def _table_decode_fp4(W, N, K):
+    """Test-side decode of an FP4 E2M1 / 1 x 32 buffer through the MX value table."""
+    import torch
+    lut = np.array(_ocp()["e2m1_values_by_code"])
+    codes = W[:N * K // 2].reshape(N, K // 2)
+    off = (N * K // 2 + 255) // 256 * 256
+    sc = W[off:off + N * (K // 32)].reshape(N, K // 32)
+    nib = np.empty((N, K), np.uint8)
+    nib[:, 0::2] = codes & 0x0F
+    nib[:, 1::2] = codes >> 4
+    s = torch.from_numpy(sc.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    return lut[nib] * np.repeat(s, 32, axis=1)
+
+
+@pytest.mark.parametrize("fmt", [2, 3])
+def test_scaled_formats_general_vs_independent_decode(orc, fmt):
+    """Ragged rows (N not a multiple of 128), several scale blocks: the oracle's dequantized
+    matrix equals the test-side decode exactly, and its GEMV equals numpy's matmul."""
+    g = np.random.default_rng(60 + fmt)
+    N, K, M = 300, 512, 3
+    W = synth.weight(fmt, g, N, K)
+    assert W.size == orc.matrix_bytes(fmt, N, K)
+    ref = _torch_decode_fp8(W, N, K) if fmt == 2 else _table_decode_fp4(W, N, K)
+    assert np.array_equal(orc.dequant(fmt, W, N, K), ref)
+    qx, dx, _ = orc.quantize_act_q8(synth.activations(g, M, K))
+    a = dx.astype(np.float64).repeat(32, axis=1) * qx.astype(np.float64)
+    y, bound = orc.gemv(fmt, W, N, K, qx, dx)
+    assert np.all(np.abs(y - a @ ref.T) <= 1e-12 * (np.abs(a) @ np.abs(ref).T))
+    assert np.allclose(bound, np.abs(a) @ np.abs(ref).T, rtol=1e-13)
+
+
+def test_fp8_scale_blocks_are_row_by_column(orc):
+    """Every code 1.0 (0x38) and every scale 2^0 except block (row block 1, column block 2) at
+    2^3: exactly rows 128..255 x columns 256..383 read 8 (a transposed scale index fails)."""
+    N, K = 300, 512
+    codes = np.full((N, K), 0x38, np.uint8)
+    sc = np.full((3, 4), 127, np.uint8)
+    sc[1, 2] = 130
+    w = orc.dequant(2, synth.fp8_from_parts(codes, sc), N, K)
+    expect = np.ones((N, K))
+    expect[128:256, 256:384] = 8.0
+    assert np.array_equal(w, expect)
+
+
+def test_fp4_nibble_order_and_scale_per_32(orc):
+    """Byte 0x21 holds element 0 = code 1 (0.5) in its low nibble and element 1 = code 2 (1.0)
+    in its high nibble; scale byte (row 1, block 1) = 2^2 multiplies exactly that block."""
+    N, K = 2, 64
+    codes = np.zeros((N, K // 2), np.uint8)
+    codes[0, 0] = 0x21
+    codes[1, 16] = 0x9F   # row 1, elements 32 (code 15: -6) and 33 (code 9: -0.5)
+    sc = np.full((N, 2), 127, np.uint8)
+    sc[1, 1] = 129
+    w = orc.dequant(3, synth.fp4_from_parts(codes, sc), N, K)
+    expect = np.zeros((N, K))
+    expect[0, 0], expect[0, 1] = 0.5, 1.0
+    expect[1, 32], expect[1, 33] = -24.0, -2.0
+    assert np.array_equal(w, expect)
+
+
+def test_scaled_formats_integer_case_is_exact(orc):
+    """Codes whose values are integers (FP8: 1, 2, 4; FP4: 1, 2, 4, 6), scale 2^0, integer
+    activation with dx = 1: the GEMV is an int64 matmul."""
+    g = np.random.default_rng(64)
+    N, K, M = 130, 256, 2
+    x = fh.integer_activation(g, M, K)
+    qx, dx, _ = orc.quantize_act_q8(x)
+    assert np.all(dx == 1.0)
+    xi = x.astype(np.int64)
+    # FP8: 0x38 = 1, 0x40 = 2, 0x48 = 4, and their negatives with the sign bit
+    pick = g.integers(0, 6, size=(N, K))
+    fp8_codes = np.array([0x38, 0x40, 0x48, 0xB8, 0xC0, 0xC8], np.uint8)[pick]
+    fp8_vals = np.array([1, 2, 4, -1, -2, -4], np.int64)[pick]
+    W8 = synth.fp8_from_parts(fp8_codes, np.full((2, 2), 127, np.uint8))
+    y8, _ = orc.gemv(2, W8, N, K, qx, dx)
+    assert np.array_equal(y8, (xi @ fp8_vals.T).astype(np.float64))
+    # FP4: codes 2 (1), 4 (2), 6 (4), 7 (6), 10 (-1), 15 (-6)
+    pick = g.integers(0, 6, size=(N, K))
+    nib = np.array([2, 4, 6, 7, 10, 15], np.uint8)[pick]
+    fp4_vals = np.array([1, 2, 4, 6, -1, -6], np.int64)[pick]
+    W4 = synth.fp4_from_parts((nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8),
+                              np.full((N, K // 32), 127, np.uint8))
+    y4, _ = orc.gemv(3, W4, N, K, qx, dx)
+    assert np.array_equal(y4, (xi @ fp4_vals.T).astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", [2, 3])
+def test_moe_routed_scaled_format_composition(orc, fmt):
+    """The routed MoE on FP8 / FP4 experts composes like the Q4_K one: top-1 with weight 1
+    gives down . Q8(silu(gate . x) * (up . x)) of the chosen expert in that format."""
+    g = np.random.default_rng(70 + fmt)
+    E, D, F = 4, 256, 512
+    gate, up, down = synth.moe_experts(g, E, D, F, fmt=fmt)
+    x = synth.activations(g, 1, D)
+    qx, dx, _ = orc.quantize_act_q8(x)
+    e = 2
+    y, _, st = orc.moe_routed(qx, dx, np.array([[e]]), np.ones((1, 1), np.float32), gate, up, down, D, F,
+                              fmt=fmt)
+    gg, _ = orc.gemv(fmt, gate[e], F, D, qx, dx)
+    vv, _ = orc.gemv(fmt, up[e], F, D, qx, dx)
+    h = np.array([orc.silu(a) for a in gg[0]]) * vv[0]
+    hq, hd, _ = orc.quantize_act_q8(h.astype(np.float32)[None])
+    o, _ = orc.gemv(fmt, down[e], D, F, hq, hd)
+    assert st == 0 and np.array_equal(y, o)
