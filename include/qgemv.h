@@ -20,6 +20,10 @@
  *          decode mat-vec plus the Q8 activation quantizer with a block sum.
  *  [ATOM]  ROCm/ATOM "DeepSeek-V4 Usage Guide" -- sigmoid routing of 6
  *          experts out of 256 or 384.
+ *  [ATOMQ] ROCm/ATOM "DeepSeek-V4 Usage Guide", section "FP8 on MI308 /
+ *          gfx942" -- the routed-expert quantization configs: FP8 e4m3 with
+ *          128 x 128 weight blocks and FP4 e2m1 with 1 x 32 microscaling, both
+ *          with ue8m0 scales (and the V4-Pro MoE backend note on FP4 e2m1).
  *  [LCPP]  llama.cpp pull request 24162 (DeepSeek V4 support) -- the grouped
  *          attention-output tensor, 8 groups of 1024 x 4096 rather than one
  *          4096 x 8192 matrix.
@@ -60,6 +64,23 @@
  *  projection here needs K % 256 == 0 (so each row is 16-byte aligned) and
  *  256 <= K <= QG_MAX_K.
  *
+ *  Block-scaled expert formats [ATOMQ] (the page gives the element, block and
+ *  scale formats, not the bytes; one matrix is one buffer of
+ *  qg_matrix_bytes(fmt, N, K) bytes: the codes, then from the first multiple
+ *  of 256 bytes after them, the scale bytes):
+ *  QG_FMT_FP8_E4M3_B128  codes uint8 [N, K], OCP FP8 E4M3 (sign, 4-bit
+ *               exponent with bias 7, 3-bit mantissa, no infinities,
+ *               S.1111.111 = NaN, largest value 448); scales uint8
+ *               [ceil(N/128), K/128], UE8M0.
+ *               weight (n, k) = e4m3(code) * 2^(S[n/128][k/128] - 127).
+ *  QG_FMT_FP4_E2M1_MX    codes uint8 [N, K/2], two OCP FP4 E2M1 values per
+ *               byte (element 2i in the low nibble of byte i, 2i+1 in the
+ *               high nibble; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ *               negatives); scales uint8 [N, K/32], UE8M0.
+ *               weight (n, k) = e2m1(code) * 2^(S[n][k/32] - 127).
+ *  UE8M0: an unsigned exponent, 2^(s - 127); s = 255 (NaN in the OCP
+ *  definition) is outside the contract.  Codes that are NaN give NaN.
+ *
  * Q8 activation (what quantize_act_q8 produces and every projection consumes):
  *  qx int8 [M, K]; dx fp32 [M, K/32], the scale of each 32-block;
  *  sx int32 [M, K/32], the sum of each block's quants (used by Q4_K's min term).
@@ -91,6 +112,8 @@ extern "C" {
 /* weight formats */
 #define QG_FMT_Q8_0 0
 #define QG_FMT_Q4K 1
+#define QG_FMT_FP8_E4M3_B128 2
+#define QG_FMT_FP4_E2M1_MX 3
 
 /* limits */
 #define QG_MAX_K 16384        /* largest K (inputs) of a projection */
@@ -199,6 +222,30 @@ int qgemv_q4k_f32(const void *W, int N, int K, const float *x, int M, float *y, 
 int qgemv_paired_f32(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const float *x, int M, float *y1,
                      float *y2, int8_t *qx, float *dx, int32_t *sx, void *stream);
 
+/* ---- block-scaled expert formats -------------------------------------- */
+/*
+ * qg_matrix_bytes -- bytes of an N x K weight matrix in format fmt (any of the
+ * four; for FP8 / FP4 the codes, the padding to 256 bytes and the scales).
+ * Returns 0 for an unknown format or an out-of-range shape (N >= 1,
+ * K % 256 == 0, 256 <= K <= QG_MAX_K).
+ */
+size_t qg_matrix_bytes(int fmt, int N, int K);
+
+/*
+ * qgemv_mx -- [ATOMQ] the expert formats' mat-vec as a dense projection:
+ *   y[m, n] = sum_k w[n, k] * (dx[m, k/32] * qx[m, k])
+ * W: QG_FMT_FP8_E4M3_B128 or QG_FMT_FP4_E2M1_MX [N, K] as described above;
+ * qx/dx: Q8 activation of M tokens; y fp32 [M, N].  The codes are converted
+ * to fp16 and dotted with the fp16 form of qx (exact) in fp32, one 16-byte
+ * chunk of a row at a time (16 FP8 or 32 FP4 weights), each chunk's sum
+ * scaled by dx * 2^(s - 127) and accumulated in fp32: the error is well under
+ * 1e-5 * sum_k |w x| per output (FP4 chunk sums are exact).
+ * Errors: QG_ERR_FORMAT (formats 2 and 3 only); QG_ERR_NULL; QG_ERR_SHAPE
+ * unless N >= 1, 1 <= M <= QG_MAX_M, K % 256 == 0, 256 <= K <= QG_MAX_K;
+ * QG_ERR_ALIGN; QG_ERR_LAUNCH.
+ */
+int qgemv_mx(int fmt, const void *W, int N, int K, const int8_t *qx, const float *dx, int M, float *y, void *stream);
+
 /* ---- routed MoE -------------------------------------------------------- */
 /*
  * Workspace of moe_routed_qgemv, in bytes, for the given sizes (0 if a size
@@ -265,6 +312,20 @@ int moe_routed_workspace_layout(int T, int topk, int E, int D, int F, size_t *of
 int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t *sx, int T, int D, int F, int E, int topk,
                      const int32_t *ids, const float *rw, const void *const *gate, const void *const *up,
                      const void *const *down, float *y, void *ws, size_t ws_bytes, int32_t *d_status, void *stream);
+
+/*
+ * moe_routed_qgemv_fmt -- moe_routed_qgemv with the experts in format fmt:
+ * QG_FMT_Q4K (exactly moe_routed_qgemv), or the [ATOMQ] expert formats
+ * QG_FMT_FP8_E4M3_B128 and QG_FMT_FP4_E2M1_MX (each gate/up/down pointer then
+ * points at one qg_matrix_bytes(fmt, ...) buffer).  Steps 1-4 as above; with
+ * the block-scaled formats gate/up and down run the qgemv_mx engine, and h is
+ * Q8-quantized once per pair before the down projection, for every T.
+ * Errors: QG_ERR_FORMAT for any other fmt; otherwise as moe_routed_qgemv.
+ */
+int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, const int32_t *sx, int T, int D, int F, int E,
+                         int topk, const int32_t *ids, const float *rw, const void *const *gate,
+                         const void *const *up, const void *const *down, float *y, void *ws, size_t ws_bytes,
+                         int32_t *d_status, void *stream);
 
 /* ---- prefill ----------------------------------------------------------- */
 /*

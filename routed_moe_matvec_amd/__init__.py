@@ -19,11 +19,14 @@ __all__ = [
     "qgemv_paired", "moe_routed_workspace_bytes", "moe_routed_workspace_layout", "moe_routed_qgemv",
     "qgemm_prefill", "qg_status_string", "qgemv_debug_block_isums", "pointer_table", "WS_REGIONS",
     "qgemv_q8_0_f32", "qgemv_q4k_f32", "qgemv_paired_f32", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
-    "qgemv_grouped", "qgemv_q8_0_quality",
+    "qgemv_grouped", "qgemv_q8_0_quality", "FMT_FP8_E4M3_B128", "FMT_FP4_E2M1_MX", "qg_matrix_bytes", "qgemv_mx",
+    "moe_routed_qgemv_fmt",
 ]
 
 FMT_Q8_0 = 0
 FMT_Q4K = 1
+FMT_FP8_E4M3_B128 = 2
+FMT_FP4_E2M1_MX = 3
 DEV_OK, DEV_BAD_EXPERT, DEV_NULL_EXPERT = 0, 1, 2
 MAX_K, MAX_M, MAX_MOE_PAIRS, MAX_EXPERTS = 16384, 32, 8192, 4096
 WS_REGIONS = ["NUNIQ", "UNIQ", "SLOT", "PAIR_OFF", "PAIRS", "G", "V", "H", "HQ", "HD", "HS", "O"]
@@ -65,6 +68,10 @@ _c_ws_bytes = _sig("moe_routed_workspace_bytes", _sz, [_i, _i, _i, _i, _i])
 _c_ws_layout = _sig("moe_routed_workspace_layout", _i, [_i, _i, _i, _i, _i, _vp])
 _c_moe = _sig("moe_routed_qgemv", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _sz, _vp, _vp])
+_c_moe_fmt = _sig("moe_routed_qgemv_fmt", _i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _vp, _sz, _vp, _vp])
+_c_matrix_bytes = _sig("qg_matrix_bytes", _sz, [_i, _i, _i])
+_c_mx = _sig("qgemv_mx", _i, [_i, _vp, _i, _i, _vp, _vp, _i, _vp, _vp])
 _c_prefill = _sig("qgemm_prefill", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
 _c_prefill_ws_bytes = _sig("qgemm_prefill_workspace_bytes", _sz, [_i, _i])
 _c_prefill_ws = _sig("qgemm_prefill_ws", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp, _sz, _vp])
@@ -175,6 +182,21 @@ def moe_routed_qgemv(qx, dx, sx, T: int, D: int, F: int, E: int, topk: int, ids,
                      ws_bytes: int, d_status, stream=None) -> None:
     _ok(_c_moe(_ptr(qx), _ptr(dx), _ptr(sx), T, D, F, E, topk, _ptr(ids), _ptr(rw), _ptr(gate), _ptr(up),
                _ptr(down), _ptr(y), _ptr(ws), ws_bytes, _ptr(d_status), _stream(stream, qx)), "moe_routed_qgemv")
+
+
+def moe_routed_qgemv_fmt(fmt: int, qx, dx, sx, T: int, D: int, F: int, E: int, topk: int, ids, rw, gate, up, down,
+                         y, ws, ws_bytes: int, d_status, stream=None) -> None:
+    _ok(_c_moe_fmt(fmt, _ptr(qx), _ptr(dx), _ptr(sx), T, D, F, E, topk, _ptr(ids), _ptr(rw), _ptr(gate), _ptr(up),
+                   _ptr(down), _ptr(y), _ptr(ws), ws_bytes, _ptr(d_status), _stream(stream, qx)),
+        "moe_routed_qgemv_fmt")
+
+
+def qg_matrix_bytes(fmt: int, N: int, K: int) -> int:
+    return int(_c_matrix_bytes(fmt, N, K))
+
+
+def qgemv_mx(fmt: int, W, N: int, K: int, qx, dx, M: int, y, stream=None) -> None:
+    _ok(_c_mx(fmt, _ptr(W), N, K, _ptr(qx), _ptr(dx), M, _ptr(y), _stream(stream, W)), "qgemv_mx")
 
 
 def qgemm_prefill(fmt: int, W, N: int, K: int, x_bf16, M: int, y, stream=None) -> None:

@@ -6,7 +6,10 @@
 // launch; its absence, or an expert id outside the expert range, is a hard
 // decode error.  Routing is 6 of 256/384 experts with sigmoid-normalized
 // weights (ROCm/ATOM "DeepSeek-V4 Usage Guide", opening paragraph and MoE
-// tips).  The experts are Q4_K (the "Q4KExperts" model of PR 623).
+// tips).  The experts are Q4_K (the "Q4KExperts" model of PR 623), or FP8
+// E4M3 with 128 x 128 block scales / FP4 E2M1 with 1 x 32 scales (the routed
+// expert formats of the same guide, section "FP8 on MI308 / gfx942"), which
+// run gate/up and down on the engine of mx_device.h.
 //
 // Launches on the caller's stream, none of which returns data to the host:
 //   1. table   : validate ids, distinct experts ascending, slots, CSR pair lists
@@ -24,6 +27,7 @@
 // computes and quantizes h itself while staging it, so 3 is not launched.
 #include "common.h"
 #include "gemv_device.h"
+#include "mx_device.h"
 #include "quantize_device.h"
 
 namespace qg {
@@ -296,6 +300,48 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     }
 }
 
+// Block-scaled expert formats (FP8 E4M3 128 x 128, FP4 E2M1 1 x 32): gate and
+// up of expert uniq[blockIdx.y] on the mx engine, workgroups [0, nwg) on gate
+// rows and [nwg, 2 nwg) on up rows, the tokens being the expert's pairs'.
+template <int FMT, int CPL>
+__global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs a, int nwg) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int R = mx_rows_per_wave(CPL);
+    const int u = blockIdx.y;
+    if (u >= *a.ws.nuniq) return;  // the whole workgroup leaves
+    const int e = a.ws.uniq[u];
+    const int p0 = a.ws.pair_off[u];
+    const int cnt = a.ws.pair_off[u + 1] - p0;
+    const bool is_up = (int)blockIdx.x >= nwg;
+    const int wg = is_up ? (int)blockIdx.x - nwg : (int)blockIdx.x;
+    const uint8_t *W = reinterpret_cast<const uint8_t *>(is_up ? a.up[e] : a.gate[e]);
+    float *dst = is_up ? a.ws.v : a.ws.g;
+    const int32_t *pairs = a.ws.pairs + p0;
+    const int topk = a.topk, F = a.F;
+    mx_workgroup<FMT, CPL>(
+        W, F, a.D, wg * kMxWaves * R, cnt, a.mt, a.qx, a.dx, [=](int m) { return pairs[m] / topk; },
+        [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; }, smem);
+}
+
+// down of expert uniq[blockIdx.y] on the mx engine against each pair's Q8 h.
+template <int FMT, int CPL>
+__global__ __launch_bounds__(kMxWaves *kWave) void moe_down_mx_kernel(MoeArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int R = mx_rows_per_wave(CPL);
+    const int u = blockIdx.y;
+    if (u >= *a.ws.nuniq) return;
+    const int e = a.ws.uniq[u];
+    const int p0 = a.ws.pair_off[u];
+    const int cnt = a.ws.pair_off[u + 1] - p0;
+    const uint8_t *W = reinterpret_cast<const uint8_t *>(a.down[e]);
+    const int32_t *pairs = a.ws.pairs + p0;
+    float *o = a.ws.o;
+    const int D = a.D;
+    mx_workgroup<FMT, CPL>(
+        W, D, a.F, (int)blockIdx.x * kMxWaves * R, cnt, a.mt, a.ws.hq, a.ws.hd, [=](int m) { return pairs[m]; },
+        [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; }, smem);
+}
+
 // h = silu(g) * v and its Q8 form for every valid pair, before the down
 // projection of more than one token: 8 lanes per 32-block, the quantizer of
 // the activation staging (so the records match the single-token form).
@@ -377,6 +423,46 @@ static bool raise_lds_limit(Kern *k, size_t bytes) {
                                (int)bytes) == hipSuccess;
 }
 
+// gate/up (K = D, F rows each) and down (K = F, D rows) on the mx engine.
+template <int FMT, int CPL>
+static int launch_moe_gate_up_mx(MoeArgs a, int Ucap, hipStream_t st) {
+    static bool raised = false;
+    if (!raised) raised = raise_lds_limit(moe_gate_up_mx_kernel<FMT, CPL>, kMxActBudget);
+    if (!raised) return QG_ERR_LAUNCH;
+    const int rows_per_wg = kMxWaves * mx_rows_per_wave(CPL);
+    const int nwg = (a.F + rows_per_wg - 1) / rows_per_wg;
+    a.mt = mx_tokens_per_chunk(a.D, QG_MAX_MOE_PAIRS);
+    hipLaunchKernelGGL((moe_gate_up_mx_kernel<FMT, CPL>), dim3(2 * nwg, Ucap), dim3(kMxWaves * kWave),
+                       (size_t)a.mt * mx_token_rec(a.D), st, a, nwg);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+template <int FMT, int CPL>
+static int launch_moe_down_mx(MoeArgs a, int Ucap, hipStream_t st) {
+    static bool raised = false;
+    if (!raised) raised = raise_lds_limit(moe_down_mx_kernel<FMT, CPL>, kMxActBudget);
+    if (!raised) return QG_ERR_LAUNCH;
+    const int rows_per_wg = kMxWaves * mx_rows_per_wave(CPL);
+    const int nwg = (a.D + rows_per_wg - 1) / rows_per_wg;
+    a.mt = mx_tokens_per_chunk(a.F, QG_MAX_MOE_PAIRS);
+    hipLaunchKernelGGL((moe_down_mx_kernel<FMT, CPL>), dim3(nwg, Ucap), dim3(kMxWaves * kWave),
+                       (size_t)a.mt * mx_token_rec(a.F), st, a);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+template <int FMT>
+static int launch_moe_mx(const MoeArgs &a, int Ucap, bool down, hipStream_t st) {
+    switch (mx_chunks_per_lane<FMT>(down ? a.F : a.D)) {
+        case 1: return down ? launch_moe_down_mx<FMT, 1>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 1>(a, Ucap, st);
+        case 2: return down ? launch_moe_down_mx<FMT, 2>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 2>(a, Ucap, st);
+        case 4: return down ? launch_moe_down_mx<FMT, 4>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 4>(a, Ucap, st);
+        case 8: return down ? launch_moe_down_mx<FMT, 8>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 8>(a, Ucap, st);
+        case 16:
+            return down ? launch_moe_down_mx<FMT, 16>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 16>(a, Ucap, st);
+        default: return QG_ERR_SHAPE;
+    }
+}
+
 }  // namespace qg
 
 extern "C" size_t moe_routed_workspace_bytes(int T, int topk, int E, int D, int F) {
@@ -392,11 +478,12 @@ extern "C" int moe_routed_workspace_layout(int T, int topk, int E, int D, int F,
     return QG_OK;
 }
 
-extern "C" int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t *sx, int T, int D, int F, int E,
-                                int topk, const int32_t *ids, const float *rw, const void *const *gate,
-                                const void *const *up, const void *const *down, float *y, void *ws,
-                                size_t ws_bytes, int32_t *d_status, void *stream) {
+extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, const int32_t *sx, int T, int D,
+                                    int F, int E, int topk, const int32_t *ids, const float *rw,
+                                    const void *const *gate, const void *const *up, const void *const *down,
+                                    float *y, void *ws, size_t ws_bytes, int32_t *d_status, void *stream) {
     using namespace qg;
+    if (fmt != QG_FMT_Q4K && fmt != QG_FMT_FP8_E4M3_B128 && fmt != QG_FMT_FP4_E2M1_MX) return QG_ERR_FORMAT;
     if (!qx || !dx || !sx || !ids || !rw || !gate || !up || !down || !y || !ws || !d_status) return QG_ERR_NULL;
     if (!moe_shape_ok(T, topk, E, D, F)) return QG_ERR_SHAPE;
     size_t off[QG_WS_COUNT];
@@ -426,6 +513,22 @@ extern "C" int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t
     a.up = up;
     a.down = down;
     a.ws = w;
+    if (fmt != QG_FMT_Q4K) {
+        // block-scaled experts: gate/up, h quantized once per pair, down, combine
+        int rc = fmt == QG_FMT_FP8_E4M3_B128 ? launch_moe_mx<QG_FMT_FP8_E4M3_B128>(a, Ucap, false, st)
+                                             : launch_moe_mx<QG_FMT_FP4_E2M1_MX>(a, Ucap, false, st);
+        if (rc) return rc;
+        const long long hthreads = (long long)P * (F / 32) * 8;
+        hipLaunchKernelGGL(moe_h_quant_kernel, dim3((unsigned)((hthreads + 255) / 256)), dim3(256), 0, st, w, P, F);
+        if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
+        rc = fmt == QG_FMT_FP8_E4M3_B128 ? launch_moe_mx<QG_FMT_FP8_E4M3_B128>(a, Ucap, true, st)
+                                         : launch_moe_mx<QG_FMT_FP4_E2M1_MX>(a, Ucap, true, st);
+        if (rc) return rc;
+        const long long cthreads = (long long)T * (D / 4);
+        hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cthreads + 255) / 256)), dim3(256), 0, st, w, rw, T,
+                           D, topk, y);
+        return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+    }
     const bool one = T == 1;  // every expert then has a single pair (a few if the token repeats an id)
     constexpr int threads = kMoeWaves * kWave;
     static bool lds_raised = false;  // idempotent: raise the dynamic-LDS limit once
@@ -468,4 +571,12 @@ extern "C" int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cthreads + 255) / 256)), dim3(256), 0, st, w, rw, T, D,
                        topk, y);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+extern "C" int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t *sx, int T, int D, int F, int E,
+                                int topk, const int32_t *ids, const float *rw, const void *const *gate,
+                                const void *const *up, const void *const *down, float *y, void *ws,
+                                size_t ws_bytes, int32_t *d_status, void *stream) {
+    return moe_routed_qgemv_fmt(QG_FMT_Q4K, qx, dx, sx, T, D, F, E, topk, ids, rw, gate, up, down, y, ws, ws_bytes,
+                                d_status, stream);
 }

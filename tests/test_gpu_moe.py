@@ -31,10 +31,10 @@ def qg():
 class MoeProblem:
     """Experts, ids, routing weights and activations on the host and the device."""
 
-    def __init__(self, qg, E, D, F, T, topk, seed, ids=None, only_selected=False, zipf=False):
+    def __init__(self, qg, E, D, F, T, topk, seed, ids=None, only_selected=False, zipf=False, fmt=1):
         import torch
         g = synth.rng(seed)
-        self.E, self.D, self.F, self.T, self.topk = E, D, F, T, topk
+        self.E, self.D, self.F, self.T, self.topk, self.fmt = E, D, F, T, topk, fmt
         if ids is None:
             ids = synth.moe_ids_zipf(g, T, E, topk) if zipf else synth.moe_ids_uniform(g, T, E, topk)
         self.ids = np.asarray(ids, np.int32)
@@ -46,9 +46,9 @@ class MoeProblem:
             if only_selected and e not in needed:
                 continue
             ge = np.random.default_rng([seed, e])  # per-expert stream: independent of which are built
-            self.gate[e] = synth.q4k_weight(ge, F, D)
-            self.up[e] = synth.q4k_weight(ge, F, D)
-            self.down[e] = synth.q4k_weight(ge, D, F)
+            self.gate[e] = synth.weight(fmt, ge, F, D)
+            self.up[e] = synth.weight(fmt, ge, F, D)
+            self.down[e] = synth.weight(fmt, ge, D, F)
         self.dgate = [None if w is None else dev(w) for w in self.gate]
         self.dup = [None if w is None else dev(w) for w in self.up]
         self.ddown = [None if w is None else dev(w) for w in self.down]
@@ -70,8 +70,12 @@ class MoeProblem:
         status = sentinel((1,), torch.int32, -99)
         y = sentinel((T, self.D), torch.float32, 777.0)
         tabs = [qg.pointer_table(lst, "cuda") for lst in (gate or self.dgate, up or self.dup, down or self.ddown)]
-        qg.moe_routed_qgemv(self.qx[:T], self.dx[:T], self.sx[:T], T, self.D, self.F, self.E, topk, dev(ids),
-                            dev(rw), tabs[0], tabs[1], tabs[2], y, ws, nbytes, status)
+        if self.fmt == 1:
+            qg.moe_routed_qgemv(self.qx[:T], self.dx[:T], self.sx[:T], T, self.D, self.F, self.E, topk, dev(ids),
+                                dev(rw), tabs[0], tabs[1], tabs[2], y, ws, nbytes, status)
+        else:
+            qg.moe_routed_qgemv_fmt(self.fmt, self.qx[:T], self.dx[:T], self.sx[:T], T, self.D, self.F, self.E,
+                                    topk, dev(ids), dev(rw), tabs[0], tabs[1], tabs[2], y, ws, nbytes, status)
         torch.cuda.synchronize()
         return host(y), ws, int(host(status)[0])
 
@@ -116,8 +120,8 @@ def check_staged(qg, orc, pb: MoeProblem, y, ws, pairs_to_check=None, tokens_to_
     o_ref = {}
     for p in check:
         t, e = p // topk, int(pb.ids.ravel()[p])
-        gr, gb = orc.gemv(1, pb.gate[e], F, D, qx[t:t + 1], dx[t:t + 1], nthreads=nt)
-        vr, vb = orc.gemv(1, pb.up[e], F, D, qx[t:t + 1], dx[t:t + 1], nthreads=nt)
+        gr, gb = orc.gemv(pb.fmt, pb.gate[e], F, D, qx[t:t + 1], dx[t:t + 1], nthreads=nt)
+        vr, vb = orc.gemv(pb.fmt, pb.up[e], F, D, qx[t:t + 1], dx[t:t + 1], nthreads=nt)
         assert_within_bound(R["g"][p:p + 1], gr, gb, what="g pair %d" % p)
         assert_within_bound(R["v"][p:p + 1], vr, vb, what="v pair %d" % p)
         g64, v64 = R["g"][p].astype(np.float64), R["v"][p].astype(np.float64)
@@ -126,7 +130,7 @@ def check_staged(qg, orc, pb: MoeProblem, y, ws, pairs_to_check=None, tokens_to_
         hq, hd, hs = orc.quantize_act_q8(R["h"][p:p + 1])
         assert np.array_equal(R["hq"][p], hq[0]) and np.array_equal(R["hs"][p], hs[0])
         assert np.array_equal(R["hd"][p].view(np.uint32), hd[0].view(np.uint32))
-        orf, ob = orc.gemv(1, pb.down[e], D, F, R["hq"][p:p + 1], R["hd"][p:p + 1], nthreads=nt)
+        orf, ob = orc.gemv(pb.fmt, pb.down[e], D, F, R["hq"][p:p + 1], R["hd"][p:p + 1], nthreads=nt)
         assert_within_bound(R["o"][p:p + 1], orf, ob, what="o pair %d" % p)
         o_ref[p] = (orf[0], ob[0])
     toks = range(pb.T) if tokens_to_check is None else tokens_to_check

@@ -106,3 +106,37 @@ def test_prefill_workspace_sizing():
         assert nb % 256 == 0 and nb <= 2 * M * K + 4 * M + 2 * 256
     for M, K in [(0, 256), (4, 300), (4, 128), (4, 16384 + 256)]:
         assert qg.qgemm_prefill_workspace_bytes(M, K) == 0, (M, K)
+
+
+def test_matrix_bytes_match_the_documented_layout():
+    """qg_matrix_bytes agrees with the storage the generators write (codes, padding to
+    256 bytes, scales) for the block-scaled formats and with whole rows for the others."""
+    import routed_moe_matvec_amd as qg
+    import synth
+    for N, K in [(1, 256), (127, 512), (129, 4096), (300, 7168), (4096, 16384)]:
+        assert qg.qg_matrix_bytes(0, N, K) == N * (K // 32) * 34
+        assert qg.qg_matrix_bytes(1, N, K) == N * (K // 256) * 144
+        for fmt in (2, 3):
+            assert qg.qg_matrix_bytes(fmt, N, K) == synth.scaled_matrix_bytes(fmt, N, K), (fmt, N, K)
+    for fmt, N, K in [(4, 8, 512), (2, 0, 512), (3, 8, 300), (2, 8, 128), (3, 8, 16384 + 256)]:
+        assert qg.qg_matrix_bytes(fmt, N, K) == 0, (fmt, N, K)
+
+
+def test_mx_host_validation_without_gpu(lib):
+    vp = ctypes.c_void_p
+    fake = vp(1 << 40)
+    f = lib.qgemv_mx
+    f.argtypes = [ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp]
+    assert f(0, fake, 8, 512, fake, fake, 1, fake, None) == -4   # Q8_0 is not a block-scaled format
+    assert f(2, None, 8, 512, fake, fake, 1, fake, None) == -1
+    assert f(3, fake, 8, 384, fake, fake, 1, fake, None) == -2
+    assert f(3, fake, 8, 512, fake, fake, 33, fake, None) == -2
+    assert f(2, vp((1 << 40) + 4), 8, 512, fake, fake, 1, fake, None) == -3
+    m = lib.moe_routed_qgemv_fmt
+    m.argtypes = [ctypes.c_int] + [vp] * 3 + [ctypes.c_int] * 5 + [vp] * 7 + [ctypes.c_size_t, vp, vp]
+    assert m(0, fake, fake, fake, 1, 4096, 2048, 256, 6, fake, fake, fake, fake, fake, fake, fake, 1 << 30,
+             fake, None) == -4
+    assert m(3, fake, fake, fake, 1, 4096, 2000, 256, 6, fake, fake, fake, fake, fake, fake, fake, 1 << 30,
+             fake, None) == -2
+    assert m(2, fake, fake, fake, 1, 4096, 2048, 256, 6, fake, fake, fake, fake, fake, fake, fake, 16,
+             fake, None) == -5
