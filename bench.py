@@ -21,7 +21,8 @@ MoE tokens/s, prefill) measured the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --summarize-rocprof DIR   (turn rocprofv3 csv output into a text summary)
-       python bench.py --probe {gemv,copy,prefill,prefill_ws,moe_e256_t1,...} --steps K
+       python bench.py --probe {gemv,gemv_batch,copy,prefill,prefill_ws,fp8_16384x4096,fp4_16384x4096,
+                                 moe_e256_t1,moe_fp8_e256_t1,moe_fp4_e384_t1,...} --steps K
                  (eager launches of one kernel, for rocprofv3 --pmc counter runs)
        python bench.py --summarize-pmc GEMV_FETCH GEMV_WRITE COPY_FETCH COPY_WRITE
                  (HBM bytes per launch of the GEMV from FETCH_SIZE / WRITE_SIZE runs,
@@ -244,6 +245,8 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
             y = torch.empty(M, G * N, dtype=torch.float32, device=dev)
             if G > 1:
                 fn = lambda i: qg.qgemv_grouped(fmt, copies[i % R], G, N, K, qx, dx, sx, M, y)
+            elif fmt in (qg.FMT_FP8_E4M3_B128, qg.FMT_FP4_E2M1_MX):
+                fn = lambda i: qg.qgemv_mx(fmt, copies[i % R], N, K, qx, dx, M, y)
             elif fmt == 0:
                 fn = lambda i: qg.qgemv_q8_0(copies[i % R], N, K, qx, dx, M, y)
             else:
@@ -252,7 +255,7 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
             g = capture(fn, n, stream)
             timer.run(g.replay)
             sec = timer.run(g.replay) / n
-            byts = W_host.nbytes + G * (M * K + M * (K // 32) * (8 if fmt else 4) + M * N * 4)
+            byts = W_host.nbytes + G * (M * K + M * (K // 32) * (8 if fmt == 1 else 4) + M * N * 4)
             res["M%d" % M] = {"us": round(sec * 1e6, 3), "GB_s": round(byts / sec / 1e9, 1),
                               "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4)}
             del g
@@ -263,6 +266,7 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
     def moe_rate(key, n_sets):
         w = synth.WORKLOADS[key]
         E, D, F, T, topk = w["E"], w["D"], w["F"], w["T"], w["topk"]
+        fmt = w.get("fmt", qg.FMT_Q4K)
         g = synth.rng(w["seed"])
         # two full expert pools, generated expert by expert straight to the device
         pools = []
@@ -270,7 +274,7 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
             pool = [[], [], []]
             for e in range(E):
                 for lst, (n, k) in zip(pool, ((F, D), (F, D), (D, F))):
-                    lst.append(torch.from_numpy(synth.q4k_weight(g, n, k)).to(dev))
+                    lst.append(torch.from_numpy(synth.weight(fmt, g, n, k)).to(dev))
             pools.append([qg.pointer_table(lst, dev) for lst in pool] + [pool])
         draw = synth.moe_ids_zipf if w["ids"] == "zipf" else synth.moe_ids_uniform
         ids = [draw(g, T, E, topk) for _ in range(n_sets)]
@@ -289,20 +293,22 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
             k = i % n_sets
             pool = pools[i % 2]
             qg.quantize_act_q8(xs[k], T, D, qx, dx, sx)
-            qg.moe_routed_qgemv(qx, dx, sx, T, D, F, E, topk, ids_d[k], rws[k], pool[0], pool[1], pool[2], y, ws,
-                                nbytes, status)
+            qg.moe_routed_qgemv_fmt(fmt, qx, dx, sx, T, D, F, E, topk, ids_d[k], rws[k], pool[0], pool[1], pool[2],
+                                    y, ws, nbytes, status)
 
         n = 2 * n_sets
         gr = capture(call, n, stream)
         timer.run(gr.replay)
         sec = timer.run(gr.replay) / n
-        expert_bytes = 2 * F * (D // 256) * 144 + D * (F // 256) * 144
+        expert_bytes = 2 * qg.qg_matrix_bytes(fmt, F, D) + qg.qg_matrix_bytes(fmt, D, F)
         uniq = np.mean([len(np.unique(i)) for i in ids])
         byts = uniq * expert_bytes + T * D * 4 * 2 + T * topk * 8
         out["moe_" + key.split("_", 1)[1]] = {
             "tokens_per_s": round(T / sec, 1), "us_per_call": round(sec * 1e6, 3), "mean_distinct_experts": float(uniq),
             "GB_s": round(byts / sec / 1e9, 1), "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4),
-            "includes": "quantize_act_q8 of the T tokens + moe_routed_qgemv (4 launches at T=1, else 5)"}
+            "includes": ("quantize_act_q8 of the T tokens + moe_routed_qgemv (4 launches at T=1, else 5)"
+                         if fmt == qg.FMT_Q4K else
+                         "quantize_act_q8 of the T tokens + moe_routed_qgemv_fmt (5 launches)")}
         del gr, pools, ws
         torch.cuda.empty_cache()
 
@@ -366,10 +372,15 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
     w = synth.WORKLOADS["q8_0_16384x4096"]
     gemv_rate(0, synth.q8_0_weight(synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], list(w["Ms"]),
               "q8_0_16384x4096")
+    for key in ("fp8_16384x4096", "fp4_16384x4096"):
+        w = synth.WORKLOADS[key]
+        gemv_rate(w["fmt"], synth.weight(w["fmt"], synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], [1], key)
     prefill_rate()
     moe_rate("moe_e256_t1", 16)
     moe_rate("moe_e256_t8", 16)
     moe_rate("moe_e384_t64_zipf", 4)
+    moe_rate("moe_fp8_e256_t1", 16)
+    moe_rate("moe_fp4_e384_t1", 16)
     return out
 
 
@@ -441,6 +452,23 @@ def run_probe(name: str, steps: int, warmup: int, qg, torch) -> None:
 
         def fn(i):
             qg.qgemv_q8_0(copies[i % R], N, K, qx, dx, M, y)
+    elif name in ("fp8_16384x4096", "fp4_16384x4096"):
+        w = synth.WORKLOADS[name]
+        g = synth.rng(w["seed"])
+        fmt, N, K = w["fmt"], w["N"], w["K"]
+        W_host = synth.weight(fmt, g, N, K)
+        R = rotation_count(W_host.nbytes)
+        base = torch.from_numpy(W_host).to("cuda")
+        copies = [base] + [base.clone() for _ in range(R - 1)]
+        x = torch.from_numpy(synth.activations(g, 1, K)).to("cuda")
+        qx = torch.empty(1, K, dtype=torch.int8, device="cuda")
+        dx = torch.empty(1, K // 32, dtype=torch.float32, device="cuda")
+        sx = torch.empty(1, K // 32, dtype=torch.int32, device="cuda")
+        qg.quantize_act_q8(x, 1, K, qx, dx, sx)
+        y = torch.empty(1, N, dtype=torch.float32, device="cuda")
+
+        def fn(i):
+            qg.qgemv_mx(fmt, copies[i % R], N, K, qx, dx, 1, y)
     elif name == "copy":
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -468,13 +496,14 @@ def run_probe(name: str, steps: int, warmup: int, qg, torch) -> None:
     elif name.startswith("moe_"):
         w = synth.WORKLOADS[name]
         E, D, F, T, topk = w["E"], w["D"], w["F"], w["T"], w["topk"]
+        fmt = w.get("fmt", qg.FMT_Q4K)
         g = synth.rng(w["seed"])
         pools = []
         for _ in range(2):
             pool = [[], [], []]
             for e in range(E):
                 for lst, (n, k) in zip(pool, ((F, D), (F, D), (D, F))):
-                    lst.append(torch.from_numpy(synth.q4k_weight(g, n, k)).to("cuda"))
+                    lst.append(torch.from_numpy(synth.weight(fmt, g, n, k)).to("cuda"))
             pools.append([qg.pointer_table(lst, "cuda") for lst in pool] + [pool])
         draw = synth.moe_ids_zipf if w["ids"] == "zipf" else synth.moe_ids_uniform
         ids_d = torch.from_numpy(draw(g, T, E, topk)).to("cuda")
@@ -491,8 +520,8 @@ def run_probe(name: str, steps: int, warmup: int, qg, torch) -> None:
         def fn(i):
             pool = pools[i % 2]
             qg.quantize_act_q8(x, T, D, qx, dx, sx)
-            qg.moe_routed_qgemv(qx, dx, sx, T, D, F, E, topk, ids_d, rw, pool[0], pool[1], pool[2], y, ws, nb,
-                                status)
+            qg.moe_routed_qgemv_fmt(fmt, qx, dx, sx, T, D, F, E, topk, ids_d, rw, pool[0], pool[1], pool[2], y, ws,
+                                    nb, status)
     else:
         raise SystemExit("unknown probe %r" % name)
     for i in range(warmup):

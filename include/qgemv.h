@@ -67,7 +67,8 @@
  *  Block-scaled expert formats [ATOMQ] (the page gives the element, block and
  *  scale formats, not the bytes; one matrix is one buffer of
  *  qg_matrix_bytes(fmt, N, K) bytes: the codes, then from the first multiple
- *  of 256 bytes after them, the scale bytes):
+ *  of 256 bytes after them, the scale bytes, then padding up to a multiple of
+ *  16 bytes, so that matrices stored back to back stay 16-byte aligned):
  *  QG_FMT_FP8_E4M3_B128  codes uint8 [N, K], OCP FP8 E4M3 (sign, 4-bit
  *               exponent with bias 7, 3-bit mantissa, no infinities,
  *               S.1111.111 = NaN, largest value 448); scales uint8
@@ -225,7 +226,8 @@ int qgemv_paired_f32(int fmt, const void *W1, int N1, const void *W2, int N2, in
 /* ---- block-scaled expert formats -------------------------------------- */
 /*
  * qg_matrix_bytes -- bytes of an N x K weight matrix in format fmt (any of the
- * four; for FP8 / FP4 the codes, the padding to 256 bytes and the scales).
+ * four; for FP8 / FP4 the codes, the padding to 256 bytes, the scales and
+ * the padding to a multiple of 16 bytes).
  * Returns 0 for an unknown format or an out-of-range shape (N >= 1,
  * K % 256 == 0, 256 <= K <= QG_MAX_K).
  */

@@ -64,7 +64,8 @@
  *   ROCm/ATOM "DeepSeek-V4 Usage Guide", section "FP8 on MI308 / gfx942":
  *   its quantization-config table and the V4-Pro MoE backend note).  One
  *   matrix of N rows and K columns is one buffer: the codes, then, from the
- *   first multiple of 256 bytes after them, the scale bytes.
+ *   first multiple of 256 bytes after them, the scale bytes, then zeros up to
+ *   a multiple of 16 bytes (matrices stored back to back stay 16-byte aligned).
  *     FP8: codes uint8 [N][K]; scales [ceil(N/128)][K/128];
  *          weight (n, k) = e4m3(code) * 2^(S[n/128][k/128] - 127).
  *     FP4: codes uint8 [N][K/2], element 2i in the low nibble of byte i and
@@ -178,11 +179,14 @@ static int64_t scale_offset(int fmt, int64_t N, int64_t K) {
     return (codes + 255) / 256 * 256;
 }
 
-/* Bytes of a whole N x K matrix in format fmt (codes and, for FP8 / FP4, scales). */
+/* Bytes of a whole N x K matrix in format fmt (codes and, for FP8 / FP4,
+ * scales, the buffer rounded up to a multiple of 16 bytes). */
 int64_t oracle_matrix_bytes(int fmt, int64_t N, int64_t K) {
-    if (fmt == ORACLE_FMT_FP8_B128) return scale_offset(fmt, N, K) + (N + 127) / 128 * (K / 128);
-    if (fmt == ORACLE_FMT_FP4_MX) return scale_offset(fmt, N, K) + N * (K / 32);
-    return N * oracle_row_bytes(fmt, K);
+    int64_t end;
+    if (fmt == ORACLE_FMT_FP8_B128) end = scale_offset(fmt, N, K) + (N + 127) / 128 * (K / 128);
+    else if (fmt == ORACLE_FMT_FP4_MX) end = scale_offset(fmt, N, K) + N * (K / 32);
+    else return N * oracle_row_bytes(fmt, K);
+    return (end + 15) / 16 * 16;
 }
 
 /* Dequantize the 32 weights of block b (0 .. K/32-1) of one row into w[32]. */

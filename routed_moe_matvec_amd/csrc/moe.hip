@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
 template <int FMT, int CPL>
 __global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs a, int nwg) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int R = mx_rows_per_wave(CPL);
+    constexpr int R = mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int u = blockIdx.y;
     if (u >= *a.ws.nuniq) return;  // the whole workgroup leaves
     const int e = a.ws.uniq[u];
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs
     float *dst = is_up ? a.ws.v : a.ws.g;
     const int32_t *pairs = a.ws.pairs + p0;
     const int topk = a.topk, F = a.F;
-    mx_workgroup<FMT, CPL>(
+    mx_workgroup<FMT, CPL, kMxLoadsRouted>(
         W, F, a.D, wg * kMxWaves * R, cnt, a.mt, a.qx, a.dx, [=](int m) { return pairs[m] / topk; },
         [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; }, smem);
 }
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs
 template <int FMT, int CPL>
 __global__ __launch_bounds__(kMxWaves *kWave) void moe_down_mx_kernel(MoeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int R = mx_rows_per_wave(CPL);
+    constexpr int R = mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int u = blockIdx.y;
     if (u >= *a.ws.nuniq) return;
     const int e = a.ws.uniq[u];
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_down_mx_kernel(MoeArgs a)
     const int32_t *pairs = a.ws.pairs + p0;
     float *o = a.ws.o;
     const int D = a.D;
-    mx_workgroup<FMT, CPL>(
+    mx_workgroup<FMT, CPL, kMxLoadsRouted>(
         W, D, a.F, (int)blockIdx.x * kMxWaves * R, cnt, a.mt, a.ws.hq, a.ws.hd, [=](int m) { return pairs[m]; },
         [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; }, smem);
 }
@@ -427,26 +427,26 @@ static bool raise_lds_limit(Kern *k, size_t bytes) {
 template <int FMT, int CPL>
 static int launch_moe_gate_up_mx(MoeArgs a, int Ucap, hipStream_t st) {
     static bool raised = false;
-    if (!raised) raised = raise_lds_limit(moe_gate_up_mx_kernel<FMT, CPL>, kMxActBudget);
+    if (!raised) raised = raise_lds_limit(moe_gate_up_mx_kernel<FMT, CPL>, kMxLdsMax);
     if (!raised) return QG_ERR_LAUNCH;
-    const int rows_per_wg = kMxWaves * mx_rows_per_wave(CPL);
+    const int rows_per_wg = kMxWaves * mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int nwg = (a.F + rows_per_wg - 1) / rows_per_wg;
     a.mt = mx_tokens_per_chunk(a.D, QG_MAX_MOE_PAIRS);
     hipLaunchKernelGGL((moe_gate_up_mx_kernel<FMT, CPL>), dim3(2 * nwg, Ucap), dim3(kMxWaves * kWave),
-                       (size_t)a.mt * mx_token_rec(a.D), st, a, nwg);
+                       (size_t)a.mt * mx_token_rec(a.D) + mx_scale_lds<FMT>(a.D, CPL, kMxLoadsRouted), st, a, nwg);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
 template <int FMT, int CPL>
 static int launch_moe_down_mx(MoeArgs a, int Ucap, hipStream_t st) {
     static bool raised = false;
-    if (!raised) raised = raise_lds_limit(moe_down_mx_kernel<FMT, CPL>, kMxActBudget);
+    if (!raised) raised = raise_lds_limit(moe_down_mx_kernel<FMT, CPL>, kMxLdsMax);
     if (!raised) return QG_ERR_LAUNCH;
-    const int rows_per_wg = kMxWaves * mx_rows_per_wave(CPL);
+    const int rows_per_wg = kMxWaves * mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int nwg = (a.D + rows_per_wg - 1) / rows_per_wg;
     a.mt = mx_tokens_per_chunk(a.F, QG_MAX_MOE_PAIRS);
     hipLaunchKernelGGL((moe_down_mx_kernel<FMT, CPL>), dim3(nwg, Ucap), dim3(kMxWaves * kWave),
-                       (size_t)a.mt * mx_token_rec(a.F), st, a);
+                       (size_t)a.mt * mx_token_rec(a.F) + mx_scale_lds<FMT>(a.F, CPL, kMxLoadsRouted), st, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 

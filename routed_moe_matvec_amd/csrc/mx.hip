@@ -17,27 +17,28 @@ struct MxArgs {
 template <int FMT, int CPL>
 __global__ __launch_bounds__(kMxWaves *kWave) void qgemv_mx_kernel(MxArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int R = mx_rows_per_wave(CPL);
+    constexpr int L = mx_loads(FMT);
+    constexpr int R = mx_rows_per_wave(L, CPL);
     float *y = a.y;
     const int N = a.N;
-    mx_workgroup<FMT, CPL>(
+    mx_workgroup<FMT, CPL, L>(
         a.W, a.N, a.K, (int)blockIdx.x * kMxWaves * R, a.M, a.mt, a.qx, a.dx, [](int m) { return m; },
         [=](int m, int row, float v) { y[(size_t)m * N + row] = v; }, smem);
 }
 
 template <int FMT, int CPL>
 static int launch_mx_cpl(MxArgs &a, hipStream_t stream) {
-    constexpr int rows_per_wg = kMxWaves * mx_rows_per_wave(CPL);
+    constexpr int rows_per_wg = kMxWaves * mx_rows_per_wave(mx_loads(FMT), CPL);
     static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_mx_kernel<FMT, CPL>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kMxActBudget) != hipSuccess)
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kMxLdsMax) != hipSuccess)
             return QG_ERR_LAUNCH;
         attr_set = true;
     }
     const int grid = (a.N + rows_per_wg - 1) / rows_per_wg;
     hipLaunchKernelGGL((qgemv_mx_kernel<FMT, CPL>), dim3(grid), dim3(kMxWaves * kWave),
-                       (size_t)a.mt * mx_token_rec(a.K), stream, a);
+                       (size_t)a.mt * mx_token_rec(a.K) + mx_scale_lds<FMT>(a.K, CPL, mx_loads(FMT)), stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
@@ -61,8 +62,9 @@ extern "C" size_t qg_matrix_bytes(int fmt, int N, int K) {
     switch (fmt) {
         case QG_FMT_Q8_0: return (size_t)N * (K / 32) * 34;
         case QG_FMT_Q4K: return (size_t)N * (K / 256) * 144;
-        case QG_FMT_FP8_E4M3_B128: return qg::mx_align256((size_t)N * K) + (size_t)((N + 127) / 128) * (K / 128);
-        case QG_FMT_FP4_E2M1_MX: return qg::mx_align256((size_t)N * K / 2) + (size_t)N * (K / 32);
+        case QG_FMT_FP8_E4M3_B128:
+            return qg::mx_align16(qg::mx_align256((size_t)N * K) + (size_t)((N + 127) / 128) * (K / 128));
+        case QG_FMT_FP4_E2M1_MX: return qg::mx_align16(qg::mx_align256((size_t)N * K / 2) + (size_t)N * (K / 32));
         default: return 0;
     }
 }

@@ -9,11 +9,13 @@
 //
 // Storage of one N x K matrix: the codes row-major (FP4: two per byte,
 // element 2i in the low nibble), then from the next multiple of 256 bytes the
-// scale bytes, [ceil(N/128)][K/128] for FP8 and [N][K/32] for FP4.
+// scale bytes, [ceil(N/128)][K/128] for FP8 and [N][K/32] for FP4, then
+// padding to a multiple of 16 bytes (so the aligned 4-byte word holding any
+// scale byte lies inside the buffer).
 //
 // A lane takes 16-byte chunks of a row (16 FP8 or 32 FP4 weights; one FP4
 // chunk is one 32-block and one scale) with 64 consecutive chunks per wave
-// instruction; a wave keeps kMxLoads chunks of R = kMxLoads / CPL rows in
+// instruction; a wave keeps L chunks of R = L / CPL rows in
 // flight (CPL chunks per lane and row).  The tokens' Q8 activation is staged
 // once per workgroup in LDS as fp16 (exact for int8), 64-byte block records
 // padded to 80 bytes so that eight lanes reading consecutive blocks meet eight
@@ -22,7 +24,7 @@
 // accumulates them against the activation in fp32 (for FP4 every partial sum
 // is a multiple of 1/2 below 2^15, so it is exact); then
 // acc = fma(partial, ldexp(dx[m, b], s - 127), acc) in chunk order and the
-// row's lanes meet in an xor butterfly.
+// row's lanes meet in a fixed DPP reduction.
 #pragma once
 
 #include "common.h"
@@ -33,12 +35,22 @@ typedef _Float16 mx_half2 __attribute__((ext_vector_type(2)));
 typedef unsigned int mx_u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMxWaves = 4;
-constexpr int kMxLoads = 16;             // 16-byte weight chunks a lane keeps in flight
+constexpr int kMxThreads = kMxWaves * 64;  // every launch of the engine uses this many threads
+// 16-byte weight chunks a lane keeps in flight (L).  Dense mat-vecs: 4 for
+// FP8, 8 for FP4 (its decode costs twice the instructions per byte); fewer
+// rows per wave and more waves measured faster for both than 16.  Routed
+// experts: 16, since each workgroup first waits for its expert's pointer and
+// pair list and the staged tokens, a cost more rows amortize.
+__host__ __device__ constexpr int mx_loads(int fmt) { return fmt == QG_FMT_FP4_E2M1_MX ? 8 : 4; }
+constexpr int kMxLoadsRouted = 16;
 constexpr int kMxActBudget = 64 * 1024;  // LDS for staged tokens
+constexpr int kMxLdsMax = kMxActBudget + 4096;  // with a workgroup's weight scales
 constexpr int kMxBlockRec = 80;          // LDS bytes of one 32-block of fp16 activation (64 + pad)
+constexpr int kMxStageRegs = 1;          // activation pieces per thread requested before the weights
 
-__host__ __device__ constexpr int mx_rows_per_wave(int cpl) { return kMxLoads / cpl > 0 ? kMxLoads / cpl : 1; }
+__host__ __device__ constexpr int mx_rows_per_wave(int loads, int cpl) { return loads / cpl > 0 ? loads / cpl : 1; }
 __host__ __device__ inline size_t mx_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline size_t mx_align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 template <int FMT>
 struct MxFmt;
@@ -66,6 +78,17 @@ struct MxFmt<QG_FMT_FP4_E2M1_MX> {
 // LDS bytes of one staged token: the fp16 block records, then the fp32 scales.
 __host__ __device__ inline int mx_token_rec(int K) { return (K / 32) * (kMxBlockRec + 4); }
 
+// LDS bytes of a workgroup's weight scales, after the staged tokens: FP4 the
+// [rows][K/32] scales of its kMxWaves * R rows, FP8 the one [K/128] row of
+// its 128-row block (a workgroup's rows never straddle one: their count
+// divides 128).
+template <int FMT>
+__host__ __device__ inline int mx_scale_lds(int K, int cpl, int loads) {
+    const int rows = kMxWaves * mx_rows_per_wave(loads, cpl);
+    const int bytes = FMT == QG_FMT_FP4_E2M1_MX ? rows * (K / 32) : K / 128;
+    return (bytes + 15) / 16 * 16;
+}
+
 // Chunks per lane and row, as a power of two (K % 256 == 0).
 template <int FMT>
 inline int mx_chunks_per_lane(int K) {
@@ -73,6 +96,25 @@ inline int mx_chunks_per_lane(int K) {
     int cpl = 1;
     while (cpl * kWave < cpr) cpl <<= 1;
     return cpl;
+}
+
+// Sum over the wave in a fixed order: DPP adds within each row of 16 lanes
+// (quad xor 1, quad xor 2, half-row mirror, row mirror: every lane then holds
+// its row's sum), then the four rows in lane order.
+template <int CTRL>
+__device__ __forceinline__ float mx_dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float mx_wave_sum(float v) {
+    v += mx_dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += mx_dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += mx_dpp<0x141>(v);  // row_half_mirror
+    v += mx_dpp<0x140>(v);  // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // fp32 dot product of one 16-byte chunk with its fp16 activation in LDS.
@@ -115,15 +157,15 @@ __device__ __forceinline__ float mx_chunk_dot(const mx_u32x4 &w, const uint8_t *
 }
 
 // One workgroup (kMxWaves waves) multiplies rows row_base .. row_base +
-// kMxWaves * R - 1 of W (clipped to N) with M tokens; token m's activation is
+// kMxWaves * R - 1 of W (clipped to N), R = mx_rows_per_wave(L, CPL), with M tokens; token m's activation is
 // row token_row(m) of qx / dx; out(m, row, value) stores a result.  Tokens are
 // staged mt at a time.  Every wave of the workgroup must call this.
-template <int FMT, int CPL, class TokenRow, class Out>
+template <int FMT, int CPL, int L, class TokenRow, class Out>
 __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int N, int K, int row_base, int M, int mt,
                                              const int8_t *__restrict__ qx, const float *__restrict__ dx,
                                              TokenRow token_row, Out out, uint8_t *smem) {
     using F = MxFmt<FMT>;
-    constexpr int R = mx_rows_per_wave(CPL);
+    constexpr int R = mx_rows_per_wave(L, CPL);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int cpr = K / F::weights_per_chunk;
     const size_t rb = F::row_bytes(K);
@@ -132,10 +174,87 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
     const int nb = K / 32;
     const int rec = mx_token_rec(K);
 
+    // tokens [m0, m0 + mtc) into LDS: int8 quants as fp16 block records, then the scales
+    const int pieces = K / 16;
+    auto put_piece = [&](int mm, int pc, const mx_u32x4 &q) __attribute__((always_inline)) {
+        const uint32_t Q[4] = {q.x, q.y, q.z, q.w};
+        uint32_t H[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t word = Q[k >> 1] >> (16 * (k & 1));
+            mx_half2 h;
+            h.x = (_Float16)(float)(int8_t)(word & 0xffu);
+            h.y = (_Float16)(float)(int8_t)((word >> 8) & 0xffu);
+            H[k] = __builtin_bit_cast(uint32_t, h);
+        }
+        uint8_t *dst = smem + (size_t)mm * rec + kMxBlockRec * (pc >> 1) + 32 * (pc & 1);
+        *reinterpret_cast<mx_u32x4 *>(dst) = mx_u32x4{H[0], H[1], H[2], H[3]};
+        *reinterpret_cast<mx_u32x4 *>(dst + 16) = mx_u32x4{H[4], H[5], H[6], H[7]};
+    };
+    auto piece_src = [&](int m0, int t) __attribute__((always_inline)) {
+        const int mm = t / pieces, pc = t - mm * pieces;
+        return reinterpret_cast<const mx_u32x4 *>(qx + (size_t)token_row(m0 + mm) * K + 16 * pc);
+    };
+    auto put_dx = [&](int m0, int t, float v) __attribute__((always_inline)) {
+        const int mm = t / nb, b = t - mm * nb;
+        reinterpret_cast<float *>(smem + (size_t)mm * rec + kMxBlockRec * nb)[b] = v;
+    };
+    auto dx_src = [&](int m0, int t) __attribute__((always_inline)) {
+        const int mm = t / nb, b = t - mm * nb;
+        return dx + (size_t)token_row(m0 + mm) * nb + b;
+    };
+    // staging after the first chunk of tokens: loads and stores together
+    auto stage = [&](int m0, int mtc, int from) {
+        for (int t = from + threadIdx.x; t < mtc * pieces; t += kMxThreads) {
+            const int mm = t / pieces;
+            put_piece(mm, t - mm * pieces, *piece_src(m0, t));
+        }
+        for (int t = from + threadIdx.x; t < mtc * nb; t += kMxThreads) put_dx(m0, t, *dx_src(m0, t));
+    };
+
+    // First chunk of tokens: its first kMxStageRegs pieces and scales per
+    // thread are requested before the weights, so that storing them waits
+    // for them alone and each row's weights are consumed as they arrive
+    // (loads return in order).  Indexes past the end re-read a valid element.
+    const int mt0 = min(mt, M);
+    // the workgroup's weight scales, one load per thread at most, requested
+    // first as well: FP4 the scales of its rows (contiguous; past the last
+    // row the load stays inside the padded buffer and is not used), FP8 the
+    // scale row of its 128-row block
+    uint8_t *lsc = smem + (size_t)mt * rec;
+    const size_t row_scale_bytes = FMT == QG_FMT_FP4_E2M1_MX ? (size_t)(K / 32) : 0;
+    const size_t scale_total = FMT == QG_FMT_FP4_E2M1_MX ? (size_t)N * (K / 32) : (size_t)((N + 127) / 128) * (K / 128);
+    const int scale_bytes = FMT == QG_FMT_FP4_E2M1_MX ? kMxWaves * R * (K / 32) : K / 128;
+    const uint8_t *scale_src = FMT == QG_FMT_FP4_E2M1_MX ? scales + (size_t)row_base * row_scale_bytes
+                                                          : scales + (size_t)(row_base >> 7) * (K / 128);
+    mx_u32x4 sreg = {0u, 0u, 0u, 0u};
+    uint32_t sbyte = 0;
+    // every thread loads and stores (threads past the end repeat the last
+    // piece: the same bytes to the same place), so that no load is moved
+    // into a conditional store behind the weights
+    const int lsc_off = FMT == QG_FMT_FP4_E2M1_MX ? min(16 * (int)threadIdx.x, scale_bytes - 16)
+                                                   : min((int)threadIdx.x, scale_bytes - 1);
+    if constexpr (FMT == QG_FMT_FP4_E2M1_MX) {
+        // 16-byte pieces; rows past N read the last piece that starts inside the scales
+        const size_t last = ((scale_total - 1) & ~(size_t)15) - (size_t)row_base * row_scale_bytes;
+        sreg = *reinterpret_cast<const mx_u32x4 *>(scale_src + min((size_t)lsc_off, last));
+    } else {
+        sbyte = scale_src[lsc_off];
+    }
+    mx_u32x4 qreg[kMxStageRegs];
+    float dreg[kMxStageRegs];
+#pragma unroll
+    for (int i = 0; i < kMxStageRegs; ++i) {
+        const int t = threadIdx.x + i * kMxThreads;
+        qreg[i] = *piece_src(0, min(t, mt0 * pieces - 1));
+        dreg[i] = *dx_src(0, min(t, mt0 * nb - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // these loads are issued before the weights
+
     // the wave's weight chunks and their scales (rows past N and chunks past
     // the row's end re-read the last ones and are not used)
     mx_u32x4 w[R][CPL];
-    int sc[R][CPL];
+
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int row = min(row0 + r, N - 1);
@@ -143,61 +262,63 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
         for (int j = 0; j < CPL; ++j) {
             const int c = min(lane + kWave * j, cpr - 1);
             w[r][j] = __builtin_nontemporal_load(reinterpret_cast<const mx_u32x4 *>(W + row * rb + 16 * (size_t)c));
-            sc[r][j] = (int)scales[F::scale_index(row, c, K)] - 127;
         }
     }
 
-    // tokens [m0, m0 + mtc) into LDS: int8 quants as fp16 block records, then the scales
-    auto stage = [&](int m0, int mtc) {
-        const int pieces = K / 16;
-        for (int t = threadIdx.x; t < mtc * pieces; t += blockDim.x) {
-            const int mm = t / pieces, pc = t - mm * pieces;
-            const mx_u32x4 q = *reinterpret_cast<const mx_u32x4 *>(qx + (size_t)token_row(m0 + mm) * K + 16 * pc);
-            const uint32_t Q[4] = {q.x, q.y, q.z, q.w};
-            uint32_t H[8];
+    // stored unconditionally (an index past the end stores the last element's
+    // value again at its own place): a conditional store would let the
+    // compiler move its load behind the weights
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FMT == QG_FMT_FP4_E2M1_MX)
+        *reinterpret_cast<mx_u32x4 *>(lsc + lsc_off) = sreg;
+    else
+        lsc[lsc_off] = (uint8_t)sbyte;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t word = Q[k >> 1] >> (16 * (k & 1));
-                mx_half2 h;
-                h.x = (_Float16)(float)(int8_t)(word & 0xffu);
-                h.y = (_Float16)(float)(int8_t)((word >> 8) & 0xffu);
-                H[k] = __builtin_bit_cast(uint32_t, h);
+    for (int i = 0; i < kMxStageRegs; ++i) {
+        const int tq = min((int)threadIdx.x + i * kMxThreads, mt0 * pieces - 1);
+        put_piece(tq / pieces, tq - (tq / pieces) * pieces, qreg[i]);
+        put_dx(0, min((int)threadIdx.x + i * kMxThreads, mt0 * nb - 1), dreg[i]);
+    }
+    stage(0, mt0, kMxStageRegs * kMxThreads);
+
+    // token mm of the chunk at m0 against every row of the wave
+    auto token = [&](int m0, int mm) __attribute__((always_inline)) {
+        const uint8_t *act = smem + (size_t)mm * rec;
+        const float *dxs = reinterpret_cast<const float *>(act + kMxBlockRec * nb);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float acc = 0.0f;
+            // row r's operands are used here, as they arrive: an empty asm that
+            // rewrites them keeps work on them inside the token loop (hoisted,
+            // it would wait for every load before the first row)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) asm volatile("" : "+v"(w[r][j]));
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = lane + kWave * j;
+                if (c < cpr) {
+                    const float p = mx_chunk_dot<FMT>(w[r][j], act + F::act_offset(c));
+                    const int e = (int)lsc[FMT == QG_FMT_FP4_E2M1_MX ? (wave * R + r) * (K / 32) + c : (c >> 3)] - 127;
+                    const float s = __builtin_ldexpf(dxs[F::act_block(c)], e);
+                    acc = fmaf_exact(p, s, acc);
+                }
             }
-            uint8_t *dst = smem + (size_t)mm * rec + kMxBlockRec * (pc >> 1) + 32 * (pc & 1);
-            *reinterpret_cast<mx_u32x4 *>(dst) = mx_u32x4{H[0], H[1], H[2], H[3]};
-            *reinterpret_cast<mx_u32x4 *>(dst + 16) = mx_u32x4{H[4], H[5], H[6], H[7]};
-        }
-        for (int t = threadIdx.x; t < mtc * nb; t += blockDim.x) {
-            const int mm = t / nb, b = t - mm * nb;
-            reinterpret_cast<float *>(smem + (size_t)mm * rec + kMxBlockRec * nb)[b] =
-                dx[(size_t)token_row(m0 + mm) * nb + b];
+            acc = mx_wave_sum(acc);
+            if (lane == 0 && row0 + r < N) out(m0 + mm, row0 + r, acc);
         }
     };
-
-    for (int m0 = 0; m0 < M; m0 += mt) {
+    // The first token runs outside any loop: in a loop that only reads
+    // registers loaded before it, every load would be waited for at its entry,
+    // while here row r waits for its own chunks only.
+    __syncthreads();
+    token(0, 0);
+    for (int mm = 1; mm < mt0; ++mm) token(0, mm);
+    for (int m0 = mt; m0 < M; m0 += mt) {
         const int mtc = min(mt, M - m0);
-        if (m0 > 0) __syncthreads();  // every wave is done with the previous tokens
-        stage(m0, mtc);
+        __syncthreads();  // every wave is done with the previous tokens
+        stage(m0, mtc, 0);
         __syncthreads();
-        for (int mm = 0; mm < mtc; ++mm) {
-            const uint8_t *act = smem + (size_t)mm * rec;
-            const float *dxs = reinterpret_cast<const float *>(act + kMxBlockRec * nb);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    const int c = lane + kWave * j;
-                    if (c < cpr) {
-                        const float p = mx_chunk_dot<FMT>(w[r][j], act + F::act_offset(c));
-                        const float s = __builtin_ldexpf(dxs[F::act_block(c)], sc[r][j]);
-                        acc = fmaf_exact(p, s, acc);
-                    }
-                }
-                for (int off = 1; off < kWave; off <<= 1) acc += shfl_xor(acc, off);
-                if (lane == 0 && row0 + r < N) out(m0 + mm, row0 + r, acc);
-            }
-        }
+        for (int mm = 0; mm < mtc; ++mm) token(m0, mm);
     }
 }
 

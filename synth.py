@@ -78,7 +78,8 @@ def q4k_weight(g: np.random.Generator, N: int, K: int, lo: float = 1e-4, hi: flo
 
 # FP8 E4M3 (128 x 128 block scales) and FP4 E2M1 (1 x 32 scales) expert
 # matrices, UE8M0 scales.  One buffer per matrix: the codes, then the scale
-# bytes from the next multiple of 256 bytes.
+# bytes from the next multiple of 256 bytes, then zeros up to a multiple of 16
+# bytes.
 FMT_FP8_B128 = 2
 FMT_FP4_MX = 3
 E4M3_NAN_CODES = (0x7F, 0xFF)
@@ -89,12 +90,14 @@ def _align256(x: int) -> int:
 
 
 def scaled_matrix_bytes(fmt: int, N: int, K: int) -> int:
-    """Bytes of an FP8 / FP4 matrix buffer: codes, padding to 256, scales."""
+    """Bytes of an FP8 / FP4 matrix buffer: codes, padding to 256, scales, padding to 16."""
     if fmt == FMT_FP8_B128:
-        return _align256(N * K) + (N + 127) // 128 * (K // 128)
-    if fmt == FMT_FP4_MX:
-        return _align256(N * K // 2) + N * (K // 32)
-    raise ValueError(fmt)
+        end = _align256(N * K) + (N + 127) // 128 * (K // 128)
+    elif fmt == FMT_FP4_MX:
+        end = _align256(N * K // 2) + N * (K // 32)
+    else:
+        raise ValueError(fmt)
+    return (end + 15) // 16 * 16
 
 
 def fp8_from_parts(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
@@ -103,7 +106,7 @@ def fp8_from_parts(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     assert scales.shape == ((N + 127) // 128, K // 128)
     buf = np.zeros(scaled_matrix_bytes(FMT_FP8_B128, N, K), np.uint8)
     buf[:N * K] = codes.reshape(-1)
-    buf[_align256(N * K):] = scales.reshape(-1)
+    buf[_align256(N * K):_align256(N * K) + scales.size] = scales.reshape(-1)
     return buf
 
 
@@ -115,7 +118,7 @@ def fp4_from_parts(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     assert scales.shape == (N, K // 32)
     buf = np.zeros(scaled_matrix_bytes(FMT_FP4_MX, N, K), np.uint8)
     buf[:N * half] = codes.reshape(-1)
-    buf[_align256(N * half):] = scales.reshape(-1)
+    buf[_align256(N * half):_align256(N * half) + scales.size] = scales.reshape(-1)
     return buf
 
 
@@ -214,5 +217,8 @@ WORKLOADS = {
     # the ATOM expert formats on the routed path, one token: FP8 E4M3 with
     # 128 x 128 block scales over 256 experts, FP4 E2M1 with 1 x 32 scales over 384
     "moe_fp8_e256_t1": dict(E=256, D=4096, F=2048, topk=6, T=1, ids="uniform", fmt=FMT_FP8_B128, seed=6),
+    # the same formats as dense 4096 -> 16384 mat-vecs, batch 1
+    "fp8_16384x4096": dict(fmt=FMT_FP8_B128, N=16384, K=4096, M=1, seed=8),
+    "fp4_16384x4096": dict(fmt=FMT_FP4_MX, N=16384, K=4096, M=1, seed=9),
     "moe_fp4_e384_t1": dict(E=384, D=4096, F=2048, topk=6, T=1, ids="uniform", fmt=FMT_FP4_MX, seed=7),
 }
