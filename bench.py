@@ -21,7 +21,7 @@ MoE tokens/s, prefill) measured the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --summarize-rocprof DIR   (turn rocprofv3 csv output into a text summary)
-       python bench.py --probe {gemv,gemv_batch,copy,prefill,prefill_ws,fp8_16384x4096,fp4_16384x4096,
+       python bench.py --probe {gemv,gemv_batch,copy,prefill,prefill_ws,prefill_q8_0,fp8_16384x4096,fp4_16384x4096,
                                  moe_e256_t1,moe_fp8_e256_t1,moe_fp4_e384_t1,...} --steps K
                  (eager launches of one kernel, for rocprofv3 --pmc counter runs)
        python bench.py --summarize-pmc GEMV_FETCH GEMV_WRITE COPY_FETCH COPY_WRITE
@@ -44,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16, published
+MFMA_INT8_PEAK_TOPS = 5000.0    # MI355X dense int8, published
 ROTATE_BYTES = 1 << 30  # > 2x the 256 MB Infinity Cache
 METRIC = "decode GEMV µs and achieved HBM GB/s (% of peak); routed-MoE tokens/s"
 
@@ -376,6 +377,32 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
         w = synth.WORKLOADS[key]
         gemv_rate(w["fmt"], synth.weight(w["fmt"], synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], [1], key)
     prefill_rate()
+    # the Q8_0 prefill product on int8 MFMA, with its activation quantization
+    w = synth.WORKLOADS["q8_0_prefill_512x8192x4096"]
+    gp = synth.rng(w["seed"])
+    N, K, M = w["N"], w["K"], w["M"]
+    W_host = synth.q8_0_weight(gp, N, K)
+    R = rotation_count(W_host.nbytes)
+    base = torch.from_numpy(W_host).to(dev)
+    copies = [base] + [base.clone() for _ in range(R - 1)]
+    xp = torch.from_numpy(synth.activations(gp, M, K)).to(dev)
+    qx, dx, sx = (torch.empty(M, K, dtype=torch.int8, device=dev), torch.empty(M, K // 32, dtype=torch.float32,
+                  device=dev), torch.empty(M, K // 32, dtype=torch.int32, device=dev))
+    yp = torch.empty(M, N, dtype=torch.float32, device=dev)
+
+    def q8_prefill(i):
+        qg.quantize_act_q8(xp, M, K, qx, dx, sx)
+        qg.qgemm_q8_0(copies[i % R], N, K, qx, dx, M, yp)
+    gr = capture(q8_prefill, R, stream)
+    timer.run(gr.replay)
+    sec = timer.run(gr.replay) / R
+    ops = 2.0 * M * N * K
+    out["prefill_q8_0_512x8192x4096"] = {
+        "us": round(sec * 1e6, 3), "TOP_s": round(ops / sec / 1e12, 1),
+        "mfma_frac": round(ops / sec / 1e12 / MFMA_INT8_PEAK_TOPS, 4),
+        "includes": "quantize_act_q8 of the 512 tokens + qgemm_q8_0 (int8 MFMA; rows equal the decode call)"}
+    del gr, copies, base
+    torch.cuda.empty_cache()
     moe_rate("moe_e256_t1", 16)
     moe_rate("moe_e256_t8", 16)
     moe_rate("moe_e384_t64_zipf", 4)
@@ -469,6 +496,23 @@ def run_probe(name: str, steps: int, warmup: int, qg, torch) -> None:
 
         def fn(i):
             qg.qgemv_mx(fmt, copies[i % R], N, K, qx, dx, 1, y)
+    elif name == "prefill_q8_0":
+        w = synth.WORKLOADS["q8_0_prefill_512x8192x4096"]
+        g = synth.rng(w["seed"])
+        N, K, M = w["N"], w["K"], w["M"]
+        W_host = synth.q8_0_weight(g, N, K)
+        R = rotation_count(W_host.nbytes)
+        base = torch.from_numpy(W_host).to("cuda")
+        copies = [base] + [base.clone() for _ in range(R - 1)]
+        x = torch.from_numpy(synth.activations(g, M, K)).to("cuda")
+        qx = torch.empty(M, K, dtype=torch.int8, device="cuda")
+        dx = torch.empty(M, K // 32, dtype=torch.float32, device="cuda")
+        sx = torch.empty(M, K // 32, dtype=torch.int32, device="cuda")
+        qg.quantize_act_q8(x, M, K, qx, dx, sx)
+        y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+
+        def fn(i):
+            qg.qgemm_q8_0(copies[i % R], N, K, qx, dx, M, y)
     elif name == "copy":
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -119,6 +119,7 @@ extern "C" {
 /* limits */
 #define QG_MAX_K 16384        /* largest K (inputs) of a projection */
 #define QG_MAX_M 32           /* largest token batch of qgemv_* */
+#define QG_MAX_PREFILL_M 65536 /* largest token count of qgemm_q8_0 */
 #define QG_MAX_MOE_PAIRS 8192 /* largest T * topk of moe_routed_qgemv */
 #define QG_MAX_EXPERTS 4096   /* largest E of moe_routed_qgemv */
 
@@ -222,6 +223,21 @@ int qgemv_q4k_f32(const void *W, int N, int K, const float *x, int M, float *y, 
                   void *stream);
 int qgemv_paired_f32(int fmt, const void *W1, int N1, const void *W2, int N2, int K, const float *x, int M, float *y1,
                      float *y2, int8_t *qx, float *dx, int32_t *sx, void *stream);
+
+/*
+ * qgemm_q8_0 -- the Q8_0 projection over a prefill-sized batch on the matrix
+ * cores ([PR623]: the Q8_0 projections on a prequantized activation; [PR621]:
+ * prefill takes the batched path): the same product and the same arithmetic
+ * as qgemv_q8_0, for M up to QG_MAX_PREFILL_M tokens, so row m equals the
+ * one-token qgemv_q8_0 call on token m bit for bit.  Each 32-block's integer
+ * sums come from int8 MFMA (v_mfma_i32_32x32x32_i8), 32 rows x 32 tokens at a
+ * time.
+ * W: QG_FMT_Q8_0 [N, K]; qx/dx: Q8 activation [M, K] (quantize_act_q8);
+ * y fp32 [M, N].
+ * Errors: QG_ERR_NULL; QG_ERR_SHAPE unless N >= 1, 1 <= M <= QG_MAX_PREFILL_M,
+ * K % 256 == 0, 256 <= K <= QG_MAX_K; QG_ERR_ALIGN; QG_ERR_LAUNCH.
+ */
+int qgemm_q8_0(const void *W, int N, int K, const int8_t *qx, const float *dx, int M, float *y, void *stream);
 
 /* ---- block-scaled expert formats -------------------------------------- */
 /*

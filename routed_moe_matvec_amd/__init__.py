@@ -20,7 +20,7 @@ __all__ = [
     "qgemm_prefill", "qg_status_string", "qgemv_debug_block_isums", "pointer_table", "WS_REGIONS",
     "qgemv_q8_0_f32", "qgemv_q4k_f32", "qgemv_paired_f32", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
     "qgemv_grouped", "qgemv_q8_0_quality", "FMT_FP8_E4M3_B128", "FMT_FP4_E2M1_MX", "qg_matrix_bytes", "qgemv_mx",
-    "moe_routed_qgemv_fmt",
+    "moe_routed_qgemv_fmt", "qgemm_q8_0",
 ]
 
 FMT_Q8_0 = 0
@@ -72,6 +72,7 @@ _c_moe_fmt = _sig("moe_routed_qgemv_fmt", _i, [_i, _vp, _vp, _vp, _i, _i, _i, _i
                                               _vp, _sz, _vp, _vp])
 _c_matrix_bytes = _sig("qg_matrix_bytes", _sz, [_i, _i, _i])
 _c_mx = _sig("qgemv_mx", _i, [_i, _vp, _i, _i, _vp, _vp, _i, _vp, _vp])
+_c_qgemm_q8_0 = _sig("qgemm_q8_0", _i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp])
 _c_prefill = _sig("qgemm_prefill", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
 _c_prefill_ws_bytes = _sig("qgemm_prefill_workspace_bytes", _sz, [_i, _i])
 _c_prefill_ws = _sig("qgemm_prefill_ws", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp, _sz, _vp])
@@ -193,6 +194,10 @@ def moe_routed_qgemv_fmt(fmt: int, qx, dx, sx, T: int, D: int, F: int, E: int, t
 
 def qg_matrix_bytes(fmt: int, N: int, K: int) -> int:
     return int(_c_matrix_bytes(fmt, N, K))
+
+
+def qgemm_q8_0(W, N: int, K: int, qx, dx, M: int, y, stream=None) -> None:
+    _ok(_c_qgemm_q8_0(_ptr(W), N, K, _ptr(qx), _ptr(dx), M, _ptr(y), _stream(stream, W)), "qgemm_q8_0")
 
 
 def qgemv_mx(fmt: int, W, N: int, K: int, qx, dx, M: int, y, stream=None) -> None:

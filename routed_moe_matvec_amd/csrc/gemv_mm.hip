@@ -15,6 +15,10 @@
 //     power of two of units (the one-token engine's xor butterfly, padded
 //     with zeros).
 //
+// Token tiles: a workgroup takes 32 tokens; larger batches (the prefill
+// product qgemm_q8_0) run one workgroup per (row tile, token tile), the token
+// tiles of a row tile next to each other in the launch order.
+//
 // Work split: a workgroup owns 32 rows of one matrix; its KS waves take
 // consecutive, power-of-two-aligned slices of the row's 256-weight groups, so
 // each slice is a subtree of the unit tree.  A wave streams its 32 rows'
@@ -39,6 +43,7 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr int kMmRows = 32;                             // weight rows of a workgroup
+constexpr int kMmTokens = 32;                           // tokens of a workgroup
 constexpr int kMmParts = 17;                            // 16-byte parts of a row's 272-byte group
 constexpr int kMmStageBytes = kMmParts * kMmRows * 16;  // one group of 32 rows: [part][row] x 16 B
 constexpr int kMmScaleBytes = 8 * kMmRows * 2;          // fp16 scales of a group: [block][lane half][16]
@@ -53,7 +58,8 @@ struct MmArgs {
     const uint8_t *W0, *W1;
     float *y0, *y1;
     int N0, N1;
-    int nt0;  // workgroups (32-row tiles) of matrix 0; matrix 1's follow
+    int nt0;  // 32-row tiles of matrix 0; matrix 1's follow
+    int ntok; // 32-token tiles: workgroup x takes row tile x / ntok, token tile x % ntok
     const int8_t *qx;
     const float *dx;
     int K, M, G;
@@ -68,8 +74,13 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // the wave index is uniform over the wave: keep it (and every slice bound) scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const bool second = (int)blockIdx.x >= a.nt0;
-    const int tile = second ? (int)blockIdx.x - a.nt0 : (int)blockIdx.x;
+    // token tiles of one row tile are neighbours in the launch order, so the
+    // row tile's weights are still in the caches when the next token tile
+    // reads them
+    const int rtile = (int)blockIdx.x / a.ntok;
+    const int m0 = ((int)blockIdx.x - rtile * a.ntok) * kMmTokens;
+    const bool second = rtile >= a.nt0;
+    const int tile = second ? rtile - a.nt0 : rtile;
     const int N = second ? a.N1 : a.N0;
     const int g = blockIdx.y;  // grouped call: matrix g against activation slice g
     const uint8_t *W = (second ? a.W1 : a.W0) + (size_t)g * N * a.row_bytes;
@@ -93,7 +104,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
     // activation: token lane % 32 (tokens past M re-read token M - 1; their
     // columns are not stored), 16 quants of each block per lane half
     const int half = lane >> 5;
-    const size_t arow = (size_t)min(r32, a.M - 1) * a.G + g;
+    const size_t arow = (size_t)min(m0 + r32, a.M - 1) * a.G + g;
     const int8_t *xp = a.qx + arow * a.K + 16 * half;
     const float *dp = a.dx + arow * (a.K / 32);
 
@@ -343,7 +354,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
             for (int s = 0; s + w < kMmMaxSlices; s += 2 * w)
                 if (s + w < KS) v[s] = v[s] + v[s + w];
         const int e = idx >> 6, l = idx & 63;
-        const int token = l & 31;
+        const int token = m0 + (l & 31);
         const int row = row0 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
         if (token < a.M && row < N) y[((size_t)token * a.G + g) * N + row] = v[0];
     }
@@ -358,7 +369,7 @@ static int launch_mm_gps(const MmArgs &a, int nt1, hipStream_t stream) {
             return QG_ERR_LAUNCH;
         attr_set = true;
     }
-    hipLaunchKernelGGL((qgemv_mm_q8_0_kernel<NB, GPS>), dim3(a.nt0 + nt1, a.G), dim3(a.KS * kWave),
+    hipLaunchKernelGGL((qgemv_mm_q8_0_kernel<NB, GPS>), dim3((a.nt0 + nt1) * a.ntok, a.G), dim3(a.KS * kWave),
                        (size_t)a.KS * mm_wave_lds(GPS), stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
@@ -373,7 +384,8 @@ static int launch_mm(MmArgs &a, hipStream_t stream) {
     while (gpow2 < a.groups) gpow2 <<= 1;
     const int nt1 = a.W1 ? (a.N1 + kMmRows - 1) / kMmRows : 0;
     a.nt0 = (a.N0 + kMmRows - 1) / kMmRows;
-    const long tiles = (long)(a.nt0 + nt1) * a.G;
+    a.ntok = (a.M + kMmTokens - 1) / kMmTokens;
+    const long tiles = (long)(a.nt0 + nt1) * a.G * a.ntok;
     int ks = gpow2 > kMmMaxGroups ? gpow2 / kMmMaxGroups : 1;
     const int ks_max = gpow2 < kMmMaxSlices ? gpow2 : kMmMaxSlices;
     while (ks < ks_max && tiles * ks < kMmTargetWaves) ks <<= 1;
@@ -408,3 +420,13 @@ int gemv_mm_q8_0(const uint8_t *W0, int N0, float *y0, const uint8_t *W1, int N1
 }
 
 }  // namespace qg
+
+extern "C" int qgemm_q8_0(const void *W, int N, int K, const int8_t *qx, const float *dx, int M, float *y,
+                          void *stream) {
+    if (!W || !qx || !dx || !y) return QG_ERR_NULL;
+    if (N < 1 || M < 1 || M > QG_MAX_PREFILL_M) return QG_ERR_SHAPE;
+    if (K < qg::kGroupWeights || K > QG_MAX_K || K % qg::kGroupWeights != 0) return QG_ERR_SHAPE;
+    if (((uintptr_t)W | (uintptr_t)qx | (uintptr_t)dx | (uintptr_t)y) & 15) return QG_ERR_ALIGN;
+    return qg::gemv_mm_q8_0(reinterpret_cast<const uint8_t *>(W), N, y, nullptr, 0, nullptr, K, qx, dx, M, 1,
+                            (hipStream_t)stream);
+}

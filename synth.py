@@ -205,6 +205,8 @@ WORKLOADS = {
     # Q4_K dense projection 4096 -> 8192, batch 1 and prefill batch 512
     "q4k_8192x4096": dict(fmt="q4k", N=8192, K=4096, M=1, seed=2),
     "q4k_prefill_512x8192x4096": dict(fmt="q4k", N=8192, K=4096, M=512, seed=2),
+    # the Q8_0 prefill product on the matrix cores: 512 tokens through 4096 -> 8192
+    "q8_0_prefill_512x8192x4096": dict(fmt="q8_0", N=8192, K=4096, M=512, seed=10),
     # grouped low-rank attention output: 8 groups of 1024 x 4096 on their own input slices
     "q8_0_grouped_8x1024x4096": dict(fmt="q8_0", G=8, N=1024, K=4096, M=1, seed=5),
     # routed MoE, 256 experts, top-6, D=4096, F=2048, T=1 and T=8

@@ -417,3 +417,53 @@ def test_grouped_errors(qg):
     assert c(0, W.data_ptr() + 4, 2, 8, 512, qx.data_ptr(), dx.data_ptr(), None, 1, y.data_ptr(), None) == -3
     torch.cuda.synchronize()
     assert np.all(host(y) == 1.0)
+
+
+# ---------------------------------------------------------------- Q8_0 prefill on the matrix cores
+
+PREFILL_Q8_0_CASES = [
+    # N, K, M: ragged token tiles and row tiles, partial K slices, the 8-block
+    # unit, a prefill-sized batch (sampled outputs)
+    (100, 1280, 77),
+    (333, 2048, 100),
+    (64, 16384, 65),
+    (1024, 4096, 512),
+]
+
+
+@pytest.mark.parametrize("N,K,M", PREFILL_Q8_0_CASES)
+def test_qgemm_q8_0_parity_and_rows_equal_decode(qg, orc, N, K, M):
+    """The prefill-sized Q8_0 product: sampled outputs match the oracle, and sampled token
+    rows equal the one-token decode call on that token bit for bit."""
+    import torch
+    progress("qgemm_q8_0 N=%d K=%d M=%d" % (N, K, M))
+    g = np.random.default_rng(6000 + N + K + M)
+    W = synth.q8_0_weight(g, N, K)
+    Wd = dev(W)
+    qx, dx, _ = orc.quantize_act_q8(synth.activations(g, M, K))
+    qxd, dxd = dev(qx), dev(dx)
+    y = sentinel((M, N), torch.float32, 7.0)
+    qg.qgemm_q8_0(Wd, N, K, qxd, dxd, M, y)
+    yh = host(y)
+    toks = np.unique(np.concatenate([[0, M - 1, M // 2], g.choice(M, min(M, 12), replace=False)]))
+    rows = np.arange(N) if N <= 400 else np.sort(g.choice(N, 128, replace=False))
+    ref, bound = orc.gemv(0, W[rows], len(rows), K, qx[toks], dx[toks], nthreads=oracle_threads())
+    assert_within_bound(yh[np.ix_(toks, rows)], ref, bound, what="qgemm_q8_0 N=%d K=%d M=%d" % (N, K, M))
+    for t in toks:
+        one = _run_gemv(qg, 0, Wd, N, K, qxd[t:t + 1], dxd[t:t + 1], None, 1)
+        assert np.array_equal(yh[t].view(np.uint32), one[0].view(np.uint32)), "token %d" % t
+
+
+def test_qgemm_q8_0_errors(qg):
+    import torch
+    W = dev(synth.q8_0_weight(np.random.default_rng(2), 8, 512))
+    qx = dev(np.zeros((40, 512), np.int8))
+    dx = dev(np.ones((40, 16), np.float32))
+    y = sentinel((40, 8), torch.float32, 3.0)
+    c = qg._c_qgemm_q8_0
+    assert c(W.data_ptr(), 8, 512, qx.data_ptr(), dx.data_ptr(), 0, y.data_ptr(), None) == -2
+    assert c(W.data_ptr(), 8, 500, qx.data_ptr(), dx.data_ptr(), 40, y.data_ptr(), None) == -2
+    assert c(None, 8, 512, qx.data_ptr(), dx.data_ptr(), 40, y.data_ptr(), None) == -1
+    assert c(W.data_ptr() + 2, 8, 512, qx.data_ptr(), dx.data_ptr(), 40, y.data_ptr(), None) == -3
+    torch.cuda.synchronize()
+    assert np.all(host(y) == 3.0)

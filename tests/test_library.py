@@ -140,3 +140,9 @@ def test_mx_host_validation_without_gpu(lib):
              fake, None) == -2
     assert m(2, fake, fake, fake, 1, 4096, 2048, 256, 6, fake, fake, fake, fake, fake, fake, fake, 16,
              fake, None) == -5
+    q = lib.qgemm_q8_0
+    q.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp]
+    assert q(fake, 8, 512, fake, fake, 0, fake, None) == -2
+    assert q(fake, 8, 512, fake, fake, 65537, fake, None) == -2
+    assert q(fake, 8, 384 + 1, fake, fake, 64, fake, None) == -2
+    assert q(fake, 8, 512, None, fake, 64, fake, None) == -1
