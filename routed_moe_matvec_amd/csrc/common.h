@@ -56,6 +56,24 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// A pointer into device (global) memory.  Loads through a pointer that was
+// itself read from memory (the routed experts' matrices) are otherwise
+// generic "flat" loads, which also count against the LDS wait counter: every
+// LDS wait would then wait for the weights in flight as well.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *as_global(const void *p) {
+    return (const __attribute__((address_space(1))) T *)p;
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every global load and store of the wave to complete; here the
+// caller's global loads (weights in flight) and stores stay outstanding.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <class T>
 __device__ __forceinline__ T shfl_xor(T v, int mask) {
     return __shfl_xor(v, mask, kWave);

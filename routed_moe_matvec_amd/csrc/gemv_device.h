@@ -245,39 +245,74 @@ struct ActStage {
     u32x4 q[kActRegChunks];
     u32x4 d, s;
 
+    // Chunk c of the token chunk's quants (16 bytes; c < mtc * K / 16).
     template <class TokenRow>
-    __device__ __forceinline__ void load_quants(const int8_t *__restrict__ qx, int K, int m0, int mtc, int base,
-                                                TokenRow token_row) {
-        const int NT = blockDim.x;
+    __device__ __forceinline__ const u32x4 *quant_src(const int8_t *__restrict__ qx, int K, int m0, int c,
+                                                      TokenRow token_row) {
         const int cpt = K / 16;
-#pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k) {
-            const int c = base + (int)threadIdx.x + k * NT;
-            if (c < mtc * cpt) {
-                const int mm = c / cpt;
-                q[k] = reinterpret_cast<const u32x4 *>(qx + (size_t)token_row(m0 + mm) * K)[c - mm * cpt];
-            }
-        }
+        const int mm = c / cpt;
+        return reinterpret_cast<const u32x4 *>(qx + (size_t)token_row(m0 + mm) * K) + (c - mm * cpt);
     }
-
+    __device__ __forceinline__ uint8_t *quant_dst(uint8_t *lds, int K, int c) {
+        constexpr int QC = U::weights / 16;  // 16-byte chunks of quants per unit
+        const int cpt = K / 16, upr = K / U::weights;
+        const int mm = c / cpt;
+        const int w = c - mm * cpt;
+        const int u = w / QC;
+        return lds + (size_t)(mm * upr + u) * REC + (w - u * QC) * 16;
+    }
+    // Chunk c of the scales (and block sums) of 4 blocks (c < mtc * K / 128).
     template <class TokenRow>
-    __device__ __forceinline__ void load_scales(const float *__restrict__ dx, const int32_t *__restrict__ sx, int K,
-                                                int m0, int mtc, int base, TokenRow token_row) {
+    __device__ __forceinline__ size_t scale_src(int K, int m0, int c, TokenRow token_row) {
         const int spt = K / 128;
-        const int c = base + (int)threadIdx.x;
-        if (c < mtc * spt) {
-            const int mm = c / spt;
-            const size_t src = (size_t)token_row(m0 + mm) * (K / 32) / 4 + (c - mm * spt);
-            d = reinterpret_cast<const u32x4 *>(dx)[src];
-            if constexpr (FMT == QG_FMT_Q4K) s = reinterpret_cast<const u32x4 *>(sx)[src];
-        }
+        const int mm = c / spt;
+        return (size_t)token_row(m0 + mm) * (K / 32) / 4 + (c - mm * spt);
+    }
+    __device__ __forceinline__ uint8_t *scale_dst(uint8_t *lds, int K, int c) {
+        constexpr int SC = U::blocks / 4;  // 16-byte chunks of scales per unit
+        const int spt = K / 128, upr = K / U::weights;
+        const int mm = c / spt;
+        const int w = c - mm * spt;
+        const int u = w / SC;
+        return lds + (size_t)(mm * upr + u) * REC + U::weights + (w - u * SC) * 16;
     }
 
+    // load() reads the first pass (the registers) and store() writes it,
+    // both unconditionally and outside any loop: a thread past the end takes
+    // one of the last 64 chunks instead (each lane a different one, so the
+    // duplicate writes, of identical bytes to the same place, do not pile on
+    // one LDS address).  The waits for the registers then count only the loads
+    // issued after them; a conditional load, or a first pass inside the pass
+    // loop, would make them wait for the caller's weight loads as well.
+    __device__ __forceinline__ static int clamp_chunk(int c, int total) {
+        return c < total ? c : max(total - kWave + lane_id(), 0);
+    }
     template <class TokenRow>
     __device__ __forceinline__ void load(const int8_t *__restrict__ qx, const float *__restrict__ dx,
                                          const int32_t *__restrict__ sx, int K, int m0, int mtc, TokenRow token_row) {
-        load_quants(qx, K, m0, mtc, 0, token_row);
-        load_scales(dx, sx, K, m0, mtc, 0, token_row);
+        const int NT = blockDim.x;
+        const int qtotal = mtc * (K / 16), stotal = mtc * (K / 128);
+        const int cpt = K / 16, spt = K / 128;
+        // the token rows first (a gathered token list costs one round trip
+        // for all of them), then the activation reads
+        // (index kActRegChunks: the scales' token)
+        int c[kActRegChunks + 1], mm[kActRegChunks + 1];
+        size_t row[kActRegChunks + 1];
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k) {
+            c[k] = clamp_chunk((int)threadIdx.x + k * NT, qtotal);
+            mm[k] = c[k] / cpt;
+        }
+        c[kActRegChunks] = clamp_chunk((int)threadIdx.x, stotal);
+        mm[kActRegChunks] = c[kActRegChunks] / spt;
+#pragma unroll
+        for (int k = 0; k <= kActRegChunks; ++k) row[k] = (size_t)token_row(m0 + mm[k]);
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k)
+            q[k] = reinterpret_cast<const u32x4 *>(qx + row[k] * K)[c[k] - mm[k] * cpt];
+        const size_t src = row[kActRegChunks] * (K / 32) / 4 + (c[kActRegChunks] - mm[kActRegChunks] * spt);
+        d = reinterpret_cast<const u32x4 *>(dx)[src];
+        if constexpr (FMT == QG_FMT_Q4K) s = reinterpret_cast<const u32x4 *>(sx)[src];
     }
 
     template <class TokenRow>
@@ -285,35 +320,33 @@ struct ActStage {
                                           const int32_t *__restrict__ sx, int K, int m0, int mtc,
                                           TokenRow token_row) {
         const int NT = blockDim.x;
-        constexpr int QC = U::weights / 16;  // 16-byte chunks of quants per unit
-        constexpr int SC = U::blocks / 4;    // 16-byte chunks of scales per unit
-        const int upr = K / U::weights;
-        const int cpt = K / 16;
-        for (int base = 0; base < mtc * cpt; base += kActRegChunks * NT) {
-            if (base > 0) load_quants(qx, K, m0, mtc, base, token_row);
+        const int qtotal = mtc * (K / 16), stotal = mtc * (K / 128);
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k)
+            *reinterpret_cast<u32x4 *>(quant_dst(lds, K, clamp_chunk((int)threadIdx.x + k * NT, qtotal))) = q[k];
+        {
+            uint8_t *rec = scale_dst(lds, K, clamp_chunk((int)threadIdx.x, stotal));
+            *reinterpret_cast<u32x4 *>(rec) = d;
+            if constexpr (FMT == QG_FMT_Q4K) *reinterpret_cast<u32x4 *>(rec + 32) = s;
+        }
+        // further passes (chunks that did not fit the registers)
+        for (int base = kActRegChunks * NT; base < qtotal; base += kActRegChunks * NT) {
 #pragma unroll
             for (int k = 0; k < kActRegChunks; ++k) {
                 const int c = base + (int)threadIdx.x + k * NT;
-                if (c < mtc * cpt) {
-                    const int mm = c / cpt;
-                    const int w = c - mm * cpt;
-                    const int u = w / QC;
-                    *reinterpret_cast<u32x4 *>(lds + (size_t)(mm * upr + u) * REC + (w - u * QC) * 16) = q[k];
-                }
+                if (c < qtotal) q[k] = *quant_src(qx, K, m0, c, token_row);
+            }
+#pragma unroll
+            for (int k = 0; k < kActRegChunks; ++k) {
+                const int c = base + (int)threadIdx.x + k * NT;
+                if (c < qtotal) *reinterpret_cast<u32x4 *>(quant_dst(lds, K, c)) = q[k];
             }
         }
-        const int spt = K / 128;
-        for (int base = 0; base < mtc * spt; base += NT) {
-            if (base > 0) load_scales(dx, sx, K, m0, mtc, base, token_row);
-            const int c = base + (int)threadIdx.x;
-            if (c < mtc * spt) {
-                const int mm = c / spt;
-                const int w = c - mm * spt;
-                const int u = w / SC;
-                uint8_t *rec = lds + (size_t)(mm * upr + u) * REC + U::weights + (w - u * SC) * 16;
-                *reinterpret_cast<u32x4 *>(rec) = d;
-                if constexpr (FMT == QG_FMT_Q4K) *reinterpret_cast<u32x4 *>(rec + 32) = s;
-            }
+        for (int c = NT + (int)threadIdx.x; c < stotal; c += NT) {
+            const size_t src = scale_src(K, m0, c, token_row);
+            uint8_t *rec = scale_dst(lds, K, c);
+            *reinterpret_cast<u32x4 *>(rec) = reinterpret_cast<const u32x4 *>(dx)[src];
+            if constexpr (FMT == QG_FMT_Q4K) *reinterpret_cast<u32x4 *>(rec + 32) = reinterpret_cast<const u32x4 *>(sx)[src];
         }
     }
 };
@@ -461,7 +494,7 @@ __device__ __forceinline__ void load_tile(const uint8_t *__restrict__ W, int N, 
     const int row0 = tile * tg.rpt;
     const int nrows = min(tg.rpt, N - row0);
     const int last = nrows * tg.row_bytes / 16 - 1;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(W + (size_t)row0 * tg.row_bytes);
+    const auto *src = as_global<u32x4>(W + (size_t)row0 * tg.row_bytes);
 #pragma unroll
     for (int i = 0; i < TileSize<U>::instr; ++i) {
         const int c = min(i * kWave + lane, last);
@@ -547,11 +580,14 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
         if (ONE) M = 1;
         // one chunk of tokens: activation reads first, then up to two tiles in
         // flight; tpw tiles in total
+        // (the first tiles are read unconditionally, clamped to the last tile,
+        // so the staging waits count them exactly; see ActStage)
         act_load(0, M);
-        if (tile0 < ntiles) load_tile<U>(W, N, tg, tile0, ra);
-        if (PIPE && tpw > 1 && tile0 + 1 < ntiles) load_tile<U>(W, N, tg, tile0 + 1, rb);
+        load_tile<U>(W, N, tg, min(tile0, ntiles - 1), ra);
+        if (PIPE) load_tile<U>(W, N, tg, min(tile0 + 1, ntiles - 1), rb);
+        __builtin_amdgcn_sched_barrier(0);  // every load is issued before the first wait
         act_store(0, M);
-        __syncthreads();
+        lds_barrier();
         for (int i = 0; i < tpw; i += 2) {
             const int ta = tile0 + i, tb = tile0 + i + 1;
             if (ta < ntiles) {
@@ -568,17 +604,25 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
             }
         }
     } else if (!ONE) {
-        // several chunks of tokens: one tile, kept in registers across chunks
+        // several chunks of tokens: one tile, kept in registers across chunks;
+        // the next chunk's activation is read into the staging registers while
+        // the current chunk is multiplied
         const bool v = unit_valid(tile0);
+        act_load(0, min(mt, M));
+        load_tile<U>(W, N, tg, min(tile0, ntiles - 1), ra);
+        __builtin_amdgcn_sched_barrier(0);
+        act_store(0, min(mt, M));
+        lds_barrier();
+        if (tile0 < ntiles) tile_to_unit<U>(ra, lw, r * tg.upr + g, v, u);
         for (int m0 = 0; m0 < M; m0 += mt) {
-            const int mtc = min(mt, M - m0);
-            if (m0 > 0) __syncthreads();  // every wave is done with the previous chunk
-            act_load(m0, mtc);
-            if (m0 == 0 && tile0 < ntiles) load_tile<U>(W, N, tg, tile0, ra);
-            act_store(m0, mtc);
-            __syncthreads();
-            if (m0 == 0 && tile0 < ntiles) tile_to_unit<U>(ra, lw, r * tg.upr + g, v, u);
-            if (tile0 < ntiles) compute(u, tile0, v, m0, mtc);
+            const int n0 = m0 + mt;
+            if (n0 < M) act_load(n0, min(mt, M - n0));
+            if (tile0 < ntiles) compute(u, tile0, v, m0, min(mt, M - m0));
+            if (n0 < M) {
+                lds_barrier();  // every wave is done with this chunk
+                act_store(n0, min(mt, M - n0));
+                lds_barrier();
+            }
         }
     }
 }

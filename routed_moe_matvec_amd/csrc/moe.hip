@@ -97,36 +97,68 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
     return incl - v;
 }
 
-// One wave.  bm: bitmap of the selected usable experts; wpre[w]: number of set
-// bits in words below w, so rank(e) = wpre[e/32] + popcount of the bits of
-// word e/32 below e.
+// One wave.  sid: the ids, staged once (every later pass reads LDS, so the
+// pair loops wait for no global load); bm: bitmap of the selected usable
+// experts; wpre[w]: number of set bits in words below w, so rank(e) =
+// wpre[e/32] + popcount of the bits of word e/32 below e.
 __global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restrict__ ids, int P, int E,
                                                          const void *const *gate, const void *const *up,
                                                          const void *const *down, MoeWs ws, int32_t *status) {
     __shared__ uint32_t bm[kTableWords];
     __shared__ int wpre[kTableWords];
     __shared__ int cur[QG_MAX_EXPERTS];  // pairs per distinct expert, then the next free position
+    __shared__ int sid[QG_MAX_MOE_PAIRS];
+    constexpr int kBatch = 8;  // independent global loads in flight per lane
     const int l = threadIdx.x;
-    if (l == 0) atomicExch(status, QG_DEV_OK);
     for (int w = l; w < kTableWords; w += kWave) bm[w] = 0u;
-    __syncthreads();
+    for (int p0 = 0; p0 < P; p0 += kBatch * kWave) {
+        int v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) v[i] = ids[min(p0 + i * kWave + l, P - 1)];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (p0 + i * kWave + l < P) sid[p0 + i * kWave + l] = v[i];
+    }
+    lds_barrier();
+    bool bad_id = false;
     for (int p = l; p < P; p += kWave) {
-        const int e = ids[p];
+        const int e = sid[p];
         if (e < 0 || e >= E)
-            atomicCAS(status, QG_DEV_OK, QG_DEV_BAD_EXPERT);
+            bad_id = true;
         else
             atomicOr(&bm[e >> 5], 1u << (e & 31));
     }
-    __syncthreads();
-    // experts with a NULL or misaligned matrix are dropped (checked once per pair)
-    for (int p = l; p < P; p += kWave) {
-        const int e = ids[p];
-        if (e >= 0 && e < E && (bad_pointer(gate[e]) || bad_pointer(up[e]) || bad_pointer(down[e]))) {
-            atomicAnd(&bm[e >> 5], ~(1u << (e & 31)));
-            atomicCAS(status, QG_DEV_OK, QG_DEV_NULL_EXPERT);
+    lds_barrier();
+    // experts with a NULL or misaligned matrix are dropped (checked per pair,
+    // kBatch pairs per lane at a time, so the pointer loads overlap)
+    bool bad_ptr = false;
+    for (int p0 = 0; p0 < P; p0 += kBatch * kWave) {
+        const void *pg[kBatch], *pu[kBatch], *pd[kBatch];
+        int ev[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int p = p0 + i * kWave + l;
+            const int e = p < P ? sid[p] : -1;
+            ev[i] = e >= 0 && e < E ? e : -1;
+            const int ec = ev[i] < 0 ? 0 : ev[i];
+            pg[i] = gate[ec];
+            pu[i] = up[ec];
+            pd[i] = down[ec];
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int e = ev[i];
+            if (e >= 0 && (bad_pointer(pg[i]) || bad_pointer(pu[i]) || bad_pointer(pd[i]))) {
+                atomicAnd(&bm[e >> 5], ~(1u << (e & 31)));
+                bad_ptr = true;
+            }
         }
     }
-    __syncthreads();
+    // the first error in pair order of the checks wins: an id outside the
+    // range before an unusable expert
+    const bool any_bad_id = __ballot(bad_id) != 0ull, any_bad_ptr = __ballot(bad_ptr) != 0ull;
+    if (l == 0) *status = any_bad_id ? QG_DEV_BAD_EXPERT : (any_bad_ptr ? QG_DEV_NULL_EXPERT : QG_DEV_OK);
+    lds_barrier();
     // ranks: each lane owns kTableWords / 64 consecutive words
     constexpr int WPL = kTableWords / kWave;
     int c = 0;
@@ -147,19 +179,20 @@ __global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restr
     }
     if (l == 0) *ws.nuniq = U;
     for (int u = l; u < U; u += kWave) cur[u] = 0;
-    __syncthreads();
-    auto slot_of = [&](int p) -> int {
-        const int e = ids[p];
-        if (e < 0 || e >= E) return -1;
-        const uint32_t word = bm[e >> 5], bit = 1u << (e & 31);
-        return (word & bit) ? wpre[e >> 5] + __popc(word & (bit - 1u)) : -1;
-    };
+    lds_barrier();
+    // each pair's slot (-1: invalid or dropped) replaces its id in sid
     for (int p = l; p < P; p += kWave) {
-        const int s = slot_of(p);
+        const int e = sid[p];
+        int s = -1;
+        if (e >= 0 && e < E) {
+            const uint32_t word = bm[e >> 5], bit = 1u << (e & 31);
+            if (word & bit) s = wpre[e >> 5] + __popc(word & (bit - 1u));
+        }
+        sid[p] = s;
         ws.slot[p] = s;
         if (s >= 0) atomicAdd(&cur[s], 1);
     }
-    __syncthreads();
+    lds_barrier();
     // CSR offsets: lane l scans experts [l*per, (l+1)*per)
     const int per = (U + kWave - 1) / kWave;
     const int lo = min(U, l * per), hi = min(U, lo + per);
@@ -174,13 +207,13 @@ __global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restr
         at += n;
     }
     if (l == 0) ws.pair_off[U] = npairs;
-    __syncthreads();
+    lds_barrier();
     // stable fill, 64 pairs at a time: a pair's place among the chunk's pairs of
     // the same expert comes from a ballot over each distinct slot in the chunk
     const uint64_t below = (1ull << l) - 1ull;
     for (int c0 = 0; c0 < P; c0 += kWave) {
         const int p = c0 + l;
-        const int s = p < P ? slot_of(p) : -1;
+        const int s = p < P ? sid[p] : -1;
         uint64_t left = __ballot(s >= 0);
         int before = 0, same = 0;
         while (left) {
@@ -194,9 +227,9 @@ __global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restr
             left &= ~m;
         }
         if (s >= 0) ws.pairs[cur[s] + before] = p;
-        __syncthreads();
+        lds_barrier();
         if (s >= 0 && before == 0) cur[s] += same;  // one lane per expert present in the chunk
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -242,7 +275,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
     act.sx = a.sx;
     if constexpr (ONE) {
         for (int m = 0; m < cnt; ++m) {
-            if (m > 0) __syncthreads();  // the previous pair's staged activation is no longer read
+            if (m > 0) lds_barrier();  // the previous pair's staged activation is no longer read
             const int p = pairs[m];
             gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8>(
                 W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p / topk; },
@@ -282,7 +315,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     act.psx = a.ws.hs;
     if constexpr (ONE) {
         for (int m = 0; m < cnt; ++m) {
-            if (m > 0) __syncthreads();
+            if (m > 0) lds_barrier();
             const int p = pairs[m];
             gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcGLU>(
                 W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p; },

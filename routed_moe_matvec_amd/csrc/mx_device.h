@@ -237,9 +237,9 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
     if constexpr (FMT == QG_FMT_FP4_E2M1_MX) {
         // 16-byte pieces; rows past N read the last piece that starts inside the scales
         const size_t last = ((scale_total - 1) & ~(size_t)15) - (size_t)row_base * row_scale_bytes;
-        sreg = *reinterpret_cast<const mx_u32x4 *>(scale_src + min((size_t)lsc_off, last));
+        sreg = *as_global<mx_u32x4>(scale_src + min((size_t)lsc_off, last));
     } else {
-        sbyte = scale_src[lsc_off];
+        sbyte = *as_global<uint8_t>(scale_src + lsc_off);
     }
     mx_u32x4 qreg[kMxStageRegs];
     float dreg[kMxStageRegs];
@@ -261,7 +261,7 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = min(lane + kWave * j, cpr - 1);
-            w[r][j] = __builtin_nontemporal_load(reinterpret_cast<const mx_u32x4 *>(W + row * rb + 16 * (size_t)c));
+            w[r][j] = __builtin_nontemporal_load(as_global<mx_u32x4>(W + row * rb + 16 * (size_t)c));
         }
     }
 
@@ -310,14 +310,14 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
     // The first token runs outside any loop: in a loop that only reads
     // registers loaded before it, every load would be waited for at its entry,
     // while here row r waits for its own chunks only.
-    __syncthreads();
+    lds_barrier();
     token(0, 0);
     for (int mm = 1; mm < mt0; ++mm) token(0, mm);
     for (int m0 = mt; m0 < M; m0 += mt) {
         const int mtc = min(mt, M - m0);
-        __syncthreads();  // every wave is done with the previous tokens
+        lds_barrier();  // every wave is done with the previous tokens
         stage(m0, mtc, 0);
-        __syncthreads();
+        lds_barrier();
         for (int mm = 0; mm < mtc; ++mm) token(m0, mm);
     }
 }

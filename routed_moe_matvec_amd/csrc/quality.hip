@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kFxMaxWaves *kWave) void qgemv_fx_kernel(FxArgs a) 
         if (live) load_tile<U>(a.W, a.N, tg, tile, ra);
         const int mtc = min(a.mt, a.M);
         stage(0, mtc);
-        __syncthreads();
+        lds_barrier();
         if (live) {
             tile_to_unit<U>(ra, lw, r * tg.upr + g, valid, u);
             dots(0, mtc);
@@ -114,9 +114,9 @@ __global__ __launch_bounds__(kFxMaxWaves *kWave) void qgemv_fx_kernel(FxArgs a) 
     }
     for (int m0 = a.mt; m0 < a.M; m0 += a.mt) {
         const int mtc = min(a.mt, a.M - m0);
-        __syncthreads();  // every wave is done with the previous tokens
+        lds_barrier();  // every wave is done with the previous tokens
         stage(m0, mtc);
-        __syncthreads();
+        lds_barrier();
         if (live) dots(m0, mtc);
     }
 }
