@@ -178,7 +178,14 @@ struct TileGeom {
     int lsh;  // log2(lpr)
     int rpt;  // rows per tile = 64 / lpr
     int row_bytes;
+    // ceil(2^32 / d) for d = K / 16, K / 128 and K / 4: the token of a staging
+    // chunk index c is then the high half of c times this, with no division in
+    // the kernel (exact while c * d < 2^32: the product overshoots c / d by less
+    // than c / 2^32 < 1 / d, and the fraction of c / d is at most 1 - 1 / d)
+    uint32_t qdiv, sdiv, fdiv;
 };
+
+inline uint32_t recip32(uint32_t d) { return (uint32_t)(((1ull << 32) + d - 1) / d); }
 
 template <class U>
 inline TileGeom make_tile_geom(int K) {
@@ -192,6 +199,9 @@ inline TileGeom make_tile_geom(int K) {
     }
     t.rpt = kWave / t.lpr;
     t.row_bytes = t.upr * U::bytes;
+    t.qdiv = recip32((uint32_t)(K / 16));
+    t.sdiv = recip32((uint32_t)(K / 128));
+    t.fdiv = recip32((uint32_t)(K / 4));
     return t;
 }
 
@@ -239,24 +249,30 @@ inline size_t gemv_lds_bytes(int waves, int K, int mt) {
 // Between the two the caller issues its weight loads, which then stay in
 // flight: the waits for the activation registers only cover loads issued
 // before them.
-template <int FMT, class U>
+template <int FMT, class U, bool ONE>
 struct ActStage {
     static constexpr int REC = U::rec_dwords * 4;
     u32x4 q[kActRegChunks];
     u32x4 d, s;
+    uint32_t qdiv, sdiv;  // TileGeom's reciprocals of K / 16 and K / 128
+
+    // token (within the chunk of tokens) of quant chunk c / of scale chunk c:
+    // always 0 in the one-token form
+    __device__ __forceinline__ int qtok(int c) const { return ONE ? 0 : (int)__umulhi((uint32_t)c, qdiv); }
+    __device__ __forceinline__ int stok(int c) const { return ONE ? 0 : (int)__umulhi((uint32_t)c, sdiv); }
 
     // Chunk c of the token chunk's quants (16 bytes; c < mtc * K / 16).
     template <class TokenRow>
     __device__ __forceinline__ const u32x4 *quant_src(const int8_t *__restrict__ qx, int K, int m0, int c,
                                                       TokenRow token_row) {
         const int cpt = K / 16;
-        const int mm = c / cpt;
+        const int mm = qtok(c);
         return reinterpret_cast<const u32x4 *>(qx + (size_t)token_row(m0 + mm) * K) + (c - mm * cpt);
     }
     __device__ __forceinline__ uint8_t *quant_dst(uint8_t *lds, int K, int c) {
         constexpr int QC = U::weights / 16;  // 16-byte chunks of quants per unit
         const int cpt = K / 16, upr = K / U::weights;
-        const int mm = c / cpt;
+        const int mm = qtok(c);
         const int w = c - mm * cpt;
         const int u = w / QC;
         return lds + (size_t)(mm * upr + u) * REC + (w - u * QC) * 16;
@@ -265,13 +281,13 @@ struct ActStage {
     template <class TokenRow>
     __device__ __forceinline__ size_t scale_src(int K, int m0, int c, TokenRow token_row) {
         const int spt = K / 128;
-        const int mm = c / spt;
+        const int mm = stok(c);
         return (size_t)token_row(m0 + mm) * (K / 32) / 4 + (c - mm * spt);
     }
     __device__ __forceinline__ uint8_t *scale_dst(uint8_t *lds, int K, int c) {
         constexpr int SC = U::blocks / 4;  // 16-byte chunks of scales per unit
         const int spt = K / 128, upr = K / U::weights;
-        const int mm = c / spt;
+        const int mm = stok(c);
         const int w = c - mm * spt;
         const int u = w / SC;
         return lds + (size_t)(mm * upr + u) * REC + U::weights + (w - u * SC) * 16;
@@ -301,10 +317,10 @@ struct ActStage {
 #pragma unroll
         for (int k = 0; k < kActRegChunks; ++k) {
             c[k] = clamp_chunk((int)threadIdx.x + k * NT, qtotal);
-            mm[k] = c[k] / cpt;
+            mm[k] = qtok(c[k]);
         }
         c[kActRegChunks] = clamp_chunk((int)threadIdx.x, stotal);
-        mm[kActRegChunks] = c[kActRegChunks] / spt;
+        mm[kActRegChunks] = stok(c[kActRegChunks]);
 #pragma unroll
         for (int k = 0; k <= kActRegChunks; ++k) row[k] = (size_t)token_row(m0 + mm[k]);
 #pragma unroll
@@ -380,12 +396,21 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // (4 values each) per thread into registers, store() quantizes each 32-block
 // on its 8 consecutive lanes and writes the records; chunks beyond what the
 // registers held are read and quantized in further passes inside store().
-// GLU = true reads two inputs and stages h = silu(g) * v.
-template <int FMT, class U, bool GLU>
+// GLU = true reads two inputs and stages h = silu(g) * v.  As in ActStage,
+// the first pass is read and written unconditionally, threads past the end
+// taking one of the last 64 chunks (whole 32-blocks per 8-lane group, since
+// the chunk count is a multiple of 64), and ONE fixes the token to 0.
+template <int FMT, class U, bool GLU, bool ONE>
 struct ActStageF32 {
     static constexpr int REC = U::rec_dwords * 4;
     float4 v[kActRegChunks];
     float4 v2[GLU ? kActRegChunks : 1];
+    uint32_t fdiv;  // TileGeom's reciprocal of K / 4
+
+    __device__ __forceinline__ int ftok(int c) const { return ONE ? 0 : (int)__umulhi((uint32_t)c, fdiv); }
+    __device__ __forceinline__ static int clamp_chunk(int c, int total) {
+        return c < total ? c : total - kWave + lane_id();
+    }
 
     template <class TokenRow>
     __device__ __forceinline__ void load_pass(const ActSrc &src, int K, int m0, int mtc, int base,
@@ -396,7 +421,7 @@ struct ActStageF32 {
         for (int k = 0; k < kActRegChunks; ++k) {
             const int c = base + (int)threadIdx.x + k * NT;
             if (c < mtc * cpt) {
-                const int mm = c / cpt;
+                const int mm = ftok(c);
                 const size_t at = (size_t)token_row(m0 + mm) * K;
                 v[k] = reinterpret_cast<const float4 *>(src.x + at)[c - mm * cpt];
                 if constexpr (GLU) v2[k] = reinterpret_cast<const float4 *>(src.x2 + at)[c - mm * cpt];
@@ -406,65 +431,83 @@ struct ActStageF32 {
 
     template <class TokenRow>
     __device__ __forceinline__ void load(const ActSrc &src, int K, int m0, int mtc, TokenRow token_row) {
-        load_pass(src, K, m0, mtc, 0, token_row);
+        const int NT = blockDim.x;
+        const int cpt = K / 4, total = mtc * cpt;
+        int c[kActRegChunks], mm[kActRegChunks];
+        size_t at[kActRegChunks];
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k) {
+            c[k] = clamp_chunk((int)threadIdx.x + k * NT, total);
+            mm[k] = ftok(c[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k) at[k] = (size_t)token_row(m0 + mm[k]) * K;
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k) {
+            v[k] = reinterpret_cast<const float4 *>(src.x + at[k])[c[k] - mm[k] * cpt];
+            if constexpr (GLU) v2[k] = reinterpret_cast<const float4 *>(src.x2 + at[k])[c[k] - mm[k] * cpt];
+        }
+    }
+
+    // quantize chunk c (values of register set k) with its 8-lane group and
+    // write the record bytes (and the published copies) when valid
+    template <class TokenRow>
+    __device__ __forceinline__ void emit(uint8_t *lds, int K, int m0, int c, int k, bool valid, TokenRow token_row,
+                                         const ActSrc &src, bool publish) {
+        const int cpt = K / 4, upr = K / U::weights;
+        float vals[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        if constexpr (GLU) {
+            vals[0] = silu(vals[0]) * v2[k].x;
+            vals[1] = silu(vals[1]) * v2[k].y;
+            vals[2] = silu(vals[2]) * v2[k].z;
+            vals[3] = silu(vals[3]) * v2[k].w;
+        }
+        if (!valid) vals[0] = vals[1] = vals[2] = vals[3] = 0.0f;
+        int8_t q[4];
+        float d;
+        int32_t s;
+        quantize_block_8lanes(vals, q, &d, &s);  // every lane takes part (shuffles)
+        if (valid) {
+            const int mm = ftok(c);
+            const int w = c - mm * cpt;
+            const int blk = w >> 3, part = w & 7;
+            const int u = blk / U::blocks, bi = blk - u * U::blocks;
+            const uint32_t packed = (uint32_t)(uint8_t)q[0] | ((uint32_t)(uint8_t)q[1] << 8) |
+                                    ((uint32_t)(uint8_t)q[2] << 16) | ((uint32_t)(uint8_t)q[3] << 24);
+            uint8_t *rec = lds + (size_t)(mm * upr + u) * REC;
+            *reinterpret_cast<uint32_t *>(rec + 32 * bi + 4 * part) = packed;
+            if (part == 0) {
+                *reinterpret_cast<float *>(rec + U::weights + 4 * bi) = d;
+                if constexpr (FMT == QG_FMT_Q4K) *reinterpret_cast<int32_t *>(rec + U::weights + 32 + 4 * bi) = s;
+            }
+            if (publish) {
+                const size_t row = (size_t)token_row(m0 + mm);
+                if (GLU && src.ph)
+                    *reinterpret_cast<float4 *>(src.ph + row * K + 4 * w) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                if (src.pqx) *reinterpret_cast<uint32_t *>(src.pqx + row * K + 32 * blk + 4 * part) = packed;
+                if (part == 0) {
+                    if (src.pdx) src.pdx[row * (K / 32) + blk] = d;
+                    if (src.psx) src.psx[row * (K / 32) + blk] = s;
+                }
+            }
+        }
     }
 
     template <class TokenRow>
     __device__ __forceinline__ void store(uint8_t *lds, int K, int m0, int mtc, TokenRow token_row,
                                           const ActSrc &src, bool publish) {
         const int NT = blockDim.x;
-        const int upr = K / U::weights;
-        const int cpt = K / 4;
-        const int total = mtc * cpt;
-        for (int base = 0; base < total; base += kActRegChunks * NT) {
-            if (base > 0) load_pass(src, K, m0, mtc, base, token_row);
+        const int total = mtc * (K / 4);
+        // 8 consecutive lanes hold one 32-block
+#pragma unroll
+        for (int k = 0; k < kActRegChunks; ++k)
+            emit(lds, K, m0, clamp_chunk((int)threadIdx.x + k * NT, total), k, true, token_row, src, publish);
+        for (int base = kActRegChunks * NT; base < total; base += kActRegChunks * NT) {
+            load_pass(src, K, m0, mtc, base, token_row);
 #pragma unroll
             for (int k = 0; k < kActRegChunks; ++k) {
-                const int c = base + (int)threadIdx.x + k * NT;  // 8 consecutive lanes hold one 32-block
-                const bool valid = c < total;
-                float vals[4] = {0.f, 0.f, 0.f, 0.f};
-                if (valid) {
-                    vals[0] = v[k].x;
-                    vals[1] = v[k].y;
-                    vals[2] = v[k].z;
-                    vals[3] = v[k].w;
-                    if constexpr (GLU) {
-                        vals[0] = silu(vals[0]) * v2[k].x;
-                        vals[1] = silu(vals[1]) * v2[k].y;
-                        vals[2] = silu(vals[2]) * v2[k].z;
-                        vals[3] = silu(vals[3]) * v2[k].w;
-                    }
-                }
-                int8_t q[4];
-                float d;
-                int32_t s;
-                quantize_block_8lanes(vals, q, &d, &s);  // every lane takes part (shuffles)
-                if (valid) {
-                    const int mm = c / cpt;
-                    const int w = c - mm * cpt;
-                    const int blk = w >> 3, part = w & 7;
-                    const int u = blk / U::blocks, bi = blk - u * U::blocks;
-                    const uint32_t packed = (uint32_t)(uint8_t)q[0] | ((uint32_t)(uint8_t)q[1] << 8) |
-                                            ((uint32_t)(uint8_t)q[2] << 16) | ((uint32_t)(uint8_t)q[3] << 24);
-                    uint8_t *rec = lds + (size_t)(mm * upr + u) * REC;
-                    *reinterpret_cast<uint32_t *>(rec + 32 * bi + 4 * part) = packed;
-                    if (part == 0) {
-                        *reinterpret_cast<float *>(rec + U::weights + 4 * bi) = d;
-                        if constexpr (FMT == QG_FMT_Q4K)
-                            *reinterpret_cast<int32_t *>(rec + U::weights + 32 + 4 * bi) = s;
-                    }
-                    if (publish) {
-                        const size_t row = (size_t)token_row(m0 + mm);
-                        if (GLU && src.ph)
-                            *reinterpret_cast<float4 *>(src.ph + row * K + 4 * w) =
-                                make_float4(vals[0], vals[1], vals[2], vals[3]);
-                        if (src.pqx) *reinterpret_cast<uint32_t *>(src.pqx + row * K + 32 * blk + 4 * part) = packed;
-                        if (part == 0) {
-                            if (src.pdx) src.pdx[row * (K / 32) + blk] = d;
-                            if (src.psx) src.psx[row * (K / 32) + blk] = s;
-                        }
-                    }
-                }
+                const int c = base + (int)threadIdx.x + k * NT;
+                emit(lds, K, m0, c, k, c < total, token_row, src, publish);
             }
         }
     }
@@ -559,8 +602,11 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
     TileRegs<U> ra, rb;
     UnitRegs<U> u;
     constexpr bool F32 = SRC != kSrcQ8;
-    ActStage<FMT, U> st;
-    ActStageF32<FMT, U, SRC == kSrcGLU> stf;
+    ActStage<FMT, U, ONE> st;
+    st.qdiv = tg.qdiv;
+    st.sdiv = tg.sdiv;
+    ActStageF32<FMT, U, SRC == kSrcGLU, ONE> stf;
+    stf.fdiv = tg.fdiv;
     // fp32 input: workgroup (0, 0) publishes the Q8 activation; SwiGLU input:
     // workgroup 0 of each blockIdx.y (one expert: its own pairs) publishes h
     const bool publish = SRC == kSrcF32 ? (blockIdx.x == 0 && blockIdx.y == 0) : (SRC == kSrcGLU && blockIdx.x == 0);

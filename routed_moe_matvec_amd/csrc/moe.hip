@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restr
         int before = 0, same = 0;
         while (left) {
             const int leader = __ffsll((unsigned long long)left) - 1;
-            const int v = __shfl(s, leader, kWave);
+            const int v = __builtin_amdgcn_readlane(s, leader);  // leader is wave-uniform
             const uint64_t m = __ballot(s == v);
             if (s == v) {
                 before = __popcll(m & below);
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
     if constexpr (ONE) {
         for (int m = 0; m < cnt; ++m) {
             if (m > 0) lds_barrier();  // the previous pair's staged activation is no longer read
-            const int p = pairs[m];
+            const int p = load_uniform(pairs + m);
             gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8>(
                 W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p / topk; },
                 [=](int, int row, float v) { dst[(size_t)p * F + row] = v; }, [](int, int, int, const int32_t *) {});
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     if constexpr (ONE) {
         for (int m = 0; m < cnt; ++m) {
             if (m > 0) lds_barrier();
-            const int p = pairs[m];
+            const int p = load_uniform(pairs + m);
             gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcGLU>(
                 W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p; },
                 [=](int, int row, float v) { o[(size_t)p * D + row] = v; }, [](int, int, int, const int32_t *) {});
