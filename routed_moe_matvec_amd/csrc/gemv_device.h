@@ -515,10 +515,24 @@ struct ActStageF32 {
 
 // ---------------------------------------------------------------- tile engine
 
-// Sum over the lpr lanes of a row with a fixed xor butterfly; every lane of
-// the row ends with the same value.
+// Sum over the lpr lanes of a row as the fixed pairwise tree of an xor
+// butterfly: level k adds the partner lane^2^k; every lane of the row ends
+// with the same value.  After level k every lane of an aligned 2^k group
+// holds the same value, so a mirror inside the next larger group reaches a
+// lane of the partner group: levels 1-2 are quad permutations, 3-4 half-row
+// and row mirrors (all DPP), 5 a swizzle with xor 16, 6 one lane permute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float row_reduce(float p, int lpr) {
-    for (int off = 1; off < lpr; off <<= 1) p += shfl_xor(p, off);
+    if (lpr >= 2) p += dpp_f32<0xB1>(p);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+    if (lpr >= 4) p += dpp_f32<0x4E>(p);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+    if (lpr >= 8) p += dpp_f32<0x141>(p);  // row_half_mirror: the other quad of 8
+    if (lpr >= 16) p += dpp_f32<0x140>(p); // row_mirror: the other 8 of 16
+    if (lpr >= 32)                         // swizzle, bit mode and 0x1f, xor 0x10
+        p += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, p), 0x401F));
+    if (lpr >= 64) p += shfl_xor(p, 32);
     return p;
 }
 
