@@ -194,6 +194,8 @@ MM_CASES = [
     # and eight groups (K = 1280, 2304: groups per row not a power of two, with
     # enough rows that a workgroup takes few slices); the 8-block unit (K > 8192)
     # with a partial slice; the largest K; ragged row tiles; 4..32 tokens
+    # (batched calls of fewer than 9 tokens run the dot-product engine, so each
+    # case also runs qgemm_q8_0, which always takes the matrix cores)
     (37, 256, 4),
     (100, 1280, 5),
     (16384, 1280, 8),
@@ -211,13 +213,18 @@ MM_CASES = [
 @pytest.mark.parametrize("N,K,M", MM_CASES)
 def test_q8_0_batch_rows_equal_single_token_calls(qg, orc, N, K, M):
     """A batch of M Q8_0 tokens: every row equals the one-token call on that token, bit for
-    bit, and sampled rows match the oracle."""
+    bit, and sampled rows match the oracle; the matrix-core form (qgemm_q8_0) gives the
+    same bits."""
+    import torch
     progress("q8_0 batch N=%d K=%d M=%d" % (N, K, M))
     g = np.random.default_rng(4000 + N + K + M)
     W = synth.q8_0_weight(g, N, K)
     Wd = dev(W)
     qx, dx, sx = gpu_quantize(qg, synth.activations(g, M, K))
     y = _run_gemv(qg, 0, Wd, N, K, qx, dx, sx, M)
+    ymm = sentinel((M, N), torch.float32)
+    qg.qgemm_q8_0(Wd, N, K, qx, dx, M, ymm)
+    assert np.array_equal(host(ymm).view(np.uint32), y.view(np.uint32)), "qgemm_q8_0 vs batched call"
     for t in range(M):
         single = _run_gemv(qg, 0, Wd, N, K, qx[t:t + 1], dx[t:t + 1], sx[t:t + 1], 1)
         assert np.array_equal(y[t].view(np.uint32), single[0].view(np.uint32)), "token %d" % t
