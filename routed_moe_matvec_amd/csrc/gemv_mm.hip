@@ -93,28 +93,31 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
     const int grp0 = wave * a.gps;
     const int ngroups = min(max(a.groups - grp0, 0), a.gps);
 
-    // Group loads: instruction i < 8 reads part 4 (i / 2) + lane % 4 of row
-    // 16 (i % 2) + lane / 4 (a quad of lanes reads 64 consecutive bytes of one
-    // row), instruction 8 part 16 of row lane % 32 (lanes 32..63 repeat it and
-    // do not store).  Rows past N re-read row N - 1.
-    const int rl = lane >> 2, pq = lane & 3, r32 = lane & 31;
-    const uint8_t *wr0 = W + (size_t)min(row0 + rl, N - 1) * a.row_bytes + 16 * pq;
-    const uint8_t *wr1 = W + (size_t)min(row0 + 16 + rl, N - 1) * a.row_bytes + 16 * pq;
-    const uint8_t *wr8 = W + (size_t)min(row0 + r32, N - 1) * a.row_bytes + 256;
+    // Group loads: the 32 rows x 17 parts (16 bytes) of a group in row order,
+    // instruction i / lane l taking chunk 64 i + l = 17 r + p, so that an
+    // instruction reads a few contiguous 272-byte runs (few cache lines per
+    // instruction: the address units, not HBM, bounded the earlier pattern of
+    // 16 rows x 64 bytes).  Instruction 8 has 32 chunks: its lanes 32..63
+    // repeat lanes 0..31 and do not store.  Rows past N re-read row N - 1.
+    const int r32 = lane & 31, half = lane >> 5;
+    const uint8_t *wt = W + (size_t)row0 * a.row_bytes;
+    uint32_t goff[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        const int idx = i < 8 ? 64 * i + lane : 512 + r32;
+        const int r = idx / kMmParts, p = idx - kMmParts * r;
+        goff[i] = (uint32_t)(min(row0 + r, N - 1) - row0) * (uint32_t)a.row_bytes + 16u * p;
+    }
     // activation: token lane % 32 (tokens past M re-read token M - 1; their
     // columns are not stored), 16 quants of each block per lane half
-    const int half = lane >> 5;
     const size_t arow = (size_t)min(m0 + r32, a.M - 1) * a.G + g;
     const int8_t *xp = a.qx + arow * a.K + 16 * half;
     const float *dp = a.dx + arow * (a.K / 32);
 
     auto load_w = [&](int gi, u32x4 (&w)[9]) __attribute__((always_inline)) {
-        const size_t off = (size_t)gi * 272;
+        const uint8_t *base = wt + (size_t)gi * 272;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            w[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(((i & 1) ? wr1 : wr0) + off + 64 * (i >> 1)));
-        w[8] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr8 + off));
+        for (int i = 0; i < 9; ++i) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + goff[i]));
     };
     auto load_dx = [&](int gi, float4 (&d)[2]) __attribute__((always_inline)) {
         d[0] = reinterpret_cast<const float4 *>(dp + 8 * gi)[0];
@@ -122,21 +125,17 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
     };
     auto load_act = [&](int gi, int b) __attribute__((always_inline)) { return *reinterpret_cast<const i32x4 *>(xp + (size_t)gi * 256 + 32 * b); };
 
-    // Stage layout: part p of row r at 16 (32 p + (r ^ 2 (p % 4))).  The xor
-    // puts the four parts a quad writes and the rows that eight lanes read
-    // at one part in eight different 16-byte bank groups.
-    auto chunk = [&](int p, int r) __attribute__((always_inline)) { return 16 * (32 * p + (r ^ (2 * (p & 3)))); };
+    // Stage layout: row r's 272 bytes at 272 r, i.e. chunk 17 r + p at 16 times
+    // that, so the loads' chunks are written linearly; a 16-lane pass reading
+    // one part of 16 rows hits 16 different 16-byte bank groups (row stride
+    // 68 dwords).
     auto store_w = [&](const u32x4 (&w)[9]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<u32x4 *>(stage + chunk(4 * (i >> 1) + pq, 16 * (i & 1) + rl)) = w[i];
-        if (lane < 32) *reinterpret_cast<u32x4 *>(stage + chunk(16, lane)) = w[8];
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(stage + 16 * (64 * i + lane)) = w[i];
+        if (lane < 32) *reinterpret_cast<u32x4 *>(stage + 16 * (512 + lane)) = w[8];
     };
-    // A-operand reads: part p0 + half of row lane % 32 sits at
-    // stage + 512 p0 + abase[p0 % 4]
-    int abase[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) abase[j] = 512 * half + 16 * (r32 ^ (2 * ((j + half) & 3)));
+    // A-operand reads: part p0 + half of row lane % 32 sits at abase + 16 p0
+    const int abase = kMmParts * 16 * r32 + 16 * half;
     // fp16 scales of the stage, arranged so that a lane half reads the 16 rows
     // 8q + 4 half + t of its MFMA result as 32 consecutive bytes
     const int slot = ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
@@ -144,8 +143,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int bb = 4 * half + j;
-            const int off = 34 * bb;
-            const uint16_t v = *reinterpret_cast<const uint16_t *>(stage + chunk(off >> 4, r32) + (off & 15));
+            const uint16_t v = *reinterpret_cast<const uint16_t *>(stage + kMmParts * 16 * r32 + 34 * bb);
             *reinterpret_cast<uint16_t *>(stab + 2 * (bb * 32 + slot)) = v;
         }
     };
@@ -236,9 +234,9 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
             constexpr int b = decltype(bi)::value;
             constexpr int o = 34 * b + 2;
             constexpr int p0 = o >> 4, sh = o & 15, wd = sh >> 2, bs = sh & 3;
-            const u32x4 c0 = *reinterpret_cast<const u32x4 *>(stage + 512 * p0 + abase[p0 & 3]);
+            const u32x4 c0 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * p0);
             u32x4 c1 = c0;
-            if constexpr (sh != 0) c1 = *reinterpret_cast<const u32x4 *>(stage + 512 * (p0 + 1) + abase[(p0 + 1) & 3]);
+            if constexpr (sh != 0) c1 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * (p0 + 1));
             const uint32_t D[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
             i32x4 A;
 #pragma unroll
