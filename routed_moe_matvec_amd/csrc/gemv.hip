@@ -17,6 +17,8 @@ constexpr int kGemvMaxWaves = 8;
 // the matrix-core form about 29.5; from 9 tokens the engine needs a second
 // staging chunk and 12 tokens take it 37.6 us against 30.1)
 constexpr int kMmMinTokens = 9;
+// the same for Q4_K
+constexpr int kMmMinTokensQ4K = 9;
 
 struct GemvArgs {
     const uint8_t *W0;
@@ -155,10 +157,9 @@ static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2
     a.M = M;
     a.isum = isum;
     a.G = G;
-    // batches of kMmMinTokens or more Q8_0 tokens go to the matrix cores
-    // (same results bit for bit)
-    if (fmt == QG_FMT_Q8_0 && !f32 && !isum && M >= kMmMinTokens)
-        return gemv_mm_q8_0(a.W0, N1, y1, a.W1, N2, y2, K, act.qx, act.dx, M, G, stream);
+    // larger batches go to the matrix cores (same results bit for bit)
+    if (!f32 && !isum && M >= (fmt == QG_FMT_Q8_0 ? kMmMinTokens : kMmMinTokensQ4K))
+        return gemv_mm(fmt, a.W0, N1, y1, a.W1, N2, y2, K, act.qx, act.dx, act.sx, M, G, stream);
     if (isum) return launch_fmt<true, false>(fmt, a, stream);
     return f32 ? launch_fmt<false, true>(fmt, a, stream) : launch_fmt<false, false>(fmt, a, stream);
 }

@@ -698,10 +698,10 @@ inline int tiles_per_wave(int ntiles, int resident_waves, bool single_chunk) {
 // Compute units of the current device (queried once per process and device).
 int device_cu_count();
 
-// The matrix-core form of the Q8_0 mat-vec on a Q8 activation (gemv_mm.hip):
-// same arguments and results as the engine above for one matrix (W1 = NULL)
-// or a pair, G groups, M tokens.
-int gemv_mm_q8_0(const uint8_t *W0, int N0, float *y0, const uint8_t *W1, int N1, float *y1, int K, const int8_t *qx,
-                 const float *dx, int M, int G, hipStream_t stream);
+// The matrix-core form of the Q8_0 / Q4_K mat-vec on a Q8 activation
+// (gemv_mm.hip): same arguments and results, bit for bit, as the engine above
+// for one matrix (W1 = NULL) or a pair, G groups, M tokens (sx: Q4_K only).
+int gemv_mm(int fmt, const uint8_t *W0, int N0, float *y0, const uint8_t *W1, int N1, float *y1, int K,
+            const int8_t *qx, const float *dx, const int32_t *sx, int M, int G, hipStream_t stream);
 
 }  // namespace qg

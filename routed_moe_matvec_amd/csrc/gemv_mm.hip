@@ -42,14 +42,35 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-constexpr int kMmRows = 32;                             // weight rows of a workgroup
-constexpr int kMmTokens = 32;                           // tokens of a workgroup
-constexpr int kMmParts = 17;                            // 16-byte parts of a row's 272-byte group
-constexpr int kMmStageBytes = kMmParts * kMmRows * 16;  // one group of 32 rows: [part][row] x 16 B
-constexpr int kMmScaleBytes = 8 * kMmRows * 2;          // fp16 scales of a group: [block][lane half][16]
+constexpr int kMmRows = 32;    // weight rows of a workgroup
+constexpr int kMmTokens = 32;  // tokens of a workgroup
+
+// Per format: 16-byte parts of a row's 256-weight group (Q8_0: 8 blocks of
+// 34 bytes; Q4_K: one 144-byte superblock), the load instructions that move
+// a group of 32 rows (the last one 32 chunks), and the per-group scale table
+// (Q8_0: fp16 block scales; Q4_K: fp32 d*sc and dmin*m of each sub-block).
+template <int FMT>
+struct MmFmt;
+template <>
+struct MmFmt<QG_FMT_Q8_0> {
+    static constexpr int parts = 17;
+    static constexpr int table_bytes = 8 * kMmRows * 2;
+};
+template <>
+struct MmFmt<QG_FMT_Q4K> {
+    static constexpr int parts = 9;
+    static constexpr int table_bytes = 8 * kMmRows * 4 * 2;
+};
+template <int FMT>
+constexpr int mm_stage_bytes() { return MmFmt<FMT>::parts * kMmRows * 16; }
+template <int FMT>
+constexpr int mm_loads() { return (MmFmt<FMT>::parts * kMmRows + kWave - 1) / kWave; }
 // LDS of a wave: the stage, the scale table and the pending tree levels 1
 // and 2 (slices of four or eight groups)
-constexpr int mm_wave_lds(int gps) { return kMmStageBytes + kMmScaleBytes + (gps >= 8 ? 2 : gps >= 4 ? 1 : 0) * 16 * 64 * 4; }
+template <int FMT>
+constexpr int mm_wave_lds(int gps) {
+    return mm_stage_bytes<FMT>() + MmFmt<FMT>::table_bytes + (gps >= 8 ? 2 : gps >= 4 ? 1 : 0) * 16 * 64 * 4;
+}
 constexpr int kMmMaxSlices = 8;       // waves of a workgroup
 constexpr int kMmMaxGroups = 8;       // groups of a slice (three stored tree levels)
 constexpr int kMmTargetWaves = 2048;  // about two waves per SIMD over the chip
@@ -62,6 +83,7 @@ struct MmArgs {
     int ntok; // 32-token tiles: workgroup x takes row tile x / ntok, token tile x % ntok
     const int8_t *qx;
     const float *dx;
+    const int32_t *sx;  // Q4_K: block sums of the activation
     int K, M, G;
     int row_bytes;
     int groups;  // 256-weight groups per row
@@ -69,8 +91,10 @@ struct MmArgs {
     int KS;      // slices = waves per workgroup
 };
 
-template <int NB, int GPS>
-__global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmArgs a) {
+template <int FMT, int NB, int GPS>
+__global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_kernel(MmArgs a) {
+    using F = MmFmt<FMT>;
+    constexpr int kParts = F::parts, kLoads = mm_loads<FMT>(), kGroupBytes = kParts * 16;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // the wave index is uniform over the wave: keep it (and every slice bound) scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -86,26 +110,27 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
     const uint8_t *W = (second ? a.W1 : a.W0) + (size_t)g * N * a.row_bytes;
     float *y = second ? a.y1 : a.y0;
     const int row0 = tile * kMmRows;
-    constexpr int kWaveLds = mm_wave_lds(GPS);
+    constexpr int kWaveLds = mm_wave_lds<FMT>(GPS);
     uint8_t *stage = smem + wave * kWaveLds;
-    uint8_t *stab = stage + kMmStageBytes;
+    uint8_t *stab = stage + mm_stage_bytes<FMT>();
 
     const int grp0 = wave * a.gps;
     const int ngroups = min(max(a.groups - grp0, 0), a.gps);
 
-    // Group loads: the 32 rows x 17 parts (16 bytes) of a group in row order,
-    // instruction i / lane l taking chunk 64 i + l = 17 r + p, so that an
-    // instruction reads a few contiguous 272-byte runs (few cache lines per
-    // instruction: the address units, not HBM, bounded the earlier pattern of
-    // 16 rows x 64 bytes).  Instruction 8 has 32 chunks: its lanes 32..63
-    // repeat lanes 0..31 and do not store.  Rows past N re-read row N - 1.
+    // Group loads: the 32 rows x kParts parts (16 bytes) of a group in row
+    // order, instruction i / lane l taking chunk 64 i + l = kParts r + p, so
+    // that an instruction reads a few contiguous runs of a row's group (few
+    // cache lines per instruction: the address units, not HBM, bounded an
+    // earlier pattern of 16 rows x 64 bytes).  The last instruction has 32
+    // chunks: its lanes 32..63 repeat lanes 0..31 and do not store.  Rows past
+    // N re-read row N - 1.
     const int r32 = lane & 31, half = lane >> 5;
     const uint8_t *wt = W + (size_t)row0 * a.row_bytes;
-    uint32_t goff[9];
+    uint32_t goff[kLoads];
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
-        const int idx = i < 8 ? 64 * i + lane : 512 + r32;
-        const int r = idx / kMmParts, p = idx - kMmParts * r;
+    for (int i = 0; i < kLoads; ++i) {
+        const int idx = i < kLoads - 1 ? 64 * i + lane : 64 * (kLoads - 1) + r32;
+        const int r = idx / kParts, p = idx - kParts * r;
         goff[i] = (uint32_t)(min(row0 + r, N - 1) - row0) * (uint32_t)a.row_bytes + 16u * p;
     }
     // activation: token lane % 32 (tokens past M re-read token M - 1; their
@@ -113,38 +138,60 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
     const size_t arow = (size_t)min(m0 + r32, a.M - 1) * a.G + g;
     const int8_t *xp = a.qx + arow * a.K + 16 * half;
     const float *dp = a.dx + arow * (a.K / 32);
+    const int32_t *sp = FMT == QG_FMT_Q4K ? a.sx + arow * (a.K / 32) : nullptr;
 
-    auto load_w = [&](int gi, u32x4 (&w)[9]) __attribute__((always_inline)) {
-        const uint8_t *base = wt + (size_t)gi * 272;
+    auto load_w = [&](int gi, u32x4 (&w)[kLoads]) __attribute__((always_inline)) {
+        const uint8_t *base = wt + (size_t)gi * kGroupBytes;
 #pragma unroll
-        for (int i = 0; i < 9; ++i) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + goff[i]));
+        for (int i = 0; i < kLoads; ++i) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + goff[i]));
     };
-    auto load_dx = [&](int gi, float4 (&d)[2]) __attribute__((always_inline)) {
+    // the 8 block scales of the token (and, Q4_K, the 8 block sums as floats)
+    auto load_dx = [&](int gi, float4 (&d)[4]) __attribute__((always_inline)) {
         d[0] = reinterpret_cast<const float4 *>(dp + 8 * gi)[0];
         d[1] = reinterpret_cast<const float4 *>(dp + 8 * gi)[1];
+        if constexpr (FMT == QG_FMT_Q4K) {
+            const int4 s0 = reinterpret_cast<const int4 *>(sp + 8 * gi)[0];
+            const int4 s1 = reinterpret_cast<const int4 *>(sp + 8 * gi)[1];
+            d[2] = make_float4((float)s0.x, (float)s0.y, (float)s0.z, (float)s0.w);
+            d[3] = make_float4((float)s1.x, (float)s1.y, (float)s1.z, (float)s1.w);
+        }
     };
     auto load_act = [&](int gi, int b) __attribute__((always_inline)) { return *reinterpret_cast<const i32x4 *>(xp + (size_t)gi * 256 + 32 * b); };
 
-    // Stage layout: row r's 272 bytes at 272 r, i.e. chunk 17 r + p at 16 times
-    // that, so the loads' chunks are written linearly; a 16-lane pass reading
-    // one part of 16 rows hits 16 different 16-byte bank groups (row stride
-    // 68 dwords).
-    auto store_w = [&](const u32x4 (&w)[9]) __attribute__((always_inline)) {
+    // Stage layout: row r's group bytes at kParts * 16 r, i.e. chunk
+    // kParts r + p at 16 times that, so the loads' chunks are written
+    // linearly; a 16-lane pass reading one part of 16 rows hits 16 different
+    // 16-byte bank groups (row strides of 68 and 36 dwords).
+    auto store_w = [&](const u32x4 (&w)[kLoads]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(stage + 16 * (64 * i + lane)) = w[i];
-        if (lane < 32) *reinterpret_cast<u32x4 *>(stage + 16 * (512 + lane)) = w[8];
+        for (int i = 0; i < kLoads - 1; ++i) *reinterpret_cast<u32x4 *>(stage + 16 * (64 * i + lane)) = w[i];
+        if (lane < 32) *reinterpret_cast<u32x4 *>(stage + 16 * (64 * (kLoads - 1) + lane)) = w[kLoads - 1];
     };
     // A-operand reads: part p0 + half of row lane % 32 sits at abase + 16 p0
-    const int abase = kMmParts * 16 * r32 + 16 * half;
-    // fp16 scales of the stage, arranged so that a lane half reads the 16 rows
-    // 8q + 4 half + t of its MFMA result as 32 consecutive bytes
+    const int abase = kParts * 16 * r32 + 16 * half;
+    // Scale table of the stage, arranged so that a lane half reads the 16 rows
+    // 8q + 4 half + t of its MFMA result as consecutive entries: Q8_0 the fp16
+    // block scales [block][slot]; Q4_K d*sc_j and dmin*m_j as fp32
+    // [sub-block][a | bm][slot] (exact products: 11-bit by 6-bit)
     const int slot = ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
     auto build_scales = [&]() __attribute__((always_inline)) {
+        if constexpr (FMT == QG_FMT_Q8_0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int bb = 4 * half + j;
-            const uint16_t v = *reinterpret_cast<const uint16_t *>(stage + kMmParts * 16 * r32 + 34 * bb);
-            *reinterpret_cast<uint16_t *>(stab + 2 * (bb * 32 + slot)) = v;
+            for (int j = 0; j < 4; ++j) {
+                const int bb = 4 * half + j;
+                const uint16_t v = *reinterpret_cast<const uint16_t *>(stage + kParts * 16 * r32 + 34 * bb);
+                *reinterpret_cast<uint16_t *>(stab + 2 * (bb * 32 + slot)) = v;
+            }
+        } else {
+            const u32x4 hd = *reinterpret_cast<const u32x4 *>(stage + kParts * 16 * r32);
+            const float d = half_bits_to_float(hd.x), dmin = half_bits_to_float(hd.x >> 16);
+            float *tab = reinterpret_cast<float *>(stab);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int jj = 4 * half + j;
+                tab[(2 * jj) * 32 + slot] = d * (float)q4k_field(hd.y, hd.z, hd.w, jj);
+                tab[(2 * jj + 1) * 32 + slot] = dmin * (float)q4k_field(hd.y, hd.z, hd.w, 8 + jj);
+            }
         }
     };
 
@@ -156,7 +203,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
     float st0[16], top[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) st0[e] = top[e] = 0.0f;
-    float *lvl = reinterpret_cast<float *>(stage + kMmStageBytes + kMmScaleBytes);  // [level - 1][16][64]
+    float *lvl = reinterpret_cast<float *>(stab + F::table_bytes);  // [level - 1][16][64]
     auto lvl_store = [&](int k, const float (&v)[16]) __attribute__((always_inline)) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) lvl[((k - 1) * 16 + e) * kWave + lane] = v[e];
@@ -205,8 +252,10 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
     };
     // Weights are requested two groups ahead (two register sets), activations
     // and their scales one group ahead.
-    u32x4 wreg[2][9];
-    float4 dxv[2];
+    // dxv: the token's 8 block scales, then (Q4_K) its 8 block sums as floats
+    constexpr int DXV = FMT == QG_FMT_Q4K ? 4 : 2;
+    u32x4 wreg[2][kLoads];
+    float4 dxv[4];
     i32x4 act[8];
     load_w(gclamp(0), wreg[0]);
     if constexpr (GPS > 1) load_w(gclamp(1), wreg[1]);
@@ -224,23 +273,32 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
         __builtin_amdgcn_sched_barrier(0);
         store_w(wreg[s & 1]);
         build_scales();
-        float4 dxn[2];
+        float4 dxn[4];
         if constexpr (PF2) load_w(gclamp(s + 2), wreg[s & 1]);
         if constexpr (PF) load_dx(gnext, dxn);
         // block b's integer sums: A operand = quants 16 half .. 16 half + 15 of
-        // block b of row lane % 32, realigned from the stage; then the next
-        // group's activation for block b is requested
+        // block (Q4_K: sub-block) b of row lane % 32 from the stage (Q8_0:
+        // realigned bytes; Q4_K: the low / high nibbles of the 32 bytes that
+        // sub-blocks 2p and 2p + 1 share); then the next group's activation
+        // for block b is requested
         auto block_sums = [&](auto bi) __attribute__((always_inline)) {
             constexpr int b = decltype(bi)::value;
-            constexpr int o = 34 * b + 2;
-            constexpr int p0 = o >> 4, sh = o & 15, wd = sh >> 2, bs = sh & 3;
-            const u32x4 c0 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * p0);
-            u32x4 c1 = c0;
-            if constexpr (sh != 0) c1 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * (p0 + 1));
-            const uint32_t D[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
             i32x4 A;
+            if constexpr (FMT == QG_FMT_Q8_0) {
+                constexpr int o = 34 * b + 2;
+                constexpr int p0 = o >> 4, sh = o & 15, wd = sh >> 2, bs = sh & 3;
+                const u32x4 c0 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * p0);
+                u32x4 c1 = c0;
+                if constexpr (sh != 0) c1 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * (p0 + 1));
+                const uint32_t D[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) A[k] = (int)(bs ? align_bytes(D[wd + k + 1], D[wd + k], bs) : D[wd + k]);
+                for (int k = 0; k < 4; ++k) A[k] = (int)(bs ? align_bytes(D[wd + k + 1], D[wd + k], bs) : D[wd + k]);
+            } else {
+                const u32x4 c = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * (1 + 2 * (b >> 1)));
+                const uint32_t D[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) A[k] = (int)(((b & 1) ? (D[k] >> 4) : D[k]) & 0x0F0F0F0Fu);
+            }
             const i32x16 zero = {};
             const i32x16 is = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, act[b], zero, 0, 0, 0);
             if constexpr (PF) act[b] = load_act(gnext, b);
@@ -250,6 +308,26 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
         // scale and accumulate block b (the next block's product is already issued)
         auto block_scale = [&](auto bi, const i32x16 &is) __attribute__((always_inline)) {
             constexpr int b = decltype(bi)::value;
+            if constexpr (FMT == QG_FMT_Q4K) {
+                // the one-token engine's sub-block step: inner = d sc_j isum -
+                // dmin m_j sx_j (one fma on the rounded product), then
+                // acc = fma(inner, dx_j, acc) from +0
+                const float *tab = reinterpret_cast<const float *>(stab);
+                float av[16], bv[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 x = reinterpret_cast<const float4 *>(tab + (2 * b) * 32 + 16 * half)[q];
+                    const float4 y = reinterpret_cast<const float4 *>(tab + (2 * b + 1) * 32 + 16 * half)[q];
+                    av[4 * q] = x.x, av[4 * q + 1] = x.y, av[4 * q + 2] = x.z, av[4 * q + 3] = x.w;
+                    bv[4 * q] = y.x, bv[4 * q + 1] = y.y, bv[4 * q + 2] = y.z, bv[4 * q + 3] = y.w;
+                }
+                const float dxb = dxv[b >> 2][b & 3], sxb = dxv[2 + (b >> 2)][b & 3];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float inner = fmaf_exact(av[e], (float)is[e], -(bv[e] * sxb));
+                    acc[e] = fmaf_exact(inner, dxb, b == 0 ? 0.0f : acc[e]);
+                }
+            } else {
             const u32x4 s0 = *reinterpret_cast<const u32x4 *>(stab + 64 * b + 32 * half);
             const u32x4 s1 = *reinterpret_cast<const u32x4 *>(stab + 64 * b + 32 * half + 16);
             const uint32_t S[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
@@ -266,6 +344,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
                 const float sc = __builtin_fmaf(dw, dxb, 0.0f);
                 const float prev = (b % NB == 0) ? 0.0f : ac[e];
                 ac[e] = fmaf_exact((float)is[e], sc, prev);
+            }
             }
         };
         using I = std::integral_constant<int, 0>;
@@ -293,8 +372,8 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
         }
         push(acc, index);
         if constexpr (PF) {
-            dxv[0] = dxn[0];
-            dxv[1] = dxn[1];
+#pragma unroll
+            for (int i = 0; i < DXV; ++i) dxv[i] = dxn[i];
         }
     };
     static_assert(GPS == 1 || GPS == 2 || GPS == 4 || GPS == 8, "groups per slice");
@@ -358,25 +437,26 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_q8_0_kernel(MmAr
     }
 }
 
-template <int NB, int GPS>
+template <int FMT, int NB, int GPS>
 static int launch_mm_gps(const MmArgs &a, int nt1, hipStream_t stream) {
     static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_mm_q8_0_kernel<NB, GPS>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kMmMaxSlices * mm_wave_lds(GPS)) != hipSuccess)
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_mm_kernel<FMT, NB, GPS>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kMmMaxSlices * mm_wave_lds<FMT>(GPS)) != hipSuccess)
             return QG_ERR_LAUNCH;
         attr_set = true;
     }
-    hipLaunchKernelGGL((qgemv_mm_q8_0_kernel<NB, GPS>), dim3((a.nt0 + nt1) * a.ntok, a.G), dim3(a.KS * kWave),
-                       (size_t)a.KS * mm_wave_lds(GPS), stream, a);
+    hipLaunchKernelGGL((qgemv_mm_kernel<FMT, NB, GPS>), dim3((a.nt0 + nt1) * a.ntok, a.G), dim3(a.KS * kWave),
+                       (size_t)a.KS * mm_wave_lds<FMT>(GPS), stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
 // Slices per workgroup: at most eight groups per slice, at most eight slices,
 // and more slices while the grid has fewer than about two waves per SIMD.
-template <int NB>
+template <int FMT, int NB>
 static int launch_mm(MmArgs &a, hipStream_t stream) {
-    a.row_bytes = a.K / 32 * 34;
+    a.row_bytes = a.K / 256 * MmFmt<FMT>::parts * 16;
     a.groups = a.K / 256;
     int gpow2 = 1;
     while (gpow2 < a.groups) gpow2 <<= 1;
@@ -390,16 +470,16 @@ static int launch_mm(MmArgs &a, hipStream_t stream) {
     a.KS = ks;
     a.gps = gpow2 / ks;
     switch (a.gps) {
-        case 1: return launch_mm_gps<NB, 1>(a, nt1, stream);
-        case 2: return launch_mm_gps<NB, 2>(a, nt1, stream);
-        case 4: return launch_mm_gps<NB, 4>(a, nt1, stream);
-        case 8: return launch_mm_gps<NB, 8>(a, nt1, stream);
+        case 1: return launch_mm_gps<FMT, NB, 1>(a, nt1, stream);
+        case 2: return launch_mm_gps<FMT, NB, 2>(a, nt1, stream);
+        case 4: return launch_mm_gps<FMT, NB, 4>(a, nt1, stream);
+        case 8: return launch_mm_gps<FMT, NB, 8>(a, nt1, stream);
         default: return QG_ERR_SHAPE;
     }
 }
 
-int gemv_mm_q8_0(const uint8_t *W0, int N0, float *y0, const uint8_t *W1, int N1, float *y1, int K, const int8_t *qx,
-                 const float *dx, int M, int G, hipStream_t stream) {
+int gemv_mm(int fmt, const uint8_t *W0, int N0, float *y0, const uint8_t *W1, int N1, float *y1, int K,
+            const int8_t *qx, const float *dx, const int32_t *sx, int M, int G, hipStream_t stream) {
     MmArgs a{};
     a.W0 = W0;
     a.N0 = N0;
@@ -410,11 +490,14 @@ int gemv_mm_q8_0(const uint8_t *W0, int N0, float *y0, const uint8_t *W1, int N1
     a.K = K;
     a.qx = qx;
     a.dx = dx;
+    a.sx = sx;
     a.M = M;
     a.G = G;
-    // the unit of the one-token engine: 4 blocks up to K = 8192, else 8
-    if (K <= 8192) return launch_mm<4>(a, stream);
-    return launch_mm<8>(a, stream);
+    // the unit of the one-token engine: Q4_K one superblock; Q8_0 4 blocks up
+    // to K = 8192, else 8
+    if (fmt == QG_FMT_Q4K) return launch_mm<QG_FMT_Q4K, 8>(a, stream);
+    if (K <= 8192) return launch_mm<QG_FMT_Q8_0, 4>(a, stream);
+    return launch_mm<QG_FMT_Q8_0, 8>(a, stream);
 }
 
 }  // namespace qg
@@ -425,6 +508,6 @@ extern "C" int qgemm_q8_0(const void *W, int N, int K, const int8_t *qx, const f
     if (N < 1 || M < 1 || M > QG_MAX_PREFILL_M) return QG_ERR_SHAPE;
     if (K < qg::kGroupWeights || K > QG_MAX_K || K % qg::kGroupWeights != 0) return QG_ERR_SHAPE;
     if (((uintptr_t)W | (uintptr_t)qx | (uintptr_t)dx | (uintptr_t)y) & 15) return QG_ERR_ALIGN;
-    return qg::gemv_mm_q8_0(reinterpret_cast<const uint8_t *>(W), N, y, nullptr, 0, nullptr, K, qx, dx, M, 1,
-                            (hipStream_t)stream);
+    return qg::gemv_mm(QG_FMT_Q8_0, reinterpret_cast<const uint8_t *>(W), N, y, nullptr, 0, nullptr, K, qx, dx,
+                       nullptr, M, 1, (hipStream_t)stream);
 }

@@ -172,10 +172,10 @@ def test_paired_equals_two_singles_and_oracle(qg, orc):
     K, N1, N2 = w["K"], w["N1"], w["N2"]
     for fmt in (0, 1):
         W1, W2 = _weights(fmt, g, N1, K), _weights(fmt, g, N2, K)
-        x = synth.activations(g, 8, K)
+        x = synth.activations(g, 12, K)
         qx, dx, sx = gpu_quantize(qg, x)
         import torch
-        for M in (1, 2, 8):
+        for M in (1, 2, 8, 12):
             y1, y2 = sentinel((M, N1), torch.float32), sentinel((M, N2), torch.float32)
             qg.qgemv_paired(fmt, dev(W1), N1, dev(W2), N2, K, qx[:M], dx[:M], sx[:M], M, y1, y2)
             s1 = _run_gemv(qg, fmt, dev(W1), N1, K, qx[:M], dx[:M], sx[:M], M)
@@ -231,6 +231,39 @@ def test_q8_0_batch_rows_equal_single_token_calls(qg, orc, N, K, M):
     rows = np.arange(N) if N <= 512 else np.sort(g.choice(N, 256, replace=False))
     ref, bound = orc.gemv(0, W[rows], len(rows), K, host(qx), host(dx), nthreads=oracle_threads())
     assert_within_bound(y[:, rows], ref, bound, what="q8_0 batch N=%d K=%d M=%d" % (N, K, M))
+
+
+MM_Q4K_CASES = [
+    # N, K, M: Q4_K batches on the matrix cores (9 tokens and more): one
+    # superblock per row; groups per row not a power of two (partial and empty
+    # K slices); the largest K; ragged row and token tiles
+    (37, 256, 9),
+    (100, 1280, 12),
+    (16384, 1280, 9),
+    (32768, 2304, 10),
+    (70, 7168, 17),
+    (9, 12288, 32),
+    (64, 16384, 16),
+    (8192, 4096, 32),
+]
+
+
+@pytest.mark.parametrize("N,K,M", MM_Q4K_CASES)
+def test_q4k_batch_rows_equal_single_token_calls(qg, orc, N, K, M):
+    """A batch of M Q4_K tokens: every row equals the one-token call on that token, bit for
+    bit, and sampled rows match the oracle."""
+    progress("q4k batch N=%d K=%d M=%d" % (N, K, M))
+    g = np.random.default_rng(7000 + N + K + M)
+    W = synth.q4k_weight(g, N, K)
+    Wd = dev(W)
+    qx, dx, sx = gpu_quantize(qg, synth.activations(g, M, K))
+    y = _run_gemv(qg, 1, Wd, N, K, qx, dx, sx, M)
+    for t in range(M):
+        single = _run_gemv(qg, 1, Wd, N, K, qx[t:t + 1], dx[t:t + 1], sx[t:t + 1], 1)
+        assert np.array_equal(y[t].view(np.uint32), single[0].view(np.uint32)), "token %d" % t
+    rows = np.arange(N) if N <= 512 else np.sort(g.choice(N, 256, replace=False))
+    ref, bound = orc.gemv(1, W[rows], len(rows), K, host(qx), host(dx), nthreads=oracle_threads())
+    assert_within_bound(y[:, rows], ref, bound, what="q4k batch N=%d K=%d M=%d" % (N, K, M))
 
 
 @pytest.mark.parametrize("fmt,N,K,M", [(0, 45, 1024, 2), (0, 8, 12288, 1), (1, 33, 2048, 3), (1, 5, 256, 1)])
@@ -363,7 +396,8 @@ def test_fused_errors(qg):
 # ---------------------------------------------------------------- grouped (attention output, low rank)
 
 @pytest.mark.parametrize("fmt,G,N,K,M", [(0, 8, 1024, 4096, 1), (0, 3, 130, 512, 3), (1, 2, 70, 1024, 2),
-                                         (0, 1, 96, 256, 5), (1, 5, 33, 256, 1), (0, 8, 1024, 4096, 12)])
+                                         (0, 1, 96, 256, 5), (1, 5, 33, 256, 1), (0, 8, 1024, 4096, 12),
+                                         (1, 3, 100, 2048, 12)])
 def test_grouped_parity(qg, orc, fmt, G, N, K, M):
     """Group g against the oracle on matrix g and input slice g; ragged N, G = 1, several tokens."""
     import torch
@@ -387,26 +421,30 @@ def test_grouped_parity(qg, orc, fmt, G, N, K, M):
 def test_grouped_equals_single_calls(qg):
     """Each group equals the single-matrix call on its slice, bit for bit."""
     g_ = np.random.default_rng(31)
-    for G, N, K, M in ((4, 200, 1024, 2), (3, 100, 2048, 9)):
-        _grouped_equals_singles(qg, g_, G, N, K, M)
+    for fmt, G, N, K, M in ((0, 4, 200, 1024, 2), (0, 3, 100, 2048, 9), (1, 3, 70, 1280, 11)):
+        _grouped_equals_singles(qg, g_, G, N, K, M, fmt)
 
 
-def _grouped_equals_singles(qg, g_, G, N, K, M):
+def _grouped_equals_singles(qg, g_, G, N, K, M, fmt=0):
     import torch
-    Ws = [synth.q8_0_weight(g_, N, K) for _ in range(G)]
+    Ws = [_weights(fmt, g_, N, K) for _ in range(G)]
     x = dev(synth.activations(g_, M, G * K))
     qx = torch.empty(M, G * K, dtype=torch.int8, device=x.device)
     dx = torch.empty(M, G * K // 32, dtype=torch.float32, device=x.device)
     sx = torch.empty(M, G * K // 32, dtype=torch.int32, device=x.device)
     qg.quantize_act_q8(x, M, G * K, qx, dx, sx)
     y = sentinel((M, G * N), torch.float32, 99.0)
-    qg.qgemv_grouped(0, dev(np.concatenate(Ws, axis=0)), G, N, K, qx, dx, sx, M, y)
+    qg.qgemv_grouped(fmt, dev(np.concatenate(Ws, axis=0)), G, N, K, qx, dx, sx, M, y)
     yh = host(y).reshape(M, G, N)
     for g in range(G):
         qs = qx[:, g * K:(g + 1) * K].contiguous()
         ds = dx[:, g * K // 32:(g + 1) * K // 32].contiguous()
+        ss = sx[:, g * K // 32:(g + 1) * K // 32].contiguous()
         y1 = sentinel((M, N), torch.float32, 99.0)
-        qg.qgemv_q8_0(dev(Ws[g]), N, K, qs, ds, M, y1)
+        if fmt == 0:
+            qg.qgemv_q8_0(dev(Ws[g]), N, K, qs, ds, M, y1)
+        else:
+            qg.qgemv_q4k(dev(Ws[g]), N, K, qs, ds, ss, M, y1)
         assert np.array_equal(host(y1).view(np.uint32), np.ascontiguousarray(yh[:, g]).view(np.uint32)), g
 
 
