@@ -285,8 +285,12 @@ size_t moe_routed_workspace_bytes(int T, int topk, int E, int D, int F);
 #define QG_WS_HD 9       /* fp32  [P, F/32] Q8 scales of h */
 #define QG_WS_HS 10      /* int32 [P, F/32] Q8 block sums of h */
 #define QG_WS_O 11       /* fp32  [P, D]   down outputs per pair */
-#define QG_WS_COUNT 12
-/* P = T * topk, Ucap = min(P, E).  Rows of pairs with an invalid id are not written. */
+#define QG_WS_HOT 12     /* int32 [1 + 2 Hcap] experts on the matrix cores: count, then per 32-pair
+                            tile (slot in uniq, first pair of the tile within the expert) */
+#define QG_WS_COUNT 13
+/* P = T * topk, Ucap = min(P, E), Hcap = P / 32 + P / QG_MOE_MM_PAIRS + 1.  Rows of pairs with an
+ * invalid id are not written. */
+#define QG_MOE_MM_PAIRS 9 /* Q4_K experts with this many pairs or more (T >= it) use the matrix cores */
 
 /*
  * moe_routed_workspace_layout -- byte offsets of the regions above, written
@@ -309,6 +313,10 @@ int moe_routed_workspace_layout(int T, int topk, int E, int D, int F, size_t *of
  *   3.   o_p = down_e . hq                              (Q4_K, D x F)
  *   4. y[t] = sum_k rw[t, k] * o_(t,k)   in k order (fp32).
  * Each selected expert's weights are streamed once for all of its pairs.
+ * With T >= QG_MOE_MM_PAIRS, experts with at least that many pairs run gate,
+ * up and down on the int8 matrix cores (32 pairs at a time, gathered through
+ * the pair list); their results equal the one-token form bit for bit, as for
+ * the dense batched calls.
  * gate/up/down are DEVICE arrays of E device pointers (pointer-backed expert
  * table); experts that are not selected are never dereferenced and may be
  * NULL.  The host never waits for the table: the number of distinct experts
@@ -316,10 +324,11 @@ int moe_routed_workspace_layout(int T, int topk, int E, int D, int F, size_t *of
  *
  * Data errors: an id outside [0, E) sets *d_status to QG_DEV_BAD_EXPERT, and
  * a selected expert whose gate, up or down pointer is NULL or not 16-byte
- * aligned sets QG_DEV_NULL_EXPERT (whichever is found first is kept); such a
- * pair gets slot -1, contributes 0 to y, and every other pair is still
- * computed.  Such an expert is left out of uniq.  *d_status is written with QG_DEV_OK first, on the
- * stream, so the caller reads it after synchronizing.
+ * aligned sets QG_DEV_NULL_EXPERT (a bad id takes precedence); such a pair
+ * gets slot -1, contributes 0 to y, and every other pair is still computed.
+ * Such an expert is left out of uniq.  *d_status (QG_DEV_OK otherwise) is
+ * written by the first launch, on the stream, so the caller reads it after
+ * synchronizing.
  *
  * Errors: QG_ERR_NULL (any pointer except unselected experts);
  * QG_ERR_SHAPE unless 1 <= T, 1 <= topk, T*topk <= QG_MAX_MOE_PAIRS,

@@ -29,7 +29,8 @@ FMT_FP8_E4M3_B128 = 2
 FMT_FP4_E2M1_MX = 3
 DEV_OK, DEV_BAD_EXPERT, DEV_NULL_EXPERT = 0, 1, 2
 MAX_K, MAX_M, MAX_MOE_PAIRS, MAX_EXPERTS = 16384, 32, 8192, 4096
-WS_REGIONS = ["NUNIQ", "UNIQ", "SLOT", "PAIR_OFF", "PAIRS", "G", "V", "H", "HQ", "HD", "HS", "O"]
+WS_REGIONS = ["NUNIQ", "UNIQ", "SLOT", "PAIR_OFF", "PAIRS", "G", "V", "H", "HQ", "HD", "HS", "O", "HOT"]
+MOE_MM_PAIRS = 9  # QG_MOE_MM_PAIRS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqgemv.so")

@@ -27,6 +27,7 @@
 // computes and quantizes h itself while staging it, so 3 is not launched.
 #include "common.h"
 #include "gemv_device.h"
+#include "mm_device.h"
 #include "mx_device.h"
 #include "quantize_device.h"
 
@@ -34,6 +35,12 @@ namespace qg {
 
 constexpr int kMoeWaves = 4;
 constexpr int kTableWords = QG_MAX_EXPERTS / 32;  // bitmap words over the expert ids
+// Q4_K experts with at least kMoeMm pairs run on the matrix cores (tiles of 32
+// pairs) when T >= kMoeMm; the dot-product kernels leave them out
+constexpr int kMoeMm = QG_MOE_MM_PAIRS;
+// matrix-core work items: a bound on the sum over such experts of their
+// 32-pair tiles (at most P / kMoeMm experts, P / 32 + one partial tile each)
+static inline int moe_mm_cap(int P) { return P / 32 + P / kMoeMm + 1; }
 
 struct MoeWs {
     int32_t *nuniq, *uniq, *slot, *pair_off, *pairs;
@@ -42,6 +49,7 @@ struct MoeWs {
     float *hd;
     int32_t *hs;
     float *o;
+    int32_t *hot;  // [0]: matrix-core work items; then (slot, first pair) per item
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -71,6 +79,7 @@ static size_t moe_layout(int T, int topk, int E, int D, int F, size_t off[QG_WS_
         4 * P * (F / 32),       // HD
         4 * P * (F / 32),       // HS
         4 * P * D,              // O
+        4 * (1 + 2 * (size_t)moe_mm_cap((int)P)),  // HOT
     };
     size_t at = 0;
     for (int i = 0; i < QG_WS_COUNT; ++i) {
@@ -103,7 +112,8 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
 // wpre[e/32] + popcount of the bits of word e/32 below e.
 __global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restrict__ ids, int P, int E,
                                                          const void *const *gate, const void *const *up,
-                                                         const void *const *down, MoeWs ws, int32_t *status) {
+                                                         const void *const *down, MoeWs ws, int32_t *status,
+                                                         int mm_on) {
     __shared__ uint32_t bm[kTableWords];
     __shared__ int wpre[kTableWords];
     __shared__ int cur[QG_MAX_EXPERTS];  // pairs per distinct expert, then the next free position
@@ -196,17 +206,31 @@ __global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restr
     // CSR offsets: lane l scans experts [l*per, (l+1)*per)
     const int per = (U + kWave - 1) / kWave;
     const int lo = min(U, l * per), hi = min(U, lo + per);
-    int sum = 0;
-    for (int u = lo; u < hi; ++u) sum += cur[u];
-    int npairs;
+    // (and the matrix-core work items: each 32-pair tile of an expert with
+    // at least kMoeMm pairs, in slot order)
+    int sum = 0, msum = 0;
+    for (int u = lo; u < hi; ++u) {
+        sum += cur[u];
+        if (mm_on && cur[u] >= kMoeMm) msum += (cur[u] + 31) / 32;
+    }
+    int npairs, nmm;
     int at = wave_exclusive_scan(sum, &npairs);
+    int mat = wave_exclusive_scan(msum, &nmm);
     for (int u = lo; u < hi; ++u) {
         const int n = cur[u];
         ws.pair_off[u] = at;
         cur[u] = at;
         at += n;
+        if (mm_on && n >= kMoeMm)
+            for (int m0 = 0; m0 < n; m0 += 32, ++mat) {
+                ws.hot[1 + 2 * mat] = u;
+                ws.hot[2 + 2 * mat] = m0;
+            }
     }
-    if (l == 0) ws.pair_off[U] = npairs;
+    if (l == 0) {
+        ws.pair_off[U] = npairs;
+        ws.hot[0] = nmm;
+    }
     lds_barrier();
     // stable fill, 64 pairs at a time: a pair's place among the chunk's pairs of
     // the same expert comes from a ballot over each distinct slot in the chunk
@@ -246,6 +270,7 @@ struct MoeArgs {
     MoeWs ws;
     TileGeom tg;  // of the projection this kernel runs
     int mt;       // tokens per LDS chunk
+    int mm_on;    // experts with kMoeMm pairs or more are left to the matrix-core kernels
 };
 
 using QU = Unit<QG_FMT_Q4K, 8>;
@@ -261,6 +286,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
     const int e = a.ws.uniq[u];
     const int p0 = a.ws.pair_off[u];
     const int cnt = a.ws.pair_off[u + 1] - p0;
+    if (a.mm_on && cnt >= kMoeMm) return;  // the matrix-core kernels take this expert
     const int ntiles = (a.F + a.tg.rpt - 1) / a.tg.rpt;
     const int nwg = (ntiles + kMoeWaves - 1) / kMoeWaves;
     const bool is_up = (int)blockIdx.x >= nwg;
@@ -301,6 +327,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     const int e = a.ws.uniq[u];
     const int p0 = a.ws.pair_off[u];
     const int cnt = a.ws.pair_off[u + 1] - p0;
+    if (a.mm_on && cnt >= kMoeMm) return;  // the matrix-core kernels take this expert
     const int ntiles = (a.D + a.tg.rpt - 1) / a.tg.rpt;
     const uint8_t *W = reinterpret_cast<const uint8_t *>(a.down[e]);
     const int32_t *pairs = a.ws.pairs + p0;
@@ -331,6 +358,73 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
             [=](int m) { return pairs[m]; }, [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; },
             [](int, int, int, const int32_t *) {});
     }
+}
+
+// Experts with kMoeMm pairs or more on the matrix cores: work item
+// blockIdx.y is one 32-pair tile of one such expert (the table lists them);
+// workgroup x takes a 32-row tile of gate (x < ntF) or up.  Same results, bit
+// for bit, as the dot-product kernels.
+template <int GPS>
+__global__ __launch_bounds__(kMmMaxSlices *kWave) void moe_mm_gate_up_kernel(MoeArgs a, int ks) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int item = blockIdx.y;
+    if (item >= load_uniform(a.ws.hot)) return;  // the whole workgroup leaves
+    const int u = load_uniform(a.ws.hot + 1 + 2 * item);
+    const int e = load_uniform(a.ws.uniq + u);
+    const int p0 = load_uniform(a.ws.pair_off + u);
+    const int ntF = (a.F + kMmRows - 1) / kMmRows;
+    const bool is_up = (int)blockIdx.x >= ntF;
+    MmTile t;
+    t.W = reinterpret_cast<const uint8_t *>(load_uniform(is_up ? a.up + e : a.gate + e));
+    t.N = a.F;
+    t.row0 = ((int)blockIdx.x - (is_up ? ntF : 0)) * kMmRows;
+    t.m0 = load_uniform(a.ws.hot + 2 + 2 * item);
+    t.M = load_uniform(a.ws.pair_off + u + 1) - p0;
+    t.qx = a.qx;
+    t.dx = a.dx;
+    t.sx = a.sx;
+    t.K = a.D;
+    t.row_bytes = a.D / 256 * 144;
+    t.groups = a.D / 256;
+    t.gps = GPS;
+    t.KS = ks;
+    const int32_t *pairs = a.ws.pairs + p0;
+    float *dst = is_up ? a.ws.v : a.ws.g;
+    const int topk = a.topk, F = a.F;
+    mm_tile<QG_FMT_Q4K, 8, GPS>(
+        t, [=](int m) { return pairs[m] / topk; }, [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; },
+        smem);
+}
+
+// down of the matrix-core experts against each pair's Q8 h
+template <int GPS>
+__global__ __launch_bounds__(kMmMaxSlices *kWave) void moe_mm_down_kernel(MoeArgs a, int ks) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int item = blockIdx.y;
+    if (item >= load_uniform(a.ws.hot)) return;
+    const int u = load_uniform(a.ws.hot + 1 + 2 * item);
+    const int e = load_uniform(a.ws.uniq + u);
+    const int p0 = load_uniform(a.ws.pair_off + u);
+    MmTile t;
+    t.W = reinterpret_cast<const uint8_t *>(load_uniform(a.down + e));
+    t.N = a.D;
+    t.row0 = (int)blockIdx.x * kMmRows;
+    t.m0 = load_uniform(a.ws.hot + 2 + 2 * item);
+    t.M = load_uniform(a.ws.pair_off + u + 1) - p0;
+    t.qx = a.ws.hq;
+    t.dx = a.ws.hd;
+    t.sx = a.ws.hs;
+    t.K = a.F;
+    t.row_bytes = a.F / 256 * 144;
+    t.groups = a.F / 256;
+    t.gps = GPS;
+    t.KS = ks;
+    const int32_t *pairs = a.ws.pairs + p0;
+    float *o = a.ws.o;
+    const int D = a.D;
+    mm_tile<QG_FMT_Q4K, 8, GPS>(
+        t, [=](int m) { return pairs[m]; }, [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; },
+        smem);
 }
 
 // Block-scaled expert formats (FP8 E4M3 128 x 128, FP4 E2M1 1 x 32): gate and
@@ -447,6 +541,7 @@ static MoeWs ws_pointers(void *ws, const size_t off[QG_WS_COUNT]) {
     w.hd = reinterpret_cast<float *>(b + off[QG_WS_HD]);
     w.hs = reinterpret_cast<int32_t *>(b + off[QG_WS_HS]);
     w.o = reinterpret_cast<float *>(b + off[QG_WS_O]);
+    w.hot = reinterpret_cast<int32_t *>(b + off[QG_WS_HOT]);
     return w;
 }
 
@@ -498,6 +593,42 @@ static int launch_moe_mx(const MoeArgs &a, int Ucap, bool down, hipStream_t st) 
 
 }  // namespace qg
 
+namespace qg {
+
+// The matrix-core expert kernels over `cap` possible work items; K = the
+// projection's input width, tiles = 32-row tiles per item.
+template <bool DOWN, int GPS>
+static int launch_moe_mm_gps(const MoeArgs &a, int tiles, int cap, int ks, hipStream_t st) {
+    static bool raised = false;  // idempotent: raising the dynamic-LDS limit once per kernel
+    auto kern = DOWN ? moe_mm_down_kernel<GPS> : moe_mm_gate_up_kernel<GPS>;
+    if (!raised) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kMmMaxSlices * mm_wave_lds<QG_FMT_Q4K>(GPS)) != hipSuccess)
+            return QG_ERR_LAUNCH;
+        raised = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(tiles, cap), dim3(ks * kWave), (size_t)ks * mm_wave_lds<QG_FMT_Q4K>(GPS), st, a, ks);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+template <bool DOWN>
+static int launch_moe_mm(const MoeArgs &a, int P, hipStream_t st) {
+    const int K = DOWN ? a.F : a.D, N = DOWN ? a.D : a.F;
+    const int tiles = (DOWN ? 1 : 2) * ((N + kMmRows - 1) / kMmRows);
+    const int cap = moe_mm_cap(P);
+    int ks, gps;
+    mm_slices(K / 256, (long)tiles * cap, &ks, &gps);
+    switch (gps) {
+        case 1: return launch_moe_mm_gps<DOWN, 1>(a, tiles, cap, ks, st);
+        case 2: return launch_moe_mm_gps<DOWN, 2>(a, tiles, cap, ks, st);
+        case 4: return launch_moe_mm_gps<DOWN, 4>(a, tiles, cap, ks, st);
+        case 8: return launch_moe_mm_gps<DOWN, 8>(a, tiles, cap, ks, st);
+        default: return QG_ERR_SHAPE;
+    }
+}
+
+}  // namespace qg
+
 extern "C" size_t moe_routed_workspace_bytes(int T, int topk, int E, int D, int F) {
     if (!qg::moe_shape_ok(T, topk, E, D, F)) return 0;
     size_t off[QG_WS_COUNT];
@@ -531,7 +662,10 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     const int Ucap = P < E ? P : E;
     MoeWs w = ws_pointers(ws, off);
 
-    hipLaunchKernelGGL(moe_table_kernel, dim3(1), dim3(kWave), 0, st, ids, P, E, gate, up, down, w, d_status);
+    // Q4_K experts with many pairs go to the matrix cores (possible from kMoeMm tokens on)
+    const int mm_on = fmt == QG_FMT_Q4K && T >= kMoeMm;
+    hipLaunchKernelGGL(moe_table_kernel, dim3(1), dim3(kWave), 0, st, ids, P, E, gate, up, down, w, d_status,
+                       mm_on);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
 
     MoeArgs a{};
@@ -546,6 +680,7 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     a.up = up;
     a.down = down;
     a.ws = w;
+    a.mm_on = mm_on;
     if (fmt != QG_FMT_Q4K) {
         // block-scaled experts: gate/up, h quantized once per pair, down, combine
         int rc = fmt == QG_FMT_FP8_E4M3_B128 ? launch_moe_mx<QG_FMT_FP8_E4M3_B128>(a, Ucap, false, st)
@@ -581,6 +716,10 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     else
         hipLaunchKernelGGL(moe_gate_up_kernel<false>, dim3(2 * nwg, Ucap), dim3(threads), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
+    if (mm_on) {
+        const int rc = launch_moe_mm<false>(a, P, st);
+        if (rc) return rc;
+    }
 
     // down: K = F.  One token: h = silu(g) * v staged from fp32 and quantized
     // there; several: h quantized once per pair first (each expert's
@@ -599,6 +738,10 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     else
         hipLaunchKernelGGL(moe_down_kernel<false>, dim3(nwg, Ucap), dim3(threads), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
+    if (mm_on) {
+        const int rc = launch_moe_mm<true>(a, P, st);
+        if (rc) return rc;
+    }
 
     const long long cthreads = (long long)T * (D / 4);
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cthreads + 255) / 256)), dim3(256), 0, st, w, rw, T, D,

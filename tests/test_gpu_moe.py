@@ -203,6 +203,42 @@ def test_moe_zipf_384_experts_t64_sampled(qg, orc):
     check_staged(qg, orc, pb, y, ws, pairs_to_check=pairs, tokens_to_check=toks)
 
 
+@pytest.mark.parametrize("E,D,F,T,topk,seed,zipf", [(4, 1280, 512, 48, 3, 41, False),
+                                                     (6, 512, 256, 40, 3, 42, False),
+                                                     (40, 768, 256, 12, 6, 43, True)])
+def test_moe_popular_experts_on_matrix_cores(qg, orc, E, D, F, T, topk, seed, zipf):
+    """From QG_MOE_MM_PAIRS tokens on, experts with that many pairs or more run on the
+    matrix cores: the work-item list is exact, every stage matches the oracle, and g, v
+    and o of those experts equal the one-token dense calls bit for bit (more than 32
+    pairs per expert, groups per row not a power of two; the last case mixes them with
+    experts on the dot-product kernels)."""
+    import torch
+    progress("moe matrix-core experts E=%d D=%d F=%d T=%d topk=%d" % (E, D, F, T, topk))
+    pb = MoeProblem(qg, E, D, F, T, topk, seed, zipf=zipf)
+    y, ws, st = pb.run()
+    assert st == 0
+    R = check_staged(qg, orc, pb, y, ws)
+    lay = qg.moe_routed_workspace_layout(T, topk, E, D, F)
+    raw = host(ws)
+    hot = raw[lay["HOT"]:].view(np.int32)
+    counts = np.diff(R["pair_off"])
+    want = [(u, m0) for u in range(R["n_uniq"]) if counts[u] >= qg.MOE_MM_PAIRS for m0 in range(0, counts[u], 32)]
+    assert hot[0] == len(want) and len(want) > 0
+    assert [tuple(hot[1 + 2 * i:3 + 2 * i]) for i in range(len(want))] == want
+    for u in sorted(set(u for u, _ in want)):
+        e = int(R["uniq"][u])
+        for p in R["pairs"][R["pair_off"][u]:R["pair_off"][u + 1]]:
+            t = int(p) // topk
+            for wd, key in ((pb.dgate[e], "g"), (pb.dup[e], "v")):
+                out = torch.empty(1, F, dtype=torch.float32, device="cuda")
+                qg.qgemv_q4k(wd, F, D, pb.qx[t:t + 1], pb.dx[t:t + 1], pb.sx[t:t + 1], 1, out)
+                assert np.array_equal(host(out)[0].view(np.uint32), R[key][p].view(np.uint32)), (key, p)
+            out = torch.empty(1, D, dtype=torch.float32, device="cuda")
+            qg.qgemv_q4k(pb.ddown[e], D, F, dev(R["hq"][p:p + 1]), dev(R["hd"][p:p + 1]), dev(R["hs"][p:p + 1]),
+                         1, out)
+            assert np.array_equal(host(out)[0].view(np.uint32), R["o"][p].view(np.uint32)), ("o", p)
+
+
 def test_moe_invariants(qg):
     pb = MoeProblem(qg, 20, 512, 256, 6, 6, 11)
     y, _, _ = pb.run()

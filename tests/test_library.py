@@ -87,11 +87,11 @@ def test_moe_workspace_sizing():
     P, Ucap = T * topk, min(T * topk, E)
     sizes = {"NUNIQ": 4, "UNIQ": 4 * Ucap, "SLOT": 4 * P, "PAIR_OFF": 4 * (Ucap + 1), "PAIRS": 4 * P,
              "G": 4 * P * F, "V": 4 * P * F, "H": 4 * P * F, "HQ": P * F, "HD": 4 * P * F // 32,
-             "HS": 4 * P * F // 32, "O": 4 * P * D}
+             "HS": 4 * P * F // 32, "O": 4 * P * D, "HOT": 4 * (1 + 2 * (P // 32 + P // qg.MOE_MM_PAIRS + 1))}
     names = qg.WS_REGIONS
     for a, b in zip(names, names[1:]):
         assert lay[b] >= lay[a] + sizes[a] and lay[b] % 256 == 0
-    assert nbytes >= lay["O"] + sizes["O"]
+    assert nbytes >= lay["HOT"] + sizes["HOT"]
     assert qg.moe_routed_workspace_bytes(8, 6, 256, 4000, 2048) == 0
     assert qg.moe_routed_workspace_bytes(2000, 6, 256, 4096, 2048) == 0  # more than 8192 pairs
     with pytest.raises(qg.QGError):
@@ -146,3 +146,15 @@ def test_mx_host_validation_without_gpu(lib):
     assert q(fake, 8, 512, fake, fake, 65537, fake, None) == -2
     assert q(fake, 8, 384 + 1, fake, fake, 64, fake, None) == -2
     assert q(fake, 8, 512, None, fake, 64, fake, None) == -1
+
+
+def test_workspace_regions_match_header():
+    """The binding's region list and the matrix-core pair threshold are the header's."""
+    import re
+    import routed_moe_matvec_amd as qg
+    hdr = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    regions = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define QG_WS_(\w+) (\d+)", hdr)}
+    count = regions.pop("COUNT")
+    assert count == len(qg.WS_REGIONS)
+    assert [name for name, _ in sorted(regions.items(), key=lambda kv: kv[1])] == qg.WS_REGIONS
+    assert int(re.search(r"#define QG_MOE_MM_PAIRS (\d+)", hdr).group(1)) == qg.MOE_MM_PAIRS
