@@ -616,8 +616,10 @@ static int launch_moe_mm(const MoeArgs &a, int P, hipStream_t st) {
     const int K = DOWN ? a.F : a.D, N = DOWN ? a.D : a.F;
     const int tiles = (DOWN ? 1 : 2) * ((N + kMmRows - 1) / kMmRows);
     const int cap = moe_mm_cap(P);
+    // the most slices: few of the cap work items are real (the popular
+    // experts of a batch), so each wave should take few groups
     int ks, gps;
-    mm_slices(K / 256, (long)tiles * cap, &ks, &gps);
+    mm_slices(K / 256, 1, &ks, &gps);
     switch (gps) {
         case 1: return launch_moe_mm_gps<DOWN, 1>(a, tiles, cap, ks, st);
         case 2: return launch_moe_mm_gps<DOWN, 2>(a, tiles, cap, ks, st);
