@@ -307,6 +307,12 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
                 W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p / topk; },
                 [=](int, int row, float v) { dst[(size_t)p * F + row] = v; }, [](int, int, int, const int32_t *) {});
         }
+    } else if (cnt == 1) {
+        // a one-pair expert of a batch: the one-token form, its token read once as a scalar
+        const int p = load_uniform(pairs);
+        gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8>(
+            W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p / topk; },
+            [=](int, int row, float v) { dst[(size_t)p * F + row] = v; }, [](int, int, int, const int32_t *) {});
     } else {
         gemv_workgroup<QG_FMT_Q4K, 8, false, false, false, kSrcQ8>(
             W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, cnt, a.mt, smem, [=](int m) { return pairs[m] / topk; },
@@ -353,6 +359,13 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
         hq.qx = a.ws.hq;
         hq.dx = a.ws.hd;
         hq.sx = a.ws.hs;
+        if (cnt == 1) {
+            const int p = load_uniform(pairs);
+            gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8>(
+                W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, hq, 1, a.mt, smem, [=](int) { return p; },
+                [=](int, int row, float v) { o[(size_t)p * D + row] = v; }, [](int, int, int, const int32_t *) {});
+            return;
+        }
         gemv_workgroup<QG_FMT_Q4K, 8, false, false, false, kSrcQ8>(
             W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, hq, cnt, a.mt, smem,
             [=](int m) { return pairs[m]; }, [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; },
@@ -445,6 +458,15 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs
     float *dst = is_up ? a.ws.v : a.ws.g;
     const int32_t *pairs = a.ws.pairs + p0;
     const int topk = a.topk, F = a.F;
+    if (cnt == 1) {
+        // one pair (the usual case in decode): its token is read once, as a
+        // scalar, so no vector load has to return before the weights are requested
+        const int p = load_uniform(pairs), tok = p / topk;
+        mx_workgroup<FMT, CPL, kMxLoadsRouted>(
+            W, F, a.D, wg * kMxWaves * R, 1, a.mt, a.qx, a.dx, [=](int) { return tok; },
+            [=](int, int row, float v) { dst[(size_t)p * F + row] = v; }, smem);
+        return;
+    }
     mx_workgroup<FMT, CPL, kMxLoadsRouted>(
         W, F, a.D, wg * kMxWaves * R, cnt, a.mt, a.qx, a.dx, [=](int m) { return pairs[m] / topk; },
         [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; }, smem);
@@ -464,6 +486,13 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_down_mx_kernel(MoeArgs a)
     const int32_t *pairs = a.ws.pairs + p0;
     float *o = a.ws.o;
     const int D = a.D;
+    if (cnt == 1) {
+        const int p = load_uniform(pairs);
+        mx_workgroup<FMT, CPL, kMxLoadsRouted>(
+            W, D, a.F, (int)blockIdx.x * kMxWaves * R, 1, a.mt, a.ws.hq, a.ws.hd, [=](int) { return p; },
+            [=](int, int row, float v) { o[(size_t)p * D + row] = v; }, smem);
+        return;
+    }
     mx_workgroup<FMT, CPL, kMxLoadsRouted>(
         W, D, a.F, (int)blockIdx.x * kMxWaves * R, cnt, a.mt, a.ws.hq, a.ws.hd, [=](int m) { return pairs[m]; },
         [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; }, smem);
