@@ -105,9 +105,8 @@ static int launch_gemv(GemvArgs &a, hipStream_t stream) {
     const int per_wg = a.waves * a.tpw;
     a.nwg0 = (a.nt0 + per_wg - 1) / per_wg;
     const int grid = a.nwg0 + (a.nt1 + per_wg - 1) / per_wg;
-    if (a.M == 1)
-        return a.tpw > 1 ? launch_kernel<FMT, NB, DEBUG_ISUM, true, true, F32>(a, grid, lds, stream)
-                         : launch_kernel<FMT, NB, DEBUG_ISUM, false, true, F32>(a, grid, lds, stream);
+    if (a.M == 1)  // (one token: tiles_per_wave gives 1)
+        return launch_kernel<FMT, NB, DEBUG_ISUM, false, true, F32>(a, grid, lds, stream);
     return a.tpw > 1 ? launch_kernel<FMT, NB, DEBUG_ISUM, true, false, F32>(a, grid, lds, stream)
                      : launch_kernel<FMT, NB, DEBUG_ISUM, false, false, F32>(a, grid, lds, stream);
 }

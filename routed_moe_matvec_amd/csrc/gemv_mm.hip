@@ -40,7 +40,7 @@ struct MmArgs {
     float *y0, *y1;
     int N0, N1;
     int nt0;  // 32-row tiles of matrix 0; matrix 1's follow
-    int ntok; // 32-token tiles: workgroup x takes row tile x / ntok, token tile x % ntok
+    int ntok; // token blocks of TT x 32 tokens: workgroup x takes row tile x / ntok, block x % ntok
     const int8_t *qx;
     const float *dx;
     const int32_t *sx;  // Q4_K: block sums of the activation
@@ -51,7 +51,7 @@ struct MmArgs {
     int KS;      // slices = waves per workgroup
 };
 
-template <int FMT, int NB, int GPS>
+template <int FMT, int NB, int GPS, int TT>
 __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_kernel(MmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // token tiles of one row tile are neighbours in the launch order, so the
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_kernel(MmArgs a)
     t.N = second ? a.N1 : a.N0;
     t.W = (second ? a.W1 : a.W0) + (size_t)g * t.N * a.row_bytes;
     t.row0 = (second ? rtile - a.nt0 : rtile) * kMmRows;
-    t.m0 = ((int)blockIdx.x - rtile * a.ntok) * kMmTokens;
+    t.m0 = ((int)blockIdx.x - rtile * a.ntok) * kMmTokens * TT;
     t.M = a.M;
     t.qx = a.qx;
     t.dx = a.dx;
@@ -77,41 +77,63 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_kernel(MmArgs a)
     t.KS = a.KS;
     float *y = second ? a.y1 : a.y0;
     const int N = t.N;
-    mm_tile<FMT, NB, GPS>(
+    mm_tile<FMT, NB, GPS, TT>(
         t, [=](int m) { return m * G + g; }, [=](int m, int row, float v) { y[((size_t)m * G + g) * N + row] = v; },
         smem);
 }
 
-template <int FMT, int NB, int GPS>
+// Dynamic LDS of a workgroup of KS slices x TT token tiles.
+template <int FMT>
+constexpr size_t mm_lds_bytes(int gps, int ks, int tt) {
+    return tt == 1 ? (size_t)ks * mm_wave_lds<FMT>(gps)
+                   : (size_t)ks * 2 * mm_stage_bytes<FMT>() + (size_t)ks * tt * (mm_wave_lds<FMT>(gps) - mm_stage_bytes<FMT>());
+}
+
+template <int FMT, int NB, int GPS, int TT>
 static int launch_mm_gps(const MmArgs &a, int nt1, hipStream_t stream) {
     static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_mm_kernel<FMT, NB, GPS>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kMmMaxSlices * mm_wave_lds<FMT>(GPS)) != hipSuccess)
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_mm_kernel<FMT, NB, GPS, TT>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
             return QG_ERR_LAUNCH;
         attr_set = true;
     }
-    hipLaunchKernelGGL((qgemv_mm_kernel<FMT, NB, GPS>), dim3((a.nt0 + nt1) * a.ntok, a.G), dim3(a.KS * kWave),
-                       (size_t)a.KS * mm_wave_lds<FMT>(GPS), stream, a);
+    hipLaunchKernelGGL((qgemv_mm_kernel<FMT, NB, GPS, TT>), dim3((a.nt0 + nt1) * a.ntok, a.G),
+                       dim3(a.KS * TT * kWave), mm_lds_bytes<FMT>(GPS, a.KS, TT), stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
+template <int FMT, int NB, int TT>
+static int launch_mm_tt(const MmArgs &a, int nt1, hipStream_t stream) {
+    switch (a.gps) {
+        case 1: return launch_mm_gps<FMT, NB, 1, TT>(a, nt1, stream);
+        case 2: return launch_mm_gps<FMT, NB, 2, TT>(a, nt1, stream);
+        case 4: return launch_mm_gps<FMT, NB, 4, TT>(a, nt1, stream);
+        case 8: return launch_mm_gps<FMT, NB, 8, TT>(a, nt1, stream);
+        default: return QG_ERR_SHAPE;
+    }
+}
+
+// K slices as mm_slices chooses them; with several 32-token tiles (prefill)
+// TT tiles of Q8_0 share each slice's weight stage (at most 8 waves), so a
+// row tile's weights are read once per TT x 32 tokens.
 template <int FMT, int NB>
 static int launch_mm(MmArgs &a, hipStream_t stream) {
     a.row_bytes = a.K / 256 * MmFmt<FMT>::parts * 16;
     a.groups = a.K / 256;
     const int nt1 = a.W1 ? (a.N1 + kMmRows - 1) / kMmRows : 0;
     a.nt0 = (a.N0 + kMmRows - 1) / kMmRows;
-    a.ntok = (a.M + kMmTokens - 1) / kMmTokens;
-    mm_slices(a.groups, (long)(a.nt0 + nt1) * a.G * a.ntok, &a.KS, &a.gps);
-    switch (a.gps) {
-        case 1: return launch_mm_gps<FMT, NB, 1>(a, nt1, stream);
-        case 2: return launch_mm_gps<FMT, NB, 2>(a, nt1, stream);
-        case 4: return launch_mm_gps<FMT, NB, 4>(a, nt1, stream);
-        case 8: return launch_mm_gps<FMT, NB, 8>(a, nt1, stream);
-        default: return QG_ERR_SHAPE;
+    const int ntok32 = (a.M + kMmTokens - 1) / kMmTokens;
+    mm_slices(a.groups, (long)(a.nt0 + nt1) * a.G * ntok32, &a.KS, &a.gps);
+    int tt = 1;
+    if (FMT == QG_FMT_Q8_0)
+        while (tt < 4 && 2 * tt <= ntok32 && a.KS * 2 * tt <= kMmMaxSlices) tt <<= 1;
+    a.ntok = (ntok32 + tt - 1) / tt;
+    if constexpr (FMT == QG_FMT_Q8_0) {
+        if (tt == 4) return launch_mm_tt<FMT, NB, 4>(a, nt1, stream);
+        if (tt == 2) return launch_mm_tt<FMT, NB, 2>(a, nt1, stream);
     }
+    return launch_mm_tt<FMT, NB, 1>(a, nt1, stream);
 }
 
 int gemv_mm(int fmt, const uint8_t *W0, int N0, float *y0, const uint8_t *W1, int N1, float *y1, int K,

@@ -61,36 +61,49 @@ struct MmTile {
     int K, row_bytes, groups, gps, KS;
 };
 
-template <int FMT, int NB, int GPS, class ActRow, class Out>
+template <int FMT, int NB, int GPS, int TT, class ActRow, class Out>
 __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out, uint8_t *smem) {
     using F = MmFmt<FMT>;
-    constexpr int kParts = F::parts, kLoads = mm_loads<FMT>(), kGroupBytes = kParts * 16;
+    static_assert(TT == 1 || FMT == QG_FMT_Q8_0, "token tiles share a stage for Q8_0 only");
+    constexpr int kParts = F::parts, kGroupBytes = kParts * 16, kStage = mm_stage_bytes<FMT>();
+    // TT token tiles of 32 share each slice's stage: a wave loads 1/TT of a group
+    constexpr int kChunks = kParts * kMmRows, kShare = kChunks / TT, kLoads = (kShare + kWave - 1) / kWave;
+    static_assert(kShare * TT == kChunks && kLoads >= 2, "stage share");
     // the wave index is uniform over the wave: keep it (and every slice bound) scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int KS = t.KS;
+    const int sl = TT == 1 ? wave : wave % KS;  // K slice
+    const int tt = TT == 1 ? 0 : wave / KS;     // token tile within the workgroup
     const uint8_t *W = t.W;
-    const int N = t.N, row0 = t.row0, m0 = t.m0;
+    const int N = t.N, row0 = t.row0, m0 = t.m0 + kMmTokens * tt;
+    // LDS: TT = 1, per wave [stage | table | levels]; TT > 1, per slice two
+    // stages (double-buffered: one barrier per group), then per wave
+    // [table | levels]
     constexpr int kWaveLds = mm_wave_lds<FMT>(GPS);
-    uint8_t *stage = smem + wave * kWaveLds;
-    uint8_t *stab = stage + mm_stage_bytes<FMT>();
+    uint8_t *stage0 = TT == 1 ? smem + wave * kWaveLds : smem + sl * 2 * kStage;
+    uint8_t *stab = TT == 1 ? stage0 + kStage : smem + KS * 2 * kStage + wave * (kWaveLds - kStage);
 
-    const int grp0 = wave * t.gps;
+    const int grp0 = sl * t.gps;
     const int ngroups = min(max(t.groups - grp0, 0), t.gps);
 
     // Group loads: the 32 rows x kParts parts (16 bytes) of a group in row
-    // order, instruction i / lane l taking chunk 64 i + l = kParts r + p, so
+    // order, chunk c = kParts r + p; the wave's share is chunks tt kShare ..
+    // + kShare, instruction i / lane l taking chunk tt kShare + 64 i + l, so
     // that an instruction reads a few contiguous runs of a row's group (few
     // cache lines per instruction: the address units, not HBM, bounded an
-    // earlier pattern of 16 rows x 64 bytes).  The last instruction has 32
-    // chunks: its lanes 32..63 repeat lanes 0..31 and do not store.  Rows past
-    // N re-read row N - 1.
+    // earlier pattern of 16 rows x 64 bytes).  Lanes past the share repeat the
+    // chunk 64 before (the same bytes to the same place).  Rows past N re-read
+    // row N - 1.
     const int r32 = lane & 31, half = lane >> 5;
     const uint8_t *wt = W + (size_t)row0 * t.row_bytes;
-    uint32_t goff[kLoads];
+    uint32_t goff[kLoads], soff[TT == 1 ? 1 : kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-        const int idx = i < kLoads - 1 ? 64 * i + lane : 64 * (kLoads - 1) + r32;
+        int idx = tt * kShare + 64 * i + lane;
+        if (idx >= (tt + 1) * kShare) idx -= 64;
         const int r = idx / kParts, p = idx - kParts * r;
         goff[i] = (uint32_t)(min(row0 + r, N - 1) - row0) * (uint32_t)t.row_bytes + 16u * p;
+        if constexpr (TT > 1) soff[i] = 16u * idx;
     }
     // activation: token lane % 32 (tokens past M re-read token M - 1; their
     // columns are not stored), 16 quants of each block per lane half
@@ -121,10 +134,16 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     // kParts r + p at 16 times that, so the loads' chunks are written
     // linearly; a 16-lane pass reading one part of 16 rows hits 16 different
     // 16-byte bank groups (row strides of 68 and 36 dwords).
-    auto store_w = [&](const u32x4 (&w)[kLoads]) __attribute__((always_inline)) {
+    auto store_w = [&](uint8_t *stage, const u32x4 (&w)[kLoads]) __attribute__((always_inline)) {
+        if constexpr (TT == 1) {
+            // chunk 64 i + l; the last instruction's lanes 32..63 hold repeats
 #pragma unroll
-        for (int i = 0; i < kLoads - 1; ++i) *reinterpret_cast<u32x4 *>(stage + 16 * (64 * i + lane)) = w[i];
-        if (lane < 32) *reinterpret_cast<u32x4 *>(stage + 16 * (64 * (kLoads - 1) + lane)) = w[kLoads - 1];
+            for (int i = 0; i < kLoads - 1; ++i) *reinterpret_cast<u32x4 *>(stage + 16 * (64 * i + lane)) = w[i];
+            if (lane < 32) *reinterpret_cast<u32x4 *>(stage + 16 * (64 * (kLoads - 1) + lane)) = w[kLoads - 1];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) *reinterpret_cast<u32x4 *>(stage + soff[i]) = w[i];
+        }
     };
     // A-operand reads: part p0 + half of row lane % 32 sits at abase + 16 p0
     const int abase = kParts * 16 * r32 + 16 * half;
@@ -133,7 +152,7 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     // block scales [block][slot]; Q4_K d*sc_j and dmin*m_j as fp32
     // [sub-block][a | bm][slot] (exact products: 11-bit by 6-bit)
     const int slot = ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
-    auto build_scales = [&]() __attribute__((always_inline)) {
+    auto build_scales = [&](const uint8_t *stage) __attribute__((always_inline)) {
         if constexpr (FMT == QG_FMT_Q8_0) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -207,6 +226,7 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     // row's last group for an empty slice): loads past the slice's end re-read
     // a valid group and are not used.
     auto gclamp = [&](int j) __attribute__((always_inline)) {
+        // (slices past the row's end re-read its last group: loads only)
         return min(grp0 + min(j, max(ngroups - 1, 0)), t.groups - 1);
     };
     // Weights are requested two groups ahead (two register sets), activations
@@ -230,8 +250,10 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
         const int gnext = gclamp(s + 1);
         // steps are not interleaved by the scheduler (registers)
         __builtin_amdgcn_sched_barrier(0);
-        store_w(wreg[s & 1]);
-        build_scales();
+        uint8_t *stage = TT == 1 ? stage0 : stage0 + (s & 1) * kStage;
+        store_w(stage, wreg[s & 1]);
+        if constexpr (TT > 1) lds_barrier();  // the slice's whole group is staged
+        build_scales(stage);
         float4 dxn[4];
         if constexpr (PF2) load_w(gclamp(s + 2), wreg[s & 1]);
         if constexpr (PF) load_dx(gnext, dxn);
@@ -336,19 +358,25 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
         }
     };
     static_assert(GPS == 1 || GPS == 2 || GPS == 4 || GPS == 8, "groups per slice");
-    if (ngroups > 0) step(std::integral_constant<int, 0>{});
-    if constexpr (GPS > 1) {
-        if (ngroups > 1) step(std::integral_constant<int, 1>{});
-    }
+    // with shared stages every wave takes part in every step's barrier, also
+    // past the end of a partial slice
+    auto run = [&](auto index) __attribute__((always_inline)) {
+        if (ngroups > decltype(index)::value)
+            step(index);
+        else if constexpr (TT > 1)
+            lds_barrier();
+    };
+    run(std::integral_constant<int, 0>{});
+    if constexpr (GPS > 1) run(std::integral_constant<int, 1>{});
     if constexpr (GPS > 2) {
-        if (ngroups > 2) step(std::integral_constant<int, 2>{});
-        if (ngroups > 3) step(std::integral_constant<int, 3>{});
+        run(std::integral_constant<int, 2>{});
+        run(std::integral_constant<int, 3>{});
     }
     if constexpr (GPS > 4) {
-        if (ngroups > 4) step(std::integral_constant<int, 4>{});
-        if (ngroups > 5) step(std::integral_constant<int, 5>{});
-        if (ngroups > 6) step(std::integral_constant<int, 6>{});
-        if (ngroups > 7) step(std::integral_constant<int, 7>{});
+        run(std::integral_constant<int, 4>{});
+        run(std::integral_constant<int, 5>{});
+        run(std::integral_constant<int, 6>{});
+        run(std::integral_constant<int, 7>{});
     }
 
     // The slice's subtree: top for a full slice; else the pending levels of
@@ -373,17 +401,21 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
             r[e] = t;
         }
     }
-    // slices meet in LDS (each wave overwrites only its own stage)
-    float *comb = reinterpret_cast<float *>(stage);
+    // slices meet in LDS: TT = 1, in each wave's own stage; TT > 1, in its
+    // slice's stages (4 KiB per token tile) once every wave is done with them
+    static_assert(TT == 1 || TT * 4096 <= 2 * kStage, "combine area");
+    auto comb_at = [&](int s_) __attribute__((always_inline)) {
+        return reinterpret_cast<float *>(TT == 1 ? smem + s_ * kWaveLds : smem + s_ * 2 * kStage + tt * 4096);
+    };
+    if constexpr (TT > 1) lds_barrier();
+    float *comb = comb_at(sl);
 #pragma unroll
     for (int e = 0; e < 16; ++e) comb[e * 64 + lane] = r[e];
-    __syncthreads();
-    const int KS = t.KS;
-    for (int idx = threadIdx.x; idx < 16 * 64; idx += KS * kWave) {
+    lds_barrier();
+    for (int idx = sl * kWave + lane; idx < 16 * 64; idx += KS * kWave) {
         float v[kMmMaxSlices];
 #pragma unroll
-        for (int s = 0; s < kMmMaxSlices; ++s)
-            v[s] = s < KS ? reinterpret_cast<const float *>(smem + s * kWaveLds)[idx] : 0.0f;
+        for (int s = 0; s < kMmMaxSlices; ++s) v[s] = s < KS ? comb_at(s)[idx] : 0.0f;
 #pragma unroll
         for (int w = 1; w < kMmMaxSlices; w <<= 1)
 #pragma unroll

@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void moe_mm_gate_up_kernel(Moe
     const int32_t *pairs = a.ws.pairs + p0;
     float *dst = is_up ? a.ws.v : a.ws.g;
     const int topk = a.topk, F = a.F;
-    mm_tile<QG_FMT_Q4K, 8, GPS>(
+    mm_tile<QG_FMT_Q4K, 8, GPS, 1>(
         t, [=](int m) { return pairs[m] / topk; }, [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; },
         smem);
 }
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void moe_mm_down_kernel(MoeArg
     const int32_t *pairs = a.ws.pairs + p0;
     float *o = a.ws.o;
     const int D = a.D;
-    mm_tile<QG_FMT_Q4K, 8, GPS>(
+    mm_tile<QG_FMT_Q4K, 8, GPS, 1>(
         t, [=](int m) { return pairs[m]; }, [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; },
         smem);
 }

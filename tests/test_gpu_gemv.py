@@ -468,11 +468,17 @@ def test_grouped_errors(qg):
 
 PREFILL_Q8_0_CASES = [
     # N, K, M: ragged token tiles and row tiles, partial K slices, the 8-block
-    # unit, a prefill-sized batch (sampled outputs)
+    # unit, a prefill-sized batch (sampled outputs); then workgroups whose
+    # token tiles share the weight stage: 4 tiles with a partial slice (5 of 8
+    # groups), 2 tiles (K = 8192), 4 tiles with a partial second slice and a
+    # last token block that holds an empty tile
     (100, 1280, 77),
     (333, 2048, 100),
     (64, 16384, 65),
     (1024, 4096, 512),
+    (4096, 1280, 500),
+    (2048, 8192, 300),
+    (8192, 2304, 200),
 ]
 
 
