@@ -34,6 +34,10 @@
 namespace qg {
 
 constexpr int kMoeWaves = 4;
+// tokens staged at once by the several-token expert kernels: most experts of
+// a decode batch have one or two pairs, and a smaller staging area lets three
+// workgroups share a CU's LDS instead of two
+constexpr int kMoeChunk = 2;
 constexpr int kTableWords = QG_MAX_EXPERTS / 32;  // bitmap words over the expert ids
 // Q4_K experts with at least kMoeMm pairs run on the matrix cores (tiles of 32
 // pairs) when T >= kMoeMm; the dot-product kernels leave them out
@@ -739,7 +743,7 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
 
     // gate/up: K = D, Q8 activation of the tokens
     a.tg = make_tile_geom<QU>(D);
-    a.mt = one ? 1 : tokens_per_chunk<QU>(D, QG_MAX_MOE_PAIRS, threads);
+    a.mt = one ? 1 : min(kMoeChunk, tokens_per_chunk<QU>(D, QG_MAX_MOE_PAIRS, threads));
     size_t lds = gemv_lds_bytes<QU>(kMoeWaves, D, a.mt);
     int nwg = ((F + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
     if (one)
@@ -761,7 +765,7 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
         if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
     }
     a.tg = make_tile_geom<QU>(F);
-    a.mt = one ? 1 : tokens_per_chunk<QU>(F, QG_MAX_MOE_PAIRS, threads);
+    a.mt = one ? 1 : min(kMoeChunk, tokens_per_chunk<QU>(F, QG_MAX_MOE_PAIRS, threads));
     lds = gemv_lds_bytes<QU>(kMoeWaves, F, a.mt);
     nwg = ((D + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
     if (one)
