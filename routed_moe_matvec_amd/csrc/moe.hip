@@ -546,15 +546,31 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeWs ws, const float 
     if (gid >= T * per_t) return;
     const int t = gid / per_t, n4 = gid - t * per_t;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < topk; ++k) {
-        const int p = t * topk + k;
-        if (ws.slot[p] < 0) continue;  // invalid id or unusable expert: contributes nothing
-        const float r = rw[p];
-        const float4 o = *reinterpret_cast<const float4 *>(ws.o + (size_t)p * D + 4 * n4);
-        acc.x = fmaf_exact(r, o.x, acc.x);
-        acc.y = fmaf_exact(r, o.y, acc.y);
-        acc.z = fmaf_exact(r, o.z, acc.z);
-        acc.w = fmaf_exact(r, o.w, acc.w);
+    // eight pairs at a time: every load is issued before the first use (a
+    // load behind a branch on the slot would wait twice per pair); pairs past
+    // topk re-read the last one and are not used
+    constexpr int kU = 8;
+    for (int k0 = 0; k0 < topk; k0 += kU) {
+        int sl[kU];
+        float r[kU];
+        float4 o[kU];
+#pragma unroll
+        for (int j = 0; j < kU; ++j) {
+            const int p = t * topk + min(k0 + j, topk - 1);
+            sl[j] = ws.slot[p];
+            r[j] = rw[p];
+            o[j] = *reinterpret_cast<const float4 *>(ws.o + (size_t)p * D + 4 * n4);
+        }
+#pragma unroll
+        for (int j = 0; j < kU; ++j) {
+            // an invalid id or unusable expert (slot -1) contributes nothing
+            if (k0 + j < topk && sl[j] >= 0) {
+                acc.x = fmaf_exact(r[j], o[j].x, acc.x);
+                acc.y = fmaf_exact(r[j], o[j].y, acc.y);
+                acc.z = fmaf_exact(r[j], o[j].z, acc.z);
+                acc.w = fmaf_exact(r[j], o[j].w, acc.w);
+            }
+        }
     }
     *reinterpret_cast<float4 *>(y + (size_t)t * D + 4 * n4) = acc;
 }
