@@ -277,6 +277,19 @@ struct MoeArgs {
     int mm_on;    // experts with kMoeMm pairs or more are left to the matrix-core kernels
 };
 
+// Expert slot u of the table: its id, first pair and pair count; false when
+// u is past the number of distinct experts.  The four values are read
+// together and all of them decide the result, so none is deferred past it.
+__device__ __forceinline__ bool moe_slot(const MoeWs &ws, int u, int *e, int *p0, int *cnt) {
+    const int nu = load_uniform(ws.nuniq);
+    const int id = load_uniform(ws.uniq + u);
+    const int a = load_uniform(ws.pair_off + u), b = load_uniform(ws.pair_off + u + 1);
+    *e = id;
+    *p0 = a;
+    *cnt = b - a;
+    return u < nu && id >= 0 && b > a;
+}
+
 using QU = Unit<QG_FMT_Q4K, 8>;
 
 // gate and up of expert uniq[blockIdx.y]: workgroups [0, nwg) take gate rows,
@@ -286,16 +299,17 @@ template <bool ONE>
 __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int u = blockIdx.y;
-    if (u >= *a.ws.nuniq) return;  // the whole workgroup leaves
-    const int e = a.ws.uniq[u];
-    const int p0 = a.ws.pair_off[u];
-    const int cnt = a.ws.pair_off[u + 1] - p0;
+    // the expert's entry is read with the count (blockIdx.y < Ucap keeps it
+    // inside the table), all as scalars in one round trip; the slots past the
+    // count leave
+    int e, p0, cnt;
+    if (!moe_slot(a.ws, u, &e, &p0, &cnt)) return;  // the whole workgroup leaves
     if (a.mm_on && cnt >= kMoeMm) return;  // the matrix-core kernels take this expert
     const int ntiles = (a.F + a.tg.rpt - 1) / a.tg.rpt;
     const int nwg = (ntiles + kMoeWaves - 1) / kMoeWaves;
     const bool is_up = (int)blockIdx.x >= nwg;
     const int wg = is_up ? (int)blockIdx.x - nwg : (int)blockIdx.x;
-    const uint8_t *W = reinterpret_cast<const uint8_t *>(is_up ? a.up[e] : a.gate[e]);
+    const uint8_t *W = reinterpret_cast<const uint8_t *>(load_uniform(is_up ? a.up + e : a.gate + e));
     float *dst = is_up ? a.ws.v : a.ws.g;
     const int32_t *pairs = a.ws.pairs + p0;
     const int topk = a.topk, F = a.F;
@@ -333,13 +347,14 @@ template <bool ONE>
 __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int u = blockIdx.y;
-    if (u >= *a.ws.nuniq) return;
-    const int e = a.ws.uniq[u];
-    const int p0 = a.ws.pair_off[u];
-    const int cnt = a.ws.pair_off[u + 1] - p0;
+    // the expert's entry is read with the count (blockIdx.y < Ucap keeps it
+    // inside the table), all as scalars in one round trip; the slots past the
+    // count leave
+    int e, p0, cnt;
+    if (!moe_slot(a.ws, u, &e, &p0, &cnt)) return;  // the whole workgroup leaves
     if (a.mm_on && cnt >= kMoeMm) return;  // the matrix-core kernels take this expert
     const int ntiles = (a.D + a.tg.rpt - 1) / a.tg.rpt;
-    const uint8_t *W = reinterpret_cast<const uint8_t *>(a.down[e]);
+    const uint8_t *W = reinterpret_cast<const uint8_t *>(load_uniform(a.down + e));
     const int32_t *pairs = a.ws.pairs + p0;
     float *o = a.ws.o;
     const int D = a.D;
@@ -452,13 +467,14 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int R = mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int u = blockIdx.y;
-    if (u >= *a.ws.nuniq) return;  // the whole workgroup leaves
-    const int e = a.ws.uniq[u];
-    const int p0 = a.ws.pair_off[u];
-    const int cnt = a.ws.pair_off[u + 1] - p0;
+    // the expert's entry is read with the count (blockIdx.y < Ucap keeps it
+    // inside the table), all as scalars in one round trip; the slots past the
+    // count leave
+    int e, p0, cnt;
+    if (!moe_slot(a.ws, u, &e, &p0, &cnt)) return;  // the whole workgroup leaves
     const bool is_up = (int)blockIdx.x >= nwg;
     const int wg = is_up ? (int)blockIdx.x - nwg : (int)blockIdx.x;
-    const uint8_t *W = reinterpret_cast<const uint8_t *>(is_up ? a.up[e] : a.gate[e]);
+    const uint8_t *W = reinterpret_cast<const uint8_t *>(load_uniform(is_up ? a.up + e : a.gate + e));
     float *dst = is_up ? a.ws.v : a.ws.g;
     const int32_t *pairs = a.ws.pairs + p0;
     const int topk = a.topk, F = a.F;
@@ -482,11 +498,12 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_down_mx_kernel(MoeArgs a)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int R = mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int u = blockIdx.y;
-    if (u >= *a.ws.nuniq) return;
-    const int e = a.ws.uniq[u];
-    const int p0 = a.ws.pair_off[u];
-    const int cnt = a.ws.pair_off[u + 1] - p0;
-    const uint8_t *W = reinterpret_cast<const uint8_t *>(a.down[e]);
+    // the expert's entry is read with the count (blockIdx.y < Ucap keeps it
+    // inside the table), all as scalars in one round trip; the slots past the
+    // count leave
+    int e, p0, cnt;
+    if (!moe_slot(a.ws, u, &e, &p0, &cnt)) return;  // the whole workgroup leaves
+    const uint8_t *W = reinterpret_cast<const uint8_t *>(load_uniform(a.down + e));
     const int32_t *pairs = a.ws.pairs + p0;
     float *o = a.ws.o;
     const int D = a.D;
