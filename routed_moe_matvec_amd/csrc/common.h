@@ -56,10 +56,6 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
-// A pointer into device (global) memory.  Loads through a pointer that was
-// itself read from memory (the routed experts' matrices) are otherwise
-// generic "flat" loads, which also count against the LDS wait counter: every
-// LDS wait would then wait for the weights in flight as well.
 // A wave-uniform read of memory that no thread of the kernel writes (tables
 // built by an earlier launch): through the constant address space it becomes
 // a scalar load, which waits on its own counter instead of queueing behind
@@ -69,6 +65,10 @@ __device__ __forceinline__ T load_uniform(const T *p) {
     return *(const __attribute__((address_space(4))) T *)p;
 }
 
+// A pointer into device (global) memory.  Loads through a pointer that was
+// itself read from memory (the routed experts' matrices) are otherwise
+// generic "flat" loads, which also count against the LDS wait counter: every
+// LDS wait would then wait for the weights in flight as well.
 template <class T>
 __device__ __forceinline__ const __attribute__((address_space(1))) T *as_global(const void *p) {
     return (const __attribute__((address_space(1))) T *)p;

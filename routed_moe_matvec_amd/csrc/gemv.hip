@@ -38,7 +38,7 @@ struct GemvArgs {
     int G;          // groups (blockIdx.y): matrix g of W0 against input slice g, 1 otherwise
 };
 
-template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32>
+template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32, int RC = kActRegChunks>
 __global__ __launch_bounds__(kGemvMaxWaves *kWave) void qgemv_kernel(GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // workgroups [0, nwg0) cover matrix 0, the rest matrix 1 (paired call)
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kGemvMaxWaves *kWave) void qgemv_kernel(GemvArgs a)
     // token's activation (row m*G + g of the [M*G, K] view), writing y[m, g, :]
     const int G = a.G, g = blockIdx.y;
     W += (size_t)g * N * a.tg.row_bytes;
-    gemv_workgroup<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32 ? kSrcF32 : kSrcQ8>(
+    gemv_workgroup<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32 ? kSrcF32 : kSrcQ8, RC>(
         W, N, a.K, a.tg, wg * a.waves * a.tpw, a.tpw, nt, a.act, a.M, a.mt, smem,
         [=](int m) { return m * G + g; }, [=](int m, int row, float v) { y[((size_t)m * G + g) * N + row] = v; },
         [=](int m, int row, int unit, const int32_t *s) {
@@ -66,17 +66,17 @@ __global__ __launch_bounds__(kGemvMaxWaves *kWave) void qgemv_kernel(GemvArgs a)
 
 static inline bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; }
 
-template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32>
+template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32, int RC = kActRegChunks>
 static int launch_kernel(const GemvArgs &a, int grid, size_t lds, hipStream_t stream) {
     static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32, RC>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
             return QG_ERR_LAUNCH;
         attr_set = true;
     }
-    hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32>), dim3(grid, a.G), dim3(a.waves * kWave),
-                       lds, stream, a);
+    hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32, RC>), dim3(grid, a.G),
+                       dim3(a.waves * kWave), lds, stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
@@ -105,8 +105,16 @@ static int launch_gemv(GemvArgs &a, hipStream_t stream) {
     const int per_wg = a.waves * a.tpw;
     a.nwg0 = (a.nt0 + per_wg - 1) / per_wg;
     const int grid = a.nwg0 + (a.nt1 + per_wg - 1) / per_wg;
-    if (a.M == 1)  // (one token: tiles_per_wave gives 1)
+    if (a.M == 1) {  // (one token: tiles_per_wave gives 1)
+        // staging registers for one pass over the token's row where it fits
+        // (the int-sum export keeps the default)
+        if constexpr (!DEBUG_ISUM) {
+            const int rc = act_reg_chunks(F32 ? a.K / 4 : a.K / 16, threads);
+            if (rc == 1) return launch_kernel<FMT, NB, false, false, true, F32, 1>(a, grid, lds, stream);
+            if (rc == 2) return launch_kernel<FMT, NB, false, false, true, F32, 2>(a, grid, lds, stream);
+        }
         return launch_kernel<FMT, NB, DEBUG_ISUM, false, true, F32>(a, grid, lds, stream);
+    }
     return a.tpw > 1 ? launch_kernel<FMT, NB, DEBUG_ISUM, true, false, F32>(a, grid, lds, stream)
                      : launch_kernel<FMT, NB, DEBUG_ISUM, false, false, F32>(a, grid, lds, stream);
 }

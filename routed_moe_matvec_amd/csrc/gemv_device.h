@@ -220,13 +220,18 @@ constexpr int kActLdsBudget = 44 * 1024;
 // 16-byte activation chunks each thread holds in registers while staging.
 constexpr int kActRegChunks = 4;
 
+// Register chunks for one pass over `chunks` 16-byte chunks (1, 2 or 4): a
+// pass that fits fewer saves the registers and the clamped duplicate reads
+// (and, from fp32, the duplicate quantization) of the unused ones.
+inline int act_reg_chunks(int chunks, int threads) {
+    return chunks <= threads ? 1 : (chunks <= 2 * threads ? 2 : kActRegChunks);
+}
+
 template <class U>
 __host__ __device__ inline int act_lds_bytes_per_token(int K) {
     return (K / U::weights) * U::rec_dwords * 4;
 }
 
-// Tokens staged at once: bounded by the LDS budget and by what the staging
-// registers of a workgroup of `threads` hold.
 // Tokens staged at once: bounded by the LDS budget, and preferably by what
 // one pass of the staging registers holds (larger rows take extra passes).
 template <class U>
@@ -249,10 +254,10 @@ inline size_t gemv_lds_bytes(int waves, int K, int mt) {
 // Between the two the caller issues its weight loads, which then stay in
 // flight: the waits for the activation registers only cover loads issued
 // before them.
-template <int FMT, class U, bool ONE>
+template <int FMT, class U, bool ONE, int RC = kActRegChunks>
 struct ActStage {
     static constexpr int REC = U::rec_dwords * 4;
-    u32x4 q[kActRegChunks];
+    u32x4 q[RC];
     u32x4 d, s;
     uint32_t qdiv, sdiv;  // TileGeom's reciprocals of K / 16 and K / 128
 
@@ -311,22 +316,22 @@ struct ActStage {
         const int cpt = K / 16, spt = K / 128;
         // the token rows first (a gathered token list costs one round trip
         // for all of them), then the activation reads
-        // (index kActRegChunks: the scales' token)
-        int c[kActRegChunks + 1], mm[kActRegChunks + 1];
-        size_t row[kActRegChunks + 1];
+        // (index RC: the scales' token)
+        int c[RC + 1], mm[RC + 1];
+        size_t row[RC + 1];
 #pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k) {
+        for (int k = 0; k < RC; ++k) {
             c[k] = clamp_chunk((int)threadIdx.x + k * NT, qtotal);
             mm[k] = qtok(c[k]);
         }
-        c[kActRegChunks] = clamp_chunk((int)threadIdx.x, stotal);
-        mm[kActRegChunks] = stok(c[kActRegChunks]);
+        c[RC] = clamp_chunk((int)threadIdx.x, stotal);
+        mm[RC] = stok(c[RC]);
 #pragma unroll
-        for (int k = 0; k <= kActRegChunks; ++k) row[k] = (size_t)token_row(m0 + mm[k]);
+        for (int k = 0; k <= RC; ++k) row[k] = (size_t)token_row(m0 + mm[k]);
 #pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k)
+        for (int k = 0; k < RC; ++k)
             q[k] = reinterpret_cast<const u32x4 *>(qx + row[k] * K)[c[k] - mm[k] * cpt];
-        const size_t src = row[kActRegChunks] * (K / 32) / 4 + (c[kActRegChunks] - mm[kActRegChunks] * spt);
+        const size_t src = row[RC] * (K / 32) / 4 + (c[RC] - mm[RC] * spt);
         d = reinterpret_cast<const u32x4 *>(dx)[src];
         if constexpr (FMT == QG_FMT_Q4K) s = reinterpret_cast<const u32x4 *>(sx)[src];
     }
@@ -338,7 +343,7 @@ struct ActStage {
         const int NT = blockDim.x;
         const int qtotal = mtc * (K / 16), stotal = mtc * (K / 128);
 #pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k)
+        for (int k = 0; k < RC; ++k)
             *reinterpret_cast<u32x4 *>(quant_dst(lds, K, clamp_chunk((int)threadIdx.x + k * NT, qtotal))) = q[k];
         {
             uint8_t *rec = scale_dst(lds, K, clamp_chunk((int)threadIdx.x, stotal));
@@ -346,14 +351,14 @@ struct ActStage {
             if constexpr (FMT == QG_FMT_Q4K) *reinterpret_cast<u32x4 *>(rec + 32) = s;
         }
         // further passes (chunks that did not fit the registers)
-        for (int base = kActRegChunks * NT; base < qtotal; base += kActRegChunks * NT) {
+        for (int base = RC * NT; base < qtotal; base += RC * NT) {
 #pragma unroll
-            for (int k = 0; k < kActRegChunks; ++k) {
+            for (int k = 0; k < RC; ++k) {
                 const int c = base + (int)threadIdx.x + k * NT;
                 if (c < qtotal) q[k] = *quant_src(qx, K, m0, c, token_row);
             }
 #pragma unroll
-            for (int k = 0; k < kActRegChunks; ++k) {
+            for (int k = 0; k < RC; ++k) {
                 const int c = base + (int)threadIdx.x + k * NT;
                 if (c < qtotal) *reinterpret_cast<u32x4 *>(quant_dst(lds, K, c)) = q[k];
             }
@@ -400,11 +405,11 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // the first pass is read and written unconditionally, threads past the end
 // taking one of the last 64 chunks (whole 32-blocks per 8-lane group, since
 // the chunk count is a multiple of 64), and ONE fixes the token to 0.
-template <int FMT, class U, bool GLU, bool ONE>
+template <int FMT, class U, bool GLU, bool ONE, int RC = kActRegChunks>
 struct ActStageF32 {
     static constexpr int REC = U::rec_dwords * 4;
-    float4 v[kActRegChunks];
-    float4 v2[GLU ? kActRegChunks : 1];
+    float4 v[RC];
+    float4 v2[GLU ? RC : 1];
     uint32_t fdiv;  // TileGeom's reciprocal of K / 4
 
     __device__ __forceinline__ int ftok(int c) const { return ONE ? 0 : (int)__umulhi((uint32_t)c, fdiv); }
@@ -418,7 +423,7 @@ struct ActStageF32 {
         const int NT = blockDim.x;
         const int cpt = K / 4;
 #pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k) {
+        for (int k = 0; k < RC; ++k) {
             const int c = base + (int)threadIdx.x + k * NT;
             if (c < mtc * cpt) {
                 const int mm = ftok(c);
@@ -433,17 +438,17 @@ struct ActStageF32 {
     __device__ __forceinline__ void load(const ActSrc &src, int K, int m0, int mtc, TokenRow token_row) {
         const int NT = blockDim.x;
         const int cpt = K / 4, total = mtc * cpt;
-        int c[kActRegChunks], mm[kActRegChunks];
-        size_t at[kActRegChunks];
+        int c[RC], mm[RC];
+        size_t at[RC];
 #pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k) {
+        for (int k = 0; k < RC; ++k) {
             c[k] = clamp_chunk((int)threadIdx.x + k * NT, total);
             mm[k] = ftok(c[k]);
         }
 #pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k) at[k] = (size_t)token_row(m0 + mm[k]) * K;
+        for (int k = 0; k < RC; ++k) at[k] = (size_t)token_row(m0 + mm[k]) * K;
 #pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k) {
+        for (int k = 0; k < RC; ++k) {
             v[k] = reinterpret_cast<const float4 *>(src.x + at[k])[c[k] - mm[k] * cpt];
             if constexpr (GLU) v2[k] = reinterpret_cast<const float4 *>(src.x2 + at[k])[c[k] - mm[k] * cpt];
         }
@@ -500,12 +505,12 @@ struct ActStageF32 {
         const int total = mtc * (K / 4);
         // 8 consecutive lanes hold one 32-block
 #pragma unroll
-        for (int k = 0; k < kActRegChunks; ++k)
+        for (int k = 0; k < RC; ++k)
             emit(lds, K, m0, clamp_chunk((int)threadIdx.x + k * NT, total), k, true, token_row, src, publish);
-        for (int base = kActRegChunks * NT; base < total; base += kActRegChunks * NT) {
+        for (int base = RC * NT; base < total; base += RC * NT) {
             load_pass(src, K, m0, mtc, base, token_row);
 #pragma unroll
-            for (int k = 0; k < kActRegChunks; ++k) {
+            for (int k = 0; k < RC; ++k) {
                 const int c = base + (int)threadIdx.x + k * NT;
                 emit(lds, K, m0, c, k, c < total, token_row, src, publish);
             }
@@ -581,9 +586,10 @@ __device__ __forceinline__ void tile_to_unit(const TileRegs<U> &r, uint8_t *lw, 
 // the workgroup must call this (it synchronizes).  PIPE = false limits tpw
 // to 1 and keeps only one tile register set; ONE = true is the M = 1 form
 // (no token loop, fewer live registers); SRC picks what is staged (kSrcQ8,
-// kSrcF32 or kSrcGLU, see ActSrc).
-template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, int SRC, class TokenRow, class Out,
-          class IsumOut>
+// kSrcF32 or kSrcGLU, see ActSrc); RC is the 16-byte chunks of activation
+// each thread stages per pass (act_reg_chunks).
+template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, int SRC, int RC = kActRegChunks,
+          class TokenRow, class Out, class IsumOut>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, int N, int K, const TileGeom &tg,
                                                int tile_base, int tpw, int ntiles, const ActSrc &src, int M, int mt,
                                                uint8_t *smem, TokenRow token_row, Out out, IsumOut isum_out) {
@@ -616,10 +622,10 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t *__restrict__ W, in
     TileRegs<U> ra, rb;
     UnitRegs<U> u;
     constexpr bool F32 = SRC != kSrcQ8;
-    ActStage<FMT, U, ONE> st;
+    ActStage<FMT, U, ONE, RC> st;
     st.qdiv = tg.qdiv;
     st.sdiv = tg.sdiv;
-    ActStageF32<FMT, U, SRC == kSrcGLU, ONE> stf;
+    ActStageF32<FMT, U, SRC == kSrcGLU, ONE, RC> stf;
     stf.fdiv = tg.fdiv;
     // fp32 input: workgroup (0, 0) publishes the Q8 activation; SwiGLU input:
     // workgroup 0 of each blockIdx.y (one expert: its own pairs) publishes h

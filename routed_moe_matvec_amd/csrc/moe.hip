@@ -294,8 +294,9 @@ using QU = Unit<QG_FMT_Q4K, 8>;
 
 // gate and up of expert uniq[blockIdx.y]: workgroups [0, nwg) take gate rows,
 // [nwg, 2 nwg) up rows; the tokens are the expert's pairs' tokens.  ONE: the
-// single-token engine, run once per pair.
-template <bool ONE>
+// single-token engine, run once per pair.  RC: staging register chunks of
+// the one-token form (act_reg_chunks of the activation's row).
+template <bool ONE, int RC>
 __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int u = blockIdx.y;
@@ -321,14 +322,14 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
         for (int m = 0; m < cnt; ++m) {
             if (m > 0) lds_barrier();  // the previous pair's staged activation is no longer read
             const int p = load_uniform(pairs + m);
-            gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8>(
+            gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8, RC>(
                 W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p / topk; },
                 [=](int, int row, float v) { dst[(size_t)p * F + row] = v; }, [](int, int, int, const int32_t *) {});
         }
     } else if (cnt == 1) {
         // a one-pair expert of a batch: the one-token form, its token read once as a scalar
         const int p = load_uniform(pairs);
-        gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8>(
+        gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8, RC>(
             W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p / topk; },
             [=](int, int row, float v) { dst[(size_t)p * F + row] = v; }, [](int, int, int, const int32_t *) {});
     } else {
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
 // each of its pairs.  ONE: h is computed and quantized while it is staged
 // (workgroup 0 of the expert stores h, hq, hd, hs of its pairs), once per
 // pair; otherwise moe_h_quant_kernel has stored hq/hd/hs before.
-template <bool ONE>
+template <bool ONE, int RC>
 __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int u = blockIdx.y;
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
         for (int m = 0; m < cnt; ++m) {
             if (m > 0) lds_barrier();
             const int p = load_uniform(pairs + m);
-            gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcGLU>(
+            gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcGLU, RC>(
                 W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p; },
                 [=](int, int row, float v) { o[(size_t)p * D + row] = v; }, [](int, int, int, const int32_t *) {});
         }
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_down_kernel(MoeArgs a) {
         hq.sx = a.ws.hs;
         if (cnt == 1) {
             const int p = load_uniform(pairs);
-            gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8>(
+            gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8, RC>(
                 W, D, a.F, a.tg, (int)blockIdx.x * kMoeWaves, 1, ntiles, hq, 1, a.mt, smem, [=](int) { return p; },
                 [=](int, int row, float v) { o[(size_t)p * D + row] = v; }, [](int, int, int, const int32_t *) {});
             return;
@@ -695,6 +696,35 @@ static int launch_moe_mm(const MoeArgs &a, int P, hipStream_t st) {
     }
 }
 
+template <int RC>
+bool raise_moe_lds() {
+    return raise_lds_limit(moe_gate_up_kernel<false, RC>, kLdsBytes) &&
+           raise_lds_limit(moe_gate_up_kernel<true, RC>, kLdsBytes) &&
+           raise_lds_limit(moe_down_kernel<false, RC>, kLdsBytes) && raise_lds_limit(moe_down_kernel<true, RC>, kLdsBytes);
+}
+
+template <bool DOWN, bool ONE, int RC>
+void launch_moe_dot_rc(dim3 grid, size_t lds, hipStream_t st, const MoeArgs &a) {
+    if constexpr (DOWN)
+        hipLaunchKernelGGL((moe_down_kernel<ONE, RC>), grid, dim3(kMoeWaves * kWave), lds, st, a);
+    else
+        hipLaunchKernelGGL((moe_gate_up_kernel<ONE, RC>), grid, dim3(kMoeWaves * kWave), lds, st, a);
+}
+
+// The dot-product expert kernel of gate/up or down, in its one-token or
+// several-token form, with rc staging register chunks (1, 2 or 4).
+template <bool DOWN>
+void launch_moe_dot(bool one, int rc, dim3 grid, size_t lds, hipStream_t st, const MoeArgs &a) {
+    if (one) {
+        if (rc == 1) return launch_moe_dot_rc<DOWN, true, 1>(grid, lds, st, a);
+        if (rc == 2) return launch_moe_dot_rc<DOWN, true, 2>(grid, lds, st, a);
+        return launch_moe_dot_rc<DOWN, true, kActRegChunks>(grid, lds, st, a);
+    }
+    if (rc == 1) return launch_moe_dot_rc<DOWN, false, 1>(grid, lds, st, a);
+    if (rc == 2) return launch_moe_dot_rc<DOWN, false, 2>(grid, lds, st, a);
+    return launch_moe_dot_rc<DOWN, false, kActRegChunks>(grid, lds, st, a);
+}
+
 }  // namespace qg
 
 extern "C" size_t moe_routed_workspace_bytes(int T, int topk, int E, int D, int F) {
@@ -769,20 +799,14 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     constexpr int threads = kMoeWaves * kWave;
     static bool lds_raised = false;  // idempotent: raise the dynamic-LDS limit once
     if (!lds_raised)
-        lds_raised = raise_lds_limit(moe_gate_up_kernel<false>, kLdsBytes) &&
-                     raise_lds_limit(moe_gate_up_kernel<true>, kLdsBytes) &&
-                     raise_lds_limit(moe_down_kernel<false>, kLdsBytes) &&
-                     raise_lds_limit(moe_down_kernel<true>, kLdsBytes);
+        lds_raised = raise_moe_lds<1>() && raise_moe_lds<2>() && raise_moe_lds<kActRegChunks>();
 
     // gate/up: K = D, Q8 activation of the tokens
     a.tg = make_tile_geom<QU>(D);
     a.mt = one ? 1 : min(kMoeChunk, tokens_per_chunk<QU>(D, QG_MAX_MOE_PAIRS, threads));
     size_t lds = gemv_lds_bytes<QU>(kMoeWaves, D, a.mt);
     int nwg = ((F + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
-    if (one)
-        hipLaunchKernelGGL(moe_gate_up_kernel<true>, dim3(2 * nwg, Ucap), dim3(threads), lds, st, a);
-    else
-        hipLaunchKernelGGL(moe_gate_up_kernel<false>, dim3(2 * nwg, Ucap), dim3(threads), lds, st, a);
+    launch_moe_dot<false>(one, act_reg_chunks(D / 16, threads), dim3(2 * nwg, Ucap), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
     if (mm_on) {
         const int rc = launch_moe_mm<false>(a, P, st);
@@ -801,10 +825,9 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     a.mt = one ? 1 : min(kMoeChunk, tokens_per_chunk<QU>(F, QG_MAX_MOE_PAIRS, threads));
     lds = gemv_lds_bytes<QU>(kMoeWaves, F, a.mt);
     nwg = ((D + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
-    if (one)
-        hipLaunchKernelGGL(moe_down_kernel<true>, dim3(nwg, Ucap), dim3(threads), lds, st, a);
-    else
-        hipLaunchKernelGGL(moe_down_kernel<false>, dim3(nwg, Ucap), dim3(threads), lds, st, a);
+    // (one token: h staged from fp32, 4 values per chunk; else the Q8 h of a
+    // one-pair expert, 16 per chunk)
+    launch_moe_dot<true>(one, act_reg_chunks(one ? F / 4 : F / 16, threads), dim3(nwg, Ucap), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
     if (mm_on) {
         const int rc = launch_moe_mm<true>(a, P, st);
