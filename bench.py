@@ -626,13 +626,6 @@ def summarize_pmc(gf: str, gw: str, cf: str, cw: str) -> str:
         "python3 bench.py --summarize-pmc %s %s %s %s" % (gf, gw, cf, cw)]
     ent["note"] = ("FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is multiplied by the factor that makes "
                    "the same counter equal the known bytes of a %d-byte device copy" % COPY_PROBE_BYTES)
-    pmc = "rocprofv3 --output-format csv --pmc %s -d %s -o run -- python3 -u bench.py --probe %s --steps %d --warmup %d"
-    ent["commands"] = [
-        pmc % ("FETCH_SIZE", gf, "gemv", 50, 5), pmc % ("WRITE_SIZE", gw, "gemv", 50, 5),
-        pmc % ("FETCH_SIZE", cf, "copy", 5, 1), pmc % ("WRITE_SIZE", cw, "copy", 5, 1),
-        "python3 bench.py --summarize-pmc %s %s %s %s" % (gf, gw, cf, cw)]
-    ent["note"] = ("FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is multiplied by the factor that makes "
-                   "the same counter equal the known bytes of a %d-byte device copy" % COPY_PROBE_BYTES)
     path = TRAFFIC_FILE
     try:
         with open(path) as f:

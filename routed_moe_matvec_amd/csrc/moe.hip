@@ -183,17 +183,17 @@ __global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restr
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
         const int w = WPL * l + i;
-        uint32_t bits = bm[w];
         wpre[w] = run;
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            ws.uniq[run++] = 32 * w + b;
-            bits &= bits - 1u;
-        }
+        run += __popc(bm[w]);
     }
     if (l == 0) *ws.nuniq = U;
     for (int u = l; u < U; u += kWave) cur[u] = 0;
     lds_barrier();
+    // the distinct ids in increasing order: one lane per id
+    for (int e = l; e < E; e += kWave) {
+        const uint32_t word = bm[e >> 5], bit = 1u << (e & 31);
+        if (word & bit) ws.uniq[wpre[e >> 5] + __popc(word & (bit - 1u))] = e;
+    }
     // each pair's slot (-1: invalid or dropped) replaces its id in sid
     for (int p = l; p < P; p += kWave) {
         const int e = sid[p];
@@ -237,23 +237,22 @@ __global__ __launch_bounds__(kWave) void moe_table_kernel(const int32_t *__restr
     }
     lds_barrier();
     // stable fill, 64 pairs at a time: a pair's place among the chunk's pairs of
-    // the same expert comes from a ballot over each distinct slot in the chunk
+    // the same expert.  The lanes holding the same slot are found bit by bit
+    // (one ballot per bit of a slot number, whatever the number of distinct
+    // slots in the chunk): a lane keeps the lanes that agree with it on
+    // every bit.
     const uint64_t below = (1ull << l) - 1ull;
+    const int sbits = 32 - __clz(max(U - 1, 1));  // bits of the largest slot number
     for (int c0 = 0; c0 < P; c0 += kWave) {
         const int p = c0 + l;
         const int s = p < P ? sid[p] : -1;
-        uint64_t left = __ballot(s >= 0);
-        int before = 0, same = 0;
-        while (left) {
-            const int leader = __ffsll((unsigned long long)left) - 1;
-            const int v = __builtin_amdgcn_readlane(s, leader);  // leader is wave-uniform
-            const uint64_t m = __ballot(s == v);
-            if (s == v) {
-                before = __popcll(m & below);
-                same = __popcll(m);
-            }
-            left &= ~m;
+        uint64_t m = __ballot(s >= 0);
+        for (int b = 0; b < sbits; ++b) {
+            const bool one = (s >> b) & 1;
+            const uint64_t ones = __ballot(one);
+            m &= one ? ones : ~ones;
         }
+        const int before = __popcll(m & below), same = __popcll(m);
         if (s >= 0) ws.pairs[cur[s] + before] = p;
         lds_barrier();
         if (s >= 0 && before == 0) cur[s] += same;  // one lane per expert present in the chunk
