@@ -313,6 +313,10 @@ int moe_routed_workspace_layout(int T, int topk, int E, int D, int F, size_t *of
  *   3.   o_p = down_e . hq                              (Q4_K, D x F)
  *   4. y[t] = sum_k rw[t, k] * o_(t,k)   in k order (fp32).
  * Each selected expert's weights are streamed once for all of its pairs.
+ * With one token and at most 64 pairs the table is built inside the first
+ * expert launch: every workgroup derives its expert from the ids, and one
+ * of them writes the table and the status word; otherwise a table launch
+ * comes first.  The workspace holds the same table either way.
  * With T >= QG_MOE_MM_PAIRS, experts with at least that many pairs run gate,
  * up and down on the int8 matrix cores (32 pairs at a time, gathered through
  * the pair list); their results equal the one-token form bit for bit, as for

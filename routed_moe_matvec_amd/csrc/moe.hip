@@ -274,7 +274,115 @@ struct MoeArgs {
     TileGeom tg;  // of the projection this kernel runs
     int mt;       // tokens per LDS chunk
     int mm_on;    // experts with kMoeMm pairs or more are left to the matrix-core kernels
+    // for the gate/up launch that builds the table of one token itself
+    const int32_t *ids;
+    int P, E;
+    int32_t *status;
 };
+
+// ---------------------------------------------------------------- the table of one token
+
+// One token with at most 64 pairs: the table in the registers of one wave,
+// lane l holding pair l.  It has the table kernel's contents (the same
+// slots, pair order and status), so the first expert launch can derive each
+// workgroup's expert itself and write the table for the later launches.
+struct TokenTable {
+    int e;                 // id of this lane's pair
+    bool in_range;         // 0 <= e < E (lanes past P: false)
+    bool usable;           // and the expert's three matrices are usable
+    uint64_t same;         // in-range lanes with the same id
+    int rank;              // usable: the slot of the expert (distinct usable ids below it)
+    int off;               // usable: the expert's first place in the pair list
+    uint64_t first;        // wave-uniform: the first lane of each usable expert
+    uintptr_t pg, pu, pd;  // the expert's gate, up and down matrices
+};
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int j) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, j);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), j);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ TokenTable token_table(const int32_t *ids, int P, int E, const void *const *gate,
+                                                  const void *const *up, const void *const *down) {
+    TokenTable t;
+    const int l = lane_id();
+    t.e = as_global<int32_t>(ids)[min(l, P - 1)];
+    t.in_range = l < P && t.e >= 0 && t.e < E;
+    const int ec = t.in_range ? t.e : 0;
+    t.pg = as_global<uintptr_t>(gate)[ec];
+    t.pu = as_global<uintptr_t>(up)[ec];
+    t.pd = as_global<uintptr_t>(down)[ec];
+    // lanes with the same id: those that agree on every bit of an id
+    const int ebits = 32 - __clz(max(E - 1, 1));
+    uint64_t m = __ballot(t.in_range);
+    for (int b = 0; b < ebits; ++b) {
+        const bool one = (t.e >> b) & 1;
+        const uint64_t ones = __ballot(one);
+        m &= one ? ones : ~ones;
+    }
+    t.same = m;
+    const auto unusable = [](uintptr_t q) { return q == 0 || (q & 15) != 0; };
+    t.usable = t.in_range && !unusable(t.pg) && !unusable(t.pu) && !unusable(t.pd);
+    t.first = __ballot(t.usable && (m & ((1ull << l) - 1ull)) == 0);
+    // slot and first place: the usable experts with a smaller id, and their pairs
+    t.rank = 0;
+    t.off = 0;
+    for (uint64_t f = t.first; f; f &= f - 1) {
+        const int j = __ffsll((unsigned long long)f) - 1;  // wave-uniform
+        if (__builtin_amdgcn_readlane(t.e, j) < t.e) {
+            ++t.rank;
+            t.off += __popcll(readlane64(m, j));
+        }
+    }
+    return t;
+}
+
+// The table and the status word, as the table kernel writes them (one wave).
+__device__ __forceinline__ void write_token_table(const TokenTable &t, int P, const MoeWs &ws, int32_t *status) {
+    const int l = lane_id();
+    const uint64_t below = (1ull << l) - 1ull;
+    const bool any_bad_id = __ballot(l < P && !t.in_range) != 0ull;
+    const bool any_bad_ptr = __ballot(t.in_range && !t.usable) != 0ull;
+    const int npairs = __popcll(__ballot(t.usable));
+    const int U = __popcll(t.first);
+    if (l < P) ws.slot[l] = t.usable ? t.rank : -1;
+    if (t.usable) ws.pairs[t.off + __popcll(t.same & below)] = l;
+    if ((t.first >> l) & 1) {
+        ws.uniq[t.rank] = t.e;
+        ws.pair_off[t.rank] = t.off;
+    }
+    if (l == 0) {
+        *ws.nuniq = U;
+        ws.pair_off[U] = npairs;
+        ws.hot[0] = 0;
+        *status = any_bad_id ? QG_DEV_BAD_EXPERT : (any_bad_ptr ? QG_DEV_NULL_EXPERT : QG_DEV_OK);
+    }
+}
+
+// The gate/up launch of one token that builds the table itself: every wave
+// derives it (token_table), workgroup (0, 0) writes it, and the workgroup
+// takes the expert of slot u: its id, its pairs (bit p: pair p) and its gate
+// or up matrix.  False past the last slot.
+__device__ __forceinline__ bool token_slot(const MoeArgs &a, int u, bool is_up, int *e, uint64_t *pairs,
+                                           const uint8_t **W) {
+    const TokenTable t = token_table(a.ids, a.P, a.E, a.gate, a.up, a.down);
+    if (blockIdx.x == 0 && u == 0 && threadIdx.x < kWave) write_token_table(t, a.P, a.ws, a.status);
+    // the first lane of the expert in slot u, if there is one
+    const uint64_t hit = __ballot(((t.first >> lane_id()) & 1) && t.rank == u);
+    if (hit == 0ull) return false;
+    const int j = __ffsll((unsigned long long)hit) - 1;
+    *e = __builtin_amdgcn_readlane(t.e, j);
+    *pairs = readlane64(t.same, j);
+    *W = reinterpret_cast<const uint8_t *>(readlane64(is_up ? t.pu : t.pg, j));
+    return true;
+}
+
+// Place of the n-th set bit of m (n < popcount(m)).
+__device__ __forceinline__ int nth_bit(uint64_t m, int n) {
+    for (int i = 0; i < n; ++i) m &= m - 1ull;
+    return __ffsll((unsigned long long)m) - 1;
+}
 
 // Expert slot u of the table: its id, first pair and pair count; false when
 // u is past the number of distinct experts.  The four values are read
@@ -294,22 +402,32 @@ using QU = Unit<QG_FMT_Q4K, 8>;
 // gate and up of expert uniq[blockIdx.y]: workgroups [0, nwg) take gate rows,
 // [nwg, 2 nwg) up rows; the tokens are the expert's pairs' tokens.  ONE: the
 // single-token engine, run once per pair.  RC: staging register chunks of
-// the one-token form (act_reg_chunks of the activation's row).
-template <bool ONE, int RC>
+// the one-token form (act_reg_chunks of the activation's row).  OWN (one
+// token, at most 64 pairs, no table kernel before): every wave derives the
+// table from the ids (token_table) and workgroup (0, 0) writes it.
+template <bool ONE, int RC, bool OWN>
 __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a) {
+    static_assert(ONE || !OWN, "the table is built in the kernel for one token only");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int u = blockIdx.y;
-    // the expert's entry is read with the count (blockIdx.y < Ucap keeps it
-    // inside the table), all as scalars in one round trip; the slots past the
-    // count leave
-    int e, p0, cnt;
-    if (!moe_slot(a.ws, u, &e, &p0, &cnt)) return;  // the whole workgroup leaves
-    if (a.mm_on && cnt >= kMoeMm) return;  // the matrix-core kernels take this expert
     const int ntiles = (a.F + a.tg.rpt - 1) / a.tg.rpt;
     const int nwg = (ntiles + kMoeWaves - 1) / kMoeWaves;
     const bool is_up = (int)blockIdx.x >= nwg;
     const int wg = is_up ? (int)blockIdx.x - nwg : (int)blockIdx.x;
-    const uint8_t *W = reinterpret_cast<const uint8_t *>(load_uniform(is_up ? a.up + e : a.gate + e));
+    int e, p0 = 0, cnt;
+    uint64_t own = 0;  // OWN: the expert's pairs, one bit each
+    const uint8_t *W;
+    if constexpr (OWN) {
+        if (!token_slot(a, u, is_up, &e, &own, &W)) return;  // the whole workgroup leaves
+        cnt = __popcll(own);
+    } else {
+        // the expert's entry is read with the count (blockIdx.y < Ucap keeps
+        // it inside the table), all as scalars in one round trip; the slots
+        // past the count leave
+        if (!moe_slot(a.ws, u, &e, &p0, &cnt)) return;  // the whole workgroup leaves
+        if (a.mm_on && cnt >= kMoeMm) return;  // the matrix-core kernels take this expert
+        W = reinterpret_cast<const uint8_t *>(load_uniform(is_up ? a.up + e : a.gate + e));
+    }
     float *dst = is_up ? a.ws.v : a.ws.g;
     const int32_t *pairs = a.ws.pairs + p0;
     const int topk = a.topk, F = a.F;
@@ -320,7 +438,13 @@ __global__ __launch_bounds__(kMoeWaves *kWave) void moe_gate_up_kernel(MoeArgs a
     if constexpr (ONE) {
         for (int m = 0; m < cnt; ++m) {
             if (m > 0) lds_barrier();  // the previous pair's staged activation is no longer read
-            const int p = load_uniform(pairs + m);
+            int p;
+            if constexpr (OWN) {
+                p = __ffsll((unsigned long long)own) - 1;  // the pairs in increasing order
+                own &= own - 1ull;
+            } else {
+                p = load_uniform(pairs + m);
+            }
             gemv_workgroup<QG_FMT_Q4K, 8, false, false, true, kSrcQ8, RC>(
                 W, F, a.D, a.tg, wg * kMoeWaves, 1, ntiles, act, 1, a.mt, smem, [=](int) { return p / topk; },
                 [=](int, int row, float v) { dst[(size_t)p * F + row] = v; }, [](int, int, int, const int32_t *) {});
@@ -462,22 +586,36 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void moe_mm_down_kernel(MoeArg
 // Block-scaled expert formats (FP8 E4M3 128 x 128, FP4 E2M1 1 x 32): gate and
 // up of expert uniq[blockIdx.y] on the mx engine, workgroups [0, nwg) on gate
 // rows and [nwg, 2 nwg) on up rows, the tokens being the expert's pairs'.
-template <int FMT, int CPL>
+template <int FMT, int CPL, bool OWN>
 __global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs a, int nwg) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int R = mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int u = blockIdx.y;
-    // the expert's entry is read with the count (blockIdx.y < Ucap keeps it
-    // inside the table), all as scalars in one round trip; the slots past the
-    // count leave
-    int e, p0, cnt;
-    if (!moe_slot(a.ws, u, &e, &p0, &cnt)) return;  // the whole workgroup leaves
     const bool is_up = (int)blockIdx.x >= nwg;
     const int wg = is_up ? (int)blockIdx.x - nwg : (int)blockIdx.x;
-    const uint8_t *W = reinterpret_cast<const uint8_t *>(load_uniform(is_up ? a.up + e : a.gate + e));
+    int e, p0 = 0, cnt;
+    uint64_t own = 0;  // OWN (one token, the table built here): the expert's pairs, one bit each
+    const uint8_t *W;
+    if constexpr (OWN) {
+        if (!token_slot(a, u, is_up, &e, &own, &W)) return;  // the whole workgroup leaves
+        cnt = __popcll(own);
+    } else {
+        // the expert's entry is read with the count (blockIdx.y < Ucap keeps
+        // it inside the table), all as scalars in one round trip; the slots
+        // past the count leave
+        if (!moe_slot(a.ws, u, &e, &p0, &cnt)) return;  // the whole workgroup leaves
+        W = reinterpret_cast<const uint8_t *>(load_uniform(is_up ? a.up + e : a.gate + e));
+    }
     float *dst = is_up ? a.ws.v : a.ws.g;
     const int32_t *pairs = a.ws.pairs + p0;
     const int topk = a.topk, F = a.F;
+    if constexpr (OWN) {
+        // one token: every pair's token is 0
+        mx_workgroup<FMT, CPL, kMxLoadsRouted>(
+            W, F, a.D, wg * kMxWaves * R, cnt, a.mt, a.qx, a.dx, [](int) { return 0; },
+            [=](int m, int row, float v) { dst[(size_t)nth_bit(own, m) * F + row] = v; }, smem);
+        return;
+    }
     if (cnt == 1) {
         // one pair (the usual case in decode): its token is read once, as a
         // scalar, so no vector load has to return before the weights are requested
@@ -618,17 +756,24 @@ static bool raise_lds_limit(Kern *k, size_t bytes) {
 }
 
 // gate/up (K = D, F rows each) and down (K = F, D rows) on the mx engine.
-template <int FMT, int CPL>
-static int launch_moe_gate_up_mx(MoeArgs a, int Ucap, hipStream_t st) {
+template <int FMT, int CPL, bool OWN>
+static int launch_moe_gate_up_mx_own(MoeArgs a, int Ucap, hipStream_t st) {
     static bool raised = false;
-    if (!raised) raised = raise_lds_limit(moe_gate_up_mx_kernel<FMT, CPL>, kMxLdsMax);
+    if (!raised) raised = raise_lds_limit(moe_gate_up_mx_kernel<FMT, CPL, OWN>, kMxLdsMax);
     if (!raised) return QG_ERR_LAUNCH;
     const int rows_per_wg = kMxWaves * mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int nwg = (a.F + rows_per_wg - 1) / rows_per_wg;
     a.mt = mx_tokens_per_chunk(a.D, QG_MAX_MOE_PAIRS);
-    hipLaunchKernelGGL((moe_gate_up_mx_kernel<FMT, CPL>), dim3(2 * nwg, Ucap), dim3(kMxWaves * kWave),
+    hipLaunchKernelGGL((moe_gate_up_mx_kernel<FMT, CPL, OWN>), dim3(2 * nwg, Ucap), dim3(kMxWaves * kWave),
                        (size_t)a.mt * mx_token_rec(a.D) + mx_scale_lds<FMT>(a.D, CPL, kMxLoadsRouted), st, a, nwg);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+// own: one token, the table built in this launch (no table kernel before)
+template <int FMT, int CPL>
+static int launch_moe_gate_up_mx(const MoeArgs &a, int Ucap, bool own, hipStream_t st) {
+    return own ? launch_moe_gate_up_mx_own<FMT, CPL, true>(a, Ucap, st)
+               : launch_moe_gate_up_mx_own<FMT, CPL, false>(a, Ucap, st);
 }
 
 template <int FMT, int CPL>
@@ -645,14 +790,19 @@ static int launch_moe_down_mx(MoeArgs a, int Ucap, hipStream_t st) {
 }
 
 template <int FMT>
-static int launch_moe_mx(const MoeArgs &a, int Ucap, bool down, hipStream_t st) {
+static int launch_moe_mx(const MoeArgs &a, int Ucap, bool down, bool own, hipStream_t st) {
     switch (mx_chunks_per_lane<FMT>(down ? a.F : a.D)) {
-        case 1: return down ? launch_moe_down_mx<FMT, 1>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 1>(a, Ucap, st);
-        case 2: return down ? launch_moe_down_mx<FMT, 2>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 2>(a, Ucap, st);
-        case 4: return down ? launch_moe_down_mx<FMT, 4>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 4>(a, Ucap, st);
-        case 8: return down ? launch_moe_down_mx<FMT, 8>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 8>(a, Ucap, st);
+        case 1:
+            return down ? launch_moe_down_mx<FMT, 1>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 1>(a, Ucap, own, st);
+        case 2:
+            return down ? launch_moe_down_mx<FMT, 2>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 2>(a, Ucap, own, st);
+        case 4:
+            return down ? launch_moe_down_mx<FMT, 4>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 4>(a, Ucap, own, st);
+        case 8:
+            return down ? launch_moe_down_mx<FMT, 8>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 8>(a, Ucap, own, st);
         case 16:
-            return down ? launch_moe_down_mx<FMT, 16>(a, Ucap, st) : launch_moe_gate_up_mx<FMT, 16>(a, Ucap, st);
+            return down ? launch_moe_down_mx<FMT, 16>(a, Ucap, st)
+                        : launch_moe_gate_up_mx<FMT, 16>(a, Ucap, own, st);
         default: return QG_ERR_SHAPE;
     }
 }
@@ -697,31 +847,41 @@ static int launch_moe_mm(const MoeArgs &a, int P, hipStream_t st) {
 
 template <int RC>
 bool raise_moe_lds() {
-    return raise_lds_limit(moe_gate_up_kernel<false, RC>, kLdsBytes) &&
-           raise_lds_limit(moe_gate_up_kernel<true, RC>, kLdsBytes) &&
+    return raise_lds_limit(moe_gate_up_kernel<false, RC, false>, kLdsBytes) &&
+           raise_lds_limit(moe_gate_up_kernel<true, RC, false>, kLdsBytes) &&
+           raise_lds_limit(moe_gate_up_kernel<true, RC, true>, kLdsBytes) &&
            raise_lds_limit(moe_down_kernel<false, RC>, kLdsBytes) && raise_lds_limit(moe_down_kernel<true, RC>, kLdsBytes);
 }
 
-template <bool DOWN, bool ONE, int RC>
+template <bool DOWN, bool ONE, int RC, bool OWN>
 void launch_moe_dot_rc(dim3 grid, size_t lds, hipStream_t st, const MoeArgs &a) {
     if constexpr (DOWN)
         hipLaunchKernelGGL((moe_down_kernel<ONE, RC>), grid, dim3(kMoeWaves * kWave), lds, st, a);
     else
-        hipLaunchKernelGGL((moe_gate_up_kernel<ONE, RC>), grid, dim3(kMoeWaves * kWave), lds, st, a);
+        hipLaunchKernelGGL((moe_gate_up_kernel<ONE, RC, OWN>), grid, dim3(kMoeWaves * kWave), lds, st, a);
 }
 
 // The dot-product expert kernel of gate/up or down, in its one-token or
-// several-token form, with rc staging register chunks (1, 2 or 4).
-template <bool DOWN>
-void launch_moe_dot(bool one, int rc, dim3 grid, size_t lds, hipStream_t st, const MoeArgs &a) {
+// several-token form, with rc staging register chunks (1, 2 or 4); own: the
+// one-token gate/up launch that builds the table itself.
+template <bool DOWN, bool OWN>
+void launch_moe_dot_own(bool one, int rc, dim3 grid, size_t lds, hipStream_t st, const MoeArgs &a) {
     if (one) {
-        if (rc == 1) return launch_moe_dot_rc<DOWN, true, 1>(grid, lds, st, a);
-        if (rc == 2) return launch_moe_dot_rc<DOWN, true, 2>(grid, lds, st, a);
-        return launch_moe_dot_rc<DOWN, true, kActRegChunks>(grid, lds, st, a);
+        if (rc == 1) return launch_moe_dot_rc<DOWN, true, 1, OWN>(grid, lds, st, a);
+        if (rc == 2) return launch_moe_dot_rc<DOWN, true, 2, OWN>(grid, lds, st, a);
+        return launch_moe_dot_rc<DOWN, true, kActRegChunks, OWN>(grid, lds, st, a);
     }
-    if (rc == 1) return launch_moe_dot_rc<DOWN, false, 1>(grid, lds, st, a);
-    if (rc == 2) return launch_moe_dot_rc<DOWN, false, 2>(grid, lds, st, a);
-    return launch_moe_dot_rc<DOWN, false, kActRegChunks>(grid, lds, st, a);
+    if constexpr (!OWN) {
+        if (rc == 1) return launch_moe_dot_rc<DOWN, false, 1, false>(grid, lds, st, a);
+        if (rc == 2) return launch_moe_dot_rc<DOWN, false, 2, false>(grid, lds, st, a);
+        return launch_moe_dot_rc<DOWN, false, kActRegChunks, false>(grid, lds, st, a);
+    }
+}
+
+template <bool DOWN>
+void launch_moe_dot(bool one, bool own, int rc, dim3 grid, size_t lds, hipStream_t st, const MoeArgs &a) {
+    if (own && !DOWN && one) return launch_moe_dot_own<false, true>(true, rc, grid, lds, st, a);
+    return launch_moe_dot_own<DOWN, false>(one, rc, grid, lds, st, a);
 }
 
 }  // namespace qg
@@ -761,9 +921,14 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
 
     // Q4_K experts with many pairs go to the matrix cores (possible from kMoeMm tokens on)
     const int mm_on = fmt == QG_FMT_Q4K && T >= kMoeMm;
-    hipLaunchKernelGGL(moe_table_kernel, dim3(1), dim3(kWave), 0, st, ids, P, E, gate, up, down, w, d_status,
-                       mm_on);
-    if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
+    // one token with at most 64 pairs: the gate/up launch builds the table
+    // itself; otherwise the table kernel runs first
+    const bool own_table = T == 1 && P <= kWave;
+    if (!own_table) {
+        hipLaunchKernelGGL(moe_table_kernel, dim3(1), dim3(kWave), 0, st, ids, P, E, gate, up, down, w, d_status,
+                           mm_on);
+        if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
+    }
 
     MoeArgs a{};
     a.qx = qx;
@@ -778,16 +943,20 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     a.down = down;
     a.ws = w;
     a.mm_on = mm_on;
+    a.ids = ids;
+    a.P = P;
+    a.E = E;
+    a.status = d_status;
     if (fmt != QG_FMT_Q4K) {
         // block-scaled experts: gate/up, h quantized once per pair, down, combine
-        int rc = fmt == QG_FMT_FP8_E4M3_B128 ? launch_moe_mx<QG_FMT_FP8_E4M3_B128>(a, Ucap, false, st)
-                                             : launch_moe_mx<QG_FMT_FP4_E2M1_MX>(a, Ucap, false, st);
+        int rc = fmt == QG_FMT_FP8_E4M3_B128 ? launch_moe_mx<QG_FMT_FP8_E4M3_B128>(a, Ucap, false, own_table, st)
+                                             : launch_moe_mx<QG_FMT_FP4_E2M1_MX>(a, Ucap, false, own_table, st);
         if (rc) return rc;
         const long long hthreads = (long long)P * (F / 32) * 8;
         hipLaunchKernelGGL(moe_h_quant_kernel, dim3((unsigned)((hthreads + 255) / 256)), dim3(256), 0, st, w, P, F);
         if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
-        rc = fmt == QG_FMT_FP8_E4M3_B128 ? launch_moe_mx<QG_FMT_FP8_E4M3_B128>(a, Ucap, true, st)
-                                         : launch_moe_mx<QG_FMT_FP4_E2M1_MX>(a, Ucap, true, st);
+        rc = fmt == QG_FMT_FP8_E4M3_B128 ? launch_moe_mx<QG_FMT_FP8_E4M3_B128>(a, Ucap, true, false, st)
+                                         : launch_moe_mx<QG_FMT_FP4_E2M1_MX>(a, Ucap, true, false, st);
         if (rc) return rc;
         const long long cthreads = (long long)T * (D / 4);
         hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cthreads + 255) / 256)), dim3(256), 0, st, w, rw, T,
@@ -805,7 +974,7 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     a.mt = one ? 1 : min(kMoeChunk, tokens_per_chunk<QU>(D, QG_MAX_MOE_PAIRS, threads));
     size_t lds = gemv_lds_bytes<QU>(kMoeWaves, D, a.mt);
     int nwg = ((F + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
-    launch_moe_dot<false>(one, act_reg_chunks(D / 16, threads), dim3(2 * nwg, Ucap), lds, st, a);
+    launch_moe_dot<false>(one, own_table, act_reg_chunks(D / 16, threads), dim3(2 * nwg, Ucap), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
     if (mm_on) {
         const int rc = launch_moe_mm<false>(a, P, st);
@@ -826,7 +995,7 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     nwg = ((D + a.tg.rpt - 1) / a.tg.rpt + kMoeWaves - 1) / kMoeWaves;
     // (one token: h staged from fp32, 4 values per chunk; else the Q8 h of a
     // one-pair expert, 16 per chunk)
-    launch_moe_dot<true>(one, act_reg_chunks(one ? F / 4 : F / 16, threads), dim3(nwg, Ucap), lds, st, a);
+    launch_moe_dot<true>(one, false, act_reg_chunks(one ? F / 4 : F / 16, threads), dim3(nwg, Ucap), lds, st, a);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
     if (mm_on) {
         const int rc = launch_moe_mm<true>(a, P, st);

@@ -59,14 +59,14 @@ class MoeProblem:
         self.sx = empty((T, D // 32), torch.int32)
         qg.quantize_act_q8(xd, T, D, self.qx, self.dx, self.sx)
 
-    def run(self, ids=None, rw=None, gate=None, up=None, down=None):
+    def run(self, ids=None, rw=None, gate=None, up=None, down=None, ws_fill=0):
         import torch
         qg = self.qg
         ids = self.ids if ids is None else np.asarray(ids, np.int32)
         rw = self.rw if rw is None else np.asarray(rw, np.float32)
         T, topk = ids.shape
         nbytes = qg.moe_routed_workspace_bytes(T, topk, self.E, self.D, self.F)
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        ws = torch.full((nbytes,), ws_fill, dtype=torch.uint8, device="cuda")
         status = sentinel((1,), torch.int32, -99)
         y = sentinel((T, self.D), torch.float32, 777.0)
         tabs = [qg.pointer_table(lst, "cuda") for lst in (gate or self.dgate, up or self.dup, down or self.ddown)]
@@ -299,6 +299,76 @@ def test_moe_device_errors(qg):
     rw0 = np.where(pb.ids == e, 0.0, pb.rw).astype(np.float32)
     yz, _, _ = pb.run(rw=rw0)
     assert np.array_equal(y.view(np.uint32), yz.view(np.uint32))
+
+
+ONE_TOKEN_CASES = ["bad_id", "null_gate", "misaligned_down", "bad_id_and_null", "all_invalid", "duplicate"]
+
+
+@pytest.mark.parametrize("case", ONE_TOKEN_CASES)
+def test_moe_one_token_table_and_status(qg, orc, case):
+    """One token (at most 64 pairs, where the first expert launch builds the table itself):
+    over a workspace filled with 0xFF, the table equals the oracle's table of the ids with every
+    unusable expert's ids taken as invalid, the status word is the documented one (a bad id
+    before an unusable expert), and the dropped pairs contribute exactly nothing."""
+    one_token_table_case(qg, orc, case, fmt=1)
+
+
+def one_token_table_case(qg, orc, case, fmt):
+    E, D, F, topk = 16, 512, 256, 6
+    pb = MoeProblem(qg, E, D, F, 1, topk, 21, fmt=fmt)
+    ids = pb.ids.copy()
+    gate, down = list(pb.dgate), list(pb.ddown)
+    dropped = set()
+    if case in ("bad_id", "bad_id_and_null"):
+        ids[0, 3] = E
+    if case in ("null_gate", "bad_id_and_null"):
+        dropped.add(int(ids[0, 0]))
+        gate[int(ids[0, 0])] = None
+    if case == "misaligned_down":
+        e = int(ids[0, 1])
+        down[e] = pb.ddown[e].reshape(-1)[8:]  # 8 bytes in: never dereferenced
+        assert down[e].data_ptr() % 16 == 8
+        dropped.add(e)
+    if case == "all_invalid":
+        ids[:] = -1
+    if case == "duplicate":
+        ids[0, 4] = ids[0, 2]
+    progress("moe one-token table fmt=%d case=%s ids=%s" % (fmt, case, ids.tolist()))
+    y, ws, st = pb.run(ids=ids, gate=gate, down=down, ws_fill=0xFF)
+    bad_id = bool(np.any((ids < 0) | (ids >= E)))
+    assert st == (qg.DEV_BAD_EXPERT if bad_id else (qg.DEV_NULL_EXPERT if dropped else qg.DEV_OK))
+    eff = np.where(np.isin(ids, sorted(dropped)), -1, ids).astype(np.int32)
+    tab = orc.moe_table(eff, E)
+    R = pb.regions(ws)
+    assert R["n_uniq"] == tab["n_uniq"]
+    assert np.array_equal(R["uniq"], tab["uniq"])
+    assert np.array_equal(R["slot"], tab["slot"].ravel())
+    assert np.array_equal(R["pair_off"], tab["pair_off"])
+    npairs = int(tab["pair_off"][-1])
+    assert np.array_equal(R["pairs"][:npairs], tab["pairs"])
+    if case == "duplicate":
+        pb.ids = ids
+        check_staged(qg, orc, pb, y, ws)
+        return
+    # dropped pairs add nothing: the same as their weights set to zero with usable experts
+    keep = (eff >= 0) & (eff < E)
+    rw0 = np.where(keep, pb.rw, 0.0).astype(np.float32)
+    yz, _, stz = pb.run(rw=rw0)
+    assert stz == qg.DEV_OK
+    assert np.array_equal(y.view(np.uint32), yz.view(np.uint32))
+    if case == "all_invalid":
+        assert R["n_uniq"] == 0 and np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("topk", [64, 65])
+def test_moe_one_token_many_pairs(qg, orc, topk):
+    """One token with 64 pairs (the table built in the first expert launch) and with 65 (the
+    table kernel): stage-by-stage parity over a workspace filled with 0xFF."""
+    progress("moe one token topk=%d" % topk)
+    pb = MoeProblem(qg, 80, 256, 256, 1, topk, 22)
+    y, ws, st = pb.run(ws_fill=0xFF)
+    assert st == 0
+    check_staged(qg, orc, pb, y, ws)
 
 
 def test_moe_host_errors_touch_nothing(qg):

@@ -13,7 +13,7 @@ import pytest
 import synth
 from tests import fmt_helpers as fh
 from tests.gpu_util import assert_within_bound, dev, empty, host, oracle_threads, progress, sentinel
-from tests.test_gpu_moe import MoeProblem, check_staged
+from tests.test_gpu_moe import ONE_TOKEN_CASES, MoeProblem, check_staged, one_token_table_case
 
 pytestmark = pytest.mark.gpu
 
@@ -194,6 +194,14 @@ def test_moe_mx_full_size_t1(qg, orc, name):
     y, ws, st = pb.run()
     assert st == 0
     check_staged(qg, orc, pb, y, ws)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", ONE_TOKEN_CASES)
+def test_moe_mx_one_token_table_and_status(qg, orc, fmt, case):
+    """The expert formats with one token (the table built in the gate/up launch): table, status
+    and dropped pairs as for Q4_K experts."""
+    one_token_table_case(qg, orc, case, fmt=fmt)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
