@@ -307,10 +307,12 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
         out["moe_" + key.split("_", 1)[1]] = {
             "tokens_per_s": round(T / sec, 1), "us_per_call": round(sec * 1e6, 3), "mean_distinct_experts": float(uniq),
             "GB_s": round(byts / sec / 1e9, 1), "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4),
-            "includes": ("quantize_act_q8 of the T tokens + moe_routed_qgemv (4 launches at T=1, 5 for 2-8 tokens, "
-                         "7 from 9 tokens: the popular experts' matrix-core launches)"
+            "includes": ("quantize_act_q8 of the T tokens + moe_routed_qgemv (3 launches at T=1, the table built "
+                         "in the gate/up launch; 5 for 2-8 tokens; 7 from 9 tokens: the popular experts' "
+                         "matrix-core launches)"
                          if fmt == qg.FMT_Q4K else
-                         "quantize_act_q8 of the T tokens + moe_routed_qgemv_fmt (5 launches)")}
+                         "quantize_act_q8 of the T tokens + moe_routed_qgemv_fmt (4 launches at T=1, the table "
+                         "built in the gate/up launch; 5 otherwise)")}
         del gr, pools, ws
         torch.cuda.empty_cache()
 
