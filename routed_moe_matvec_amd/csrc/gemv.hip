@@ -99,9 +99,12 @@ static int launch_gemv(GemvArgs &a, hipStream_t stream) {
     const int wg_per_cu = max(1, min(32 / a.waves, (int)(kLdsBytes / lds)));
     // Two tiles per wave only pay when registers allow the extra set: for
     // M = 1 more workgroups in staggered rounds measured faster, and the
-    // 8-block Q8_0 unit would spill.
+    // 8-block Q8_0 unit would spill.  The second register set also leaves
+    // room for only one 8-wave workgroup per CU, so where the LDS admits two,
+    // one tile per wave is taken (16384 x 4096, 2 tokens: 17.7 -> 14.7 us).
     a.tpw = tiles_per_wave(tiles, cus * wg_per_cu * a.waves,
-                           a.M > 1 && a.M <= a.mt && !(FMT == QG_FMT_Q8_0 && NB == 8));
+                           a.M > 1 && a.M <= a.mt && !(FMT == QG_FMT_Q8_0 && NB == 8) &&
+                               !(a.waves == kGemvMaxWaves && wg_per_cu >= 2));
     const int per_wg = a.waves * a.tpw;
     a.nwg0 = (a.nt0 + per_wg - 1) / per_wg;
     const int grid = a.nwg0 + (a.nt1 + per_wg - 1) / per_wg;
