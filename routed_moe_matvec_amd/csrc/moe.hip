@@ -313,28 +313,26 @@ __device__ __forceinline__ TokenTable token_table(const int32_t *ids, int P, int
     t.pg = as_global<uintptr_t>(gate)[ec];
     t.pu = as_global<uintptr_t>(up)[ec];
     t.pd = as_global<uintptr_t>(down)[ec];
-    // lanes with the same id: those that agree on every bit of an id
+    // the in-range lanes with the same id and with a smaller one, bit by bit
+    // from the top: a lane keeps the lanes that agree with it on the bits so
+    // far (eq), and those that agree above bit b and hold 0 where it holds 1
+    // are smaller (lt)
     const int ebits = 32 - __clz(max(E - 1, 1));
-    uint64_t m = __ballot(t.in_range);
-    for (int b = 0; b < ebits; ++b) {
+    uint64_t eq = __ballot(t.in_range), lt = 0;
+    for (int b = ebits - 1; b >= 0; --b) {
         const bool one = (t.e >> b) & 1;
         const uint64_t ones = __ballot(one);
-        m &= one ? ones : ~ones;
+        if (one) lt |= eq & ~ones;
+        eq &= one ? ones : ~ones;
     }
-    t.same = m;
+    t.same = eq;
     const auto unusable = [](uintptr_t q) { return q == 0 || (q & 15) != 0; };
     t.usable = t.in_range && !unusable(t.pg) && !unusable(t.pu) && !unusable(t.pd);
-    t.first = __ballot(t.usable && (m & ((1ull << l) - 1ull)) == 0);
-    // slot and first place: the usable experts with a smaller id, and their pairs
-    t.rank = 0;
-    t.off = 0;
-    for (uint64_t f = t.first; f; f &= f - 1) {
-        const int j = __ffsll((unsigned long long)f) - 1;  // wave-uniform
-        if (__builtin_amdgcn_readlane(t.e, j) < t.e) {
-            ++t.rank;
-            t.off += __popcll(readlane64(m, j));
-        }
-    }
+    t.first = __ballot(t.usable && (eq & ((1ull << l) - 1ull)) == 0);
+    // slot: the usable experts with a smaller id; first place: their pairs
+    // (an expert is usable for all of its pairs or none)
+    t.rank = __popcll(lt & t.first);
+    t.off = __popcll(lt & __ballot(t.usable));
     return t;
 }
 
@@ -922,7 +920,9 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     // Q4_K experts with many pairs go to the matrix cores (possible from kMoeMm tokens on)
     const int mm_on = fmt == QG_FMT_Q4K && T >= kMoeMm;
     // one token with at most 64 pairs: the gate/up launch builds the table
-    // itself; otherwise the table kernel runs first
+    // itself; otherwise the table kernel runs first.  (Batches with few
+    // pairs measured slower so: each of their many workgroup rounds pays the
+    // ids-then-pointers chain, T = 8: 123.8 -> 130.0 us.)
     const bool own_table = T == 1 && P <= kWave;
     if (!own_table) {
         hipLaunchKernelGGL(moe_table_kernel, dim3(1), dim3(kWave), 0, st, ids, P, E, gate, up, down, w, d_status,

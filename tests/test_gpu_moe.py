@@ -360,12 +360,12 @@ def one_token_table_case(qg, orc, case, fmt):
         assert R["n_uniq"] == 0 and np.all(y == 0.0)
 
 
-@pytest.mark.parametrize("topk", [64, 65])
-def test_moe_one_token_many_pairs(qg, orc, topk):
-    """One token with 64 pairs (the table built in the first expert launch) and with 65 (the
-    table kernel): stage-by-stage parity over a workspace filled with 0xFF."""
-    progress("moe one token topk=%d" % topk)
-    pb = MoeProblem(qg, 80, 256, 256, 1, topk, 22)
+@pytest.mark.parametrize("T,topk", [(1, 64), (1, 65), (8, 8), (5, 13)])
+def test_moe_one_token_many_pairs(qg, orc, T, topk):
+    """64 pairs (the table built in the first expert launch) and 65 (the table kernel), with one
+    token and with several: stage-by-stage parity over a workspace filled with 0xFF."""
+    progress("moe many pairs T=%d topk=%d" % (T, topk))
+    pb = MoeProblem(qg, 80, 256, 256, T, topk, 22)
     y, ws, st = pb.run(ws_fill=0xFF)
     assert st == 0
     check_staged(qg, orc, pb, y, ws)
