@@ -661,8 +661,9 @@ def main():
         print(summarize_pmc(*args.summarize_pmc))
         return 0
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the decode mat-vec would "
-              "shard by output rows with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the decode mat-vec would "
+              "shard by output rows with no exchange, the routed experts by expert). Run with --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import torch
