@@ -692,13 +692,34 @@ __global__ __launch_bounds__(256) void moe_h_quant_kernel(MoeWs ws, int P, int F
 
 // ---------------------------------------------------------------- 4. combine
 
+// V consecutive outputs per thread (1, 2 or 4; D % 4 == 0): fewer per
+// thread spread a small batch's loads over more CUs.
+template <int V>
+struct CombineVec;
+template <>
+struct CombineVec<1> {
+    typedef float type;
+};
+template <>
+struct CombineVec<2> {
+    typedef float2 type;
+};
+template <>
+struct CombineVec<4> {
+    typedef float4 type;
+};
+
+template <int V>
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeWs ws, const float *__restrict__ rw, int T, int D,
                                                           int topk, float *__restrict__ y) {
+    typedef typename CombineVec<V>::type vec;
     const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-    const int per_t = D / 4;
+    const int per_t = D / V;
     if (gid >= T * per_t) return;
-    const int t = gid / per_t, n4 = gid - t * per_t;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int t = gid / per_t, n = gid - t * per_t;
+    float acc[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = 0.0f;
     // eight pairs at a time: every load is issued before the first use (a
     // load behind a branch on the slot would wait twice per pair); pairs past
     // topk re-read the last one and are not used
@@ -706,26 +727,40 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeWs ws, const float 
     for (int k0 = 0; k0 < topk; k0 += kU) {
         int sl[kU];
         float r[kU];
-        float4 o[kU];
+        vec o[kU];
 #pragma unroll
         for (int j = 0; j < kU; ++j) {
             const int p = t * topk + min(k0 + j, topk - 1);
             sl[j] = ws.slot[p];
             r[j] = rw[p];
-            o[j] = *reinterpret_cast<const float4 *>(ws.o + (size_t)p * D + 4 * n4);
+            o[j] = *reinterpret_cast<const vec *>(ws.o + (size_t)p * D + V * n);
         }
 #pragma unroll
         for (int j = 0; j < kU; ++j) {
             // an invalid id or unusable expert (slot -1) contributes nothing
             if (k0 + j < topk && sl[j] >= 0) {
-                acc.x = fmaf_exact(r[j], o[j].x, acc.x);
-                acc.y = fmaf_exact(r[j], o[j].y, acc.y);
-                acc.z = fmaf_exact(r[j], o[j].z, acc.z);
-                acc.w = fmaf_exact(r[j], o[j].w, acc.w);
+                const float *oj = reinterpret_cast<const float *>(&o[j]);
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[e] = fmaf_exact(r[j], oj[e], acc[e]);
             }
         }
     }
-    *reinterpret_cast<float4 *>(y + (size_t)t * D + 4 * n4) = acc;
+    *reinterpret_cast<vec *>(y + (size_t)t * D + V * n) = *reinterpret_cast<const vec *>(acc);
+}
+
+// The combine launch: one output per thread while the batch's outputs fill
+// fewer than 64 workgroups of 256 threads that way, else four.
+static int launch_combine(const MoeWs &w, const float *rw, int T, int D, int topk, float *y, hipStream_t st) {
+    const long long n1 = (long long)T * D;
+    if (n1 < 64LL * 256) {
+        hipLaunchKernelGGL(moe_combine_kernel<1>, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, st, w, rw, T, D,
+                           topk, y);
+    } else {
+        const long long n4 = n1 / 4;
+        hipLaunchKernelGGL(moe_combine_kernel<4>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, w, rw, T, D,
+                           topk, y);
+    }
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
 static MoeWs ws_pointers(void *ws, const size_t off[QG_WS_COUNT]) {
@@ -958,10 +993,7 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
         rc = fmt == QG_FMT_FP8_E4M3_B128 ? launch_moe_mx<QG_FMT_FP8_E4M3_B128>(a, Ucap, true, false, st)
                                          : launch_moe_mx<QG_FMT_FP4_E2M1_MX>(a, Ucap, true, false, st);
         if (rc) return rc;
-        const long long cthreads = (long long)T * (D / 4);
-        hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cthreads + 255) / 256)), dim3(256), 0, st, w, rw, T,
-                           D, topk, y);
-        return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+        return launch_combine(w, rw, T, D, topk, y, st);
     }
     const bool one = T == 1;  // every expert then has a single pair (a few if the token repeats an id)
     constexpr int threads = kMoeWaves * kWave;
@@ -1002,10 +1034,7 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
         if (rc) return rc;
     }
 
-    const long long cthreads = (long long)T * (D / 4);
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cthreads + 255) / 256)), dim3(256), 0, st, w, rw, T, D,
-                       topk, y);
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+    return launch_combine(w, rw, T, D, topk, y, st);
 }
 
 extern "C" int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t *sx, int T, int D, int F, int E,
