@@ -585,7 +585,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void moe_mm_down_kernel(MoeArg
 // up of expert uniq[blockIdx.y] on the mx engine, workgroups [0, nwg) on gate
 // rows and [nwg, 2 nwg) on up rows, the tokens being the expert's pairs'.
 template <int FMT, int CPL, bool OWN>
-__global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs a, int nwg) {
+__global__ __launch_bounds__(mx_routed_waves(FMT) * kWave) void moe_gate_up_mx_kernel(MoeArgs a, int nwg) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int R = mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int u = blockIdx.y;
@@ -609,8 +609,8 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs
     const int topk = a.topk, F = a.F;
     if constexpr (OWN) {
         // one token: every pair's token is 0
-        mx_workgroup<FMT, CPL, kMxLoadsRouted>(
-            W, F, a.D, wg * kMxWaves * R, cnt, a.mt, a.qx, a.dx, [](int) { return 0; },
+        mx_workgroup<FMT, CPL, kMxLoadsRouted, mx_routed_waves(FMT)>(
+            W, F, a.D, wg * mx_routed_waves(FMT) * R, cnt, a.mt, a.qx, a.dx, [](int) { return 0; },
             [=](int m, int row, float v) { dst[(size_t)nth_bit(own, m) * F + row] = v; }, smem);
         return;
     }
@@ -618,19 +618,19 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_gate_up_mx_kernel(MoeArgs
         // one pair (the usual case in decode): its token is read once, as a
         // scalar, so no vector load has to return before the weights are requested
         const int p = load_uniform(pairs), tok = p / topk;
-        mx_workgroup<FMT, CPL, kMxLoadsRouted>(
-            W, F, a.D, wg * kMxWaves * R, 1, a.mt, a.qx, a.dx, [=](int) { return tok; },
+        mx_workgroup<FMT, CPL, kMxLoadsRouted, mx_routed_waves(FMT)>(
+            W, F, a.D, wg * mx_routed_waves(FMT) * R, 1, a.mt, a.qx, a.dx, [=](int) { return tok; },
             [=](int, int row, float v) { dst[(size_t)p * F + row] = v; }, smem);
         return;
     }
-    mx_workgroup<FMT, CPL, kMxLoadsRouted>(
-        W, F, a.D, wg * kMxWaves * R, cnt, a.mt, a.qx, a.dx, [=](int m) { return pairs[m] / topk; },
+    mx_workgroup<FMT, CPL, kMxLoadsRouted, mx_routed_waves(FMT)>(
+        W, F, a.D, wg * mx_routed_waves(FMT) * R, cnt, a.mt, a.qx, a.dx, [=](int m) { return pairs[m] / topk; },
         [=](int m, int row, float v) { dst[(size_t)pairs[m] * F + row] = v; }, smem);
 }
 
 // down of expert uniq[blockIdx.y] on the mx engine against each pair's Q8 h.
 template <int FMT, int CPL>
-__global__ __launch_bounds__(kMxWaves *kWave) void moe_down_mx_kernel(MoeArgs a) {
+__global__ __launch_bounds__(mx_routed_waves(FMT) * kWave) void moe_down_mx_kernel(MoeArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int R = mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int u = blockIdx.y;
@@ -645,13 +645,13 @@ __global__ __launch_bounds__(kMxWaves *kWave) void moe_down_mx_kernel(MoeArgs a)
     const int D = a.D;
     if (cnt == 1) {
         const int p = load_uniform(pairs);
-        mx_workgroup<FMT, CPL, kMxLoadsRouted>(
-            W, D, a.F, (int)blockIdx.x * kMxWaves * R, 1, a.mt, a.ws.hq, a.ws.hd, [=](int) { return p; },
+        mx_workgroup<FMT, CPL, kMxLoadsRouted, mx_routed_waves(FMT)>(
+            W, D, a.F, (int)blockIdx.x * mx_routed_waves(FMT) * R, 1, a.mt, a.ws.hq, a.ws.hd, [=](int) { return p; },
             [=](int, int row, float v) { o[(size_t)p * D + row] = v; }, smem);
         return;
     }
-    mx_workgroup<FMT, CPL, kMxLoadsRouted>(
-        W, D, a.F, (int)blockIdx.x * kMxWaves * R, cnt, a.mt, a.ws.hq, a.ws.hd, [=](int m) { return pairs[m]; },
+    mx_workgroup<FMT, CPL, kMxLoadsRouted, mx_routed_waves(FMT)>(
+        W, D, a.F, (int)blockIdx.x * mx_routed_waves(FMT) * R, cnt, a.mt, a.ws.hq, a.ws.hd, [=](int m) { return pairs[m]; },
         [=](int m, int row, float v) { o[(size_t)pairs[m] * D + row] = v; }, smem);
 }
 
@@ -794,11 +794,14 @@ static int launch_moe_gate_up_mx_own(MoeArgs a, int Ucap, hipStream_t st) {
     static bool raised = false;
     if (!raised) raised = raise_lds_limit(moe_gate_up_mx_kernel<FMT, CPL, OWN>, kMxLdsMax);
     if (!raised) return QG_ERR_LAUNCH;
-    const int rows_per_wg = kMxWaves * mx_rows_per_wave(kMxLoadsRouted, CPL);
+    const int rows_per_wg = mx_routed_waves(FMT) * mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int nwg = (a.F + rows_per_wg - 1) / rows_per_wg;
     a.mt = mx_tokens_per_chunk(a.D, QG_MAX_MOE_PAIRS);
-    hipLaunchKernelGGL((moe_gate_up_mx_kernel<FMT, CPL, OWN>), dim3(2 * nwg, Ucap), dim3(kMxWaves * kWave),
-                       (size_t)a.mt * mx_token_rec(a.D) + mx_scale_lds<FMT>(a.D, CPL, kMxLoadsRouted), st, a, nwg);
+    hipLaunchKernelGGL((moe_gate_up_mx_kernel<FMT, CPL, OWN>), dim3(2 * nwg, Ucap),
+                       dim3(mx_routed_waves(FMT) * kWave),
+                       (size_t)a.mt * mx_token_rec(a.D) +
+                           mx_scale_lds<FMT>(a.D, CPL, kMxLoadsRouted, mx_routed_waves(FMT)),
+                       st, a, nwg);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
@@ -814,11 +817,14 @@ static int launch_moe_down_mx(MoeArgs a, int Ucap, hipStream_t st) {
     static bool raised = false;
     if (!raised) raised = raise_lds_limit(moe_down_mx_kernel<FMT, CPL>, kMxLdsMax);
     if (!raised) return QG_ERR_LAUNCH;
-    const int rows_per_wg = kMxWaves * mx_rows_per_wave(kMxLoadsRouted, CPL);
+    const int rows_per_wg = mx_routed_waves(FMT) * mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int nwg = (a.D + rows_per_wg - 1) / rows_per_wg;
     a.mt = mx_tokens_per_chunk(a.F, QG_MAX_MOE_PAIRS);
-    hipLaunchKernelGGL((moe_down_mx_kernel<FMT, CPL>), dim3(nwg, Ucap), dim3(kMxWaves * kWave),
-                       (size_t)a.mt * mx_token_rec(a.F) + mx_scale_lds<FMT>(a.F, CPL, kMxLoadsRouted), st, a);
+    hipLaunchKernelGGL((moe_down_mx_kernel<FMT, CPL>), dim3(nwg, Ucap),
+                       dim3(mx_routed_waves(FMT) * kWave),
+                       (size_t)a.mt * mx_token_rec(a.F) +
+                           mx_scale_lds<FMT>(a.F, CPL, kMxLoadsRouted, mx_routed_waves(FMT)),
+                       st, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 

@@ -34,8 +34,7 @@ namespace qg {
 typedef _Float16 mx_half2 __attribute__((ext_vector_type(2)));
 typedef unsigned int mx_u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMxWaves = 4;
-constexpr int kMxThreads = kMxWaves * 64;  // every launch of the engine uses this many threads
+constexpr int kMxWaves = 4;  // waves per workgroup of the dense calls (mx_workgroup's NW)
 // 16-byte weight chunks a lane keeps in flight (L).  Dense mat-vecs: 4 for
 // FP8, 8 for FP4 (its decode costs twice the instructions per byte); fewer
 // rows per wave and more waves measured faster for both than 16.  Routed
@@ -43,6 +42,10 @@ constexpr int kMxThreads = kMxWaves * 64;  // every launch of the engine uses th
 // pair list and the staged tokens, a cost more rows amortize.
 __host__ __device__ constexpr int mx_loads(int fmt) { return fmt == QG_FMT_FP4_E2M1_MX ? 8 : 4; }
 constexpr int kMxLoadsRouted = 16;
+// Waves per workgroup of the routed kernels: 8 for FP8 (each expert's rows in
+// half as many workgroups, which share one staging of the tokens; measured
+// faster at one token), 4 for FP4 (measured faster, as for the dense calls).
+__host__ __device__ constexpr int mx_routed_waves(int fmt) { return fmt == QG_FMT_FP8_E4M3_B128 ? 8 : kMxWaves; }
 constexpr int kMxActBudget = 64 * 1024;  // LDS for staged tokens
 constexpr int kMxLdsMax = kMxActBudget + 4096;  // with a workgroup's weight scales
 constexpr int kMxBlockRec = 80;          // LDS bytes of one 32-block of fp16 activation (64 + pad)
@@ -79,12 +82,12 @@ struct MxFmt<QG_FMT_FP4_E2M1_MX> {
 __host__ __device__ inline int mx_token_rec(int K) { return (K / 32) * (kMxBlockRec + 4); }
 
 // LDS bytes of a workgroup's weight scales, after the staged tokens: FP4 the
-// [rows][K/32] scales of its kMxWaves * R rows, FP8 the one [K/128] row of
+// [rows][K/32] scales of its waves * R rows, FP8 the one [K/128] row of
 // its 128-row block (a workgroup's rows never straddle one: their count
 // divides 128).
 template <int FMT>
-__host__ __device__ inline int mx_scale_lds(int K, int cpl, int loads) {
-    const int rows = kMxWaves * mx_rows_per_wave(loads, cpl);
+__host__ __device__ inline int mx_scale_lds(int K, int cpl, int loads, int waves = kMxWaves) {
+    const int rows = waves * mx_rows_per_wave(loads, cpl);
     const int bytes = FMT == QG_FMT_FP4_E2M1_MX ? rows * (K / 32) : K / 128;
     return (bytes + 15) / 16 * 16;
 }
@@ -156,11 +159,11 @@ __device__ __forceinline__ float mx_chunk_dot(const mx_u32x4 &w, const uint8_t *
     return p;
 }
 
-// One workgroup (kMxWaves waves) multiplies rows row_base .. row_base +
-// kMxWaves * R - 1 of W (clipped to N), R = mx_rows_per_wave(L, CPL), with M tokens; token m's activation is
+// One workgroup (NW waves) multiplies rows row_base .. row_base +
+// NW * R - 1 of W (clipped to N), R = mx_rows_per_wave(L, CPL), with M tokens; token m's activation is
 // row token_row(m) of qx / dx; out(m, row, value) stores a result.  Tokens are
 // staged mt at a time.  Every wave of the workgroup must call this.
-template <int FMT, int CPL, int L, class TokenRow, class Out>
+template <int FMT, int CPL, int L, int NW = kMxWaves, class TokenRow, class Out>
 __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int N, int K, int row_base, int M, int mt,
                                              const int8_t *__restrict__ qx, const float *__restrict__ dx,
                                              TokenRow token_row, Out out, uint8_t *smem) {
@@ -205,11 +208,11 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
     };
     // staging after the first chunk of tokens: loads and stores together
     auto stage = [&](int m0, int mtc, int from) {
-        for (int t = from + threadIdx.x; t < mtc * pieces; t += kMxThreads) {
+        for (int t = from + threadIdx.x; t < mtc * pieces; t += (NW * kWave)) {
             const int mm = t / pieces;
             put_piece(mm, t - mm * pieces, *piece_src(m0, t));
         }
-        for (int t = from + threadIdx.x; t < mtc * nb; t += kMxThreads) put_dx(m0, t, *dx_src(m0, t));
+        for (int t = from + threadIdx.x; t < mtc * nb; t += (NW * kWave)) put_dx(m0, t, *dx_src(m0, t));
     };
 
     // First chunk of tokens: its first kMxStageRegs pieces and scales per
@@ -224,7 +227,7 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
     uint8_t *lsc = smem + (size_t)mt * rec;
     const size_t row_scale_bytes = FMT == QG_FMT_FP4_E2M1_MX ? (size_t)(K / 32) : 0;
     const size_t scale_total = FMT == QG_FMT_FP4_E2M1_MX ? (size_t)N * (K / 32) : (size_t)((N + 127) / 128) * (K / 128);
-    const int scale_bytes = FMT == QG_FMT_FP4_E2M1_MX ? kMxWaves * R * (K / 32) : K / 128;
+    const int scale_bytes = FMT == QG_FMT_FP4_E2M1_MX ? NW * R * (K / 32) : K / 128;
     const uint8_t *scale_src = FMT == QG_FMT_FP4_E2M1_MX ? scales + (size_t)row_base * row_scale_bytes
                                                           : scales + (size_t)(row_base >> 7) * (K / 128);
     mx_u32x4 sreg = {0u, 0u, 0u, 0u};
@@ -245,7 +248,7 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
     float dreg[kMxStageRegs];
 #pragma unroll
     for (int i = 0; i < kMxStageRegs; ++i) {
-        const int t = threadIdx.x + i * kMxThreads;
+        const int t = threadIdx.x + i * (NW * kWave);
         qreg[i] = *piece_src(0, min(t, mt0 * pieces - 1));
         dreg[i] = *dx_src(0, min(t, mt0 * nb - 1));
     }
@@ -275,11 +278,11 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
         lsc[lsc_off] = (uint8_t)sbyte;
 #pragma unroll
     for (int i = 0; i < kMxStageRegs; ++i) {
-        const int tq = min((int)threadIdx.x + i * kMxThreads, mt0 * pieces - 1);
+        const int tq = min((int)threadIdx.x + i * (NW * kWave), mt0 * pieces - 1);
         put_piece(tq / pieces, tq - (tq / pieces) * pieces, qreg[i]);
-        put_dx(0, min((int)threadIdx.x + i * kMxThreads, mt0 * nb - 1), dreg[i]);
+        put_dx(0, min((int)threadIdx.x + i * (NW * kWave), mt0 * nb - 1), dreg[i]);
     }
-    stage(0, mt0, kMxStageRegs * kMxThreads);
+    stage(0, mt0, kMxStageRegs * (NW * kWave));
 
     // token mm of the chunk at m0 against every row of the wave
     auto token = [&](int m0, int mm) __attribute__((always_inline)) {
