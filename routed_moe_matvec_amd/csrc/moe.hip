@@ -35,9 +35,9 @@ namespace qg {
 
 constexpr int kMoeWaves = 4;
 // tokens staged at once by the several-token expert kernels: most experts of
-// a decode batch have one or two pairs, and a smaller staging area lets three
-// workgroups share a CU's LDS instead of two
-constexpr int kMoeChunk = 2;
+// a decode batch have a few pairs, and a staging area of up to three tokens
+// still lets three workgroups share a CU's LDS (four would leave two)
+constexpr int kMoeChunk = 3;
 constexpr int kTableWords = QG_MAX_EXPERTS / 32;  // bitmap words over the expert ids
 // Q4_K experts with at least kMoeMm pairs run on the matrix cores (tiles of 32
 // pairs) when T >= kMoeMm; the dot-product kernels leave them out
