@@ -311,8 +311,9 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
                          "in the gate/up launch; 5 for 2-8 tokens; 7 from 9 tokens: the popular experts' "
                          "matrix-core launches)"
                          if fmt == qg.FMT_Q4K else
-                         "quantize_act_q8 of the T tokens + moe_routed_qgemv_fmt (4 launches at T=1, the table "
-                         "built in the gate/up launch; 5 otherwise)")}
+                         "quantize_act_q8 of the T tokens + moe_routed_qgemv_fmt (at T=1 the table built in the "
+                         "gate/up launch: 4 launches, 3 for FP4 experts whose down launch also forms h; 5 "
+                         "otherwise)")}
         del gr, pools, ws
         torch.cuda.empty_cache()
 

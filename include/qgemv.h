@@ -350,7 +350,9 @@ int moe_routed_qgemv(const int8_t *qx, const float *dx, const int32_t *sx, int T
  * QG_FMT_FP8_E4M3_B128 and QG_FMT_FP4_E2M1_MX (each gate/up/down pointer then
  * points at one qg_matrix_bytes(fmt, ...) buffer).  Steps 1-4 as above; with
  * the block-scaled formats gate/up and down run the qgemv_mx engine, and h is
- * Q8-quantized once per pair before the down projection, for every T.
+ * Q8-quantized once per pair before the down projection (for one token with
+ * FP4 experts inside the down launch, while it stages h; the workspace holds
+ * h and its Q8 form either way).
  * Errors: QG_ERR_FORMAT for any other fmt; otherwise as moe_routed_qgemv.
  */
 int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, const int32_t *sx, int T, int D, int F, int E,

@@ -395,7 +395,6 @@ constexpr int kSrcQ8 = 0;
 constexpr int kSrcF32 = 1;
 constexpr int kSrcGLU = 2;
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Staging from fp32: load() reads the first kActRegChunks 16-byte chunks
 // (4 values each) per thread into registers, store() quantizes each 32-block

@@ -28,11 +28,25 @@
 #pragma once
 
 #include "common.h"
+#include "quantize_device.h"
 
 namespace qg {
 
 typedef _Float16 mx_half2 __attribute__((ext_vector_type(2)));
 typedef unsigned int mx_u32x4 __attribute__((ext_vector_type(4)));
+typedef float mx_f32x4 __attribute__((ext_vector_type(4)));
+
+// One token's activation given as the SwiGLU inputs instead of a Q8 vector:
+// the staging forms h = silu(g) * v and its Q8 form itself (the activation
+// quantizer, so the values equal a separate quantization bit for bit); when
+// ph is set the workgroup also stores h, its quants, scales and block sums.
+struct MxGlu {
+    const float *g, *v;  // the token's rows (K values each)
+    float *ph;
+    int8_t *pqx;
+    float *pdx;
+    int32_t *psx;
+};
 
 constexpr int kMxWaves = 4;  // waves per workgroup of the dense calls (mx_workgroup's NW)
 // 16-byte weight chunks a lane keeps in flight (L).  Dense mat-vecs: 4 for
@@ -163,10 +177,12 @@ __device__ __forceinline__ float mx_chunk_dot(const mx_u32x4 &w, const uint8_t *
 // NW * R - 1 of W (clipped to N), R = mx_rows_per_wave(L, CPL), with M tokens; token m's activation is
 // row token_row(m) of qx / dx; out(m, row, value) stores a result.  Tokens are
 // staged mt at a time.  Every wave of the workgroup must call this.
-template <int FMT, int CPL, int L, int NW = kMxWaves, class TokenRow, class Out>
+// GLU: one token (M = 1) whose activation is glu's SwiGLU inputs (MxGlu);
+// qx, dx and token_row are then unused.
+template <int FMT, int CPL, int L, int NW = kMxWaves, bool GLU = false, class TokenRow, class Out>
 __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int N, int K, int row_base, int M, int mt,
                                              const int8_t *__restrict__ qx, const float *__restrict__ dx,
-                                             TokenRow token_row, Out out, uint8_t *smem) {
+                                             TokenRow token_row, Out out, uint8_t *smem, const MxGlu &glu = {}) {
     using F = MxFmt<FMT>;
     constexpr int R = mx_rows_per_wave(L, CPL);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -246,13 +262,62 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
     }
     mx_u32x4 qreg[kMxStageRegs];
     float dreg[kMxStageRegs];
+    // GLU: 16-byte chunks c of g and v (4 values; 8 lanes form a 32-block);
+    // the first kMxGluRegs per thread are read before the weights.  A wave
+    // past the end takes the last 64 chunks again (K / 4 is a multiple of 64):
+    // identical values to the same places.
+    constexpr int kMxGluRegs = 1;
+    const int gchunks = K / 4;
+    auto glu_chunk = [&](int t) __attribute__((always_inline)) {
+        return t < gchunks ? t : gchunks - kWave + lane;
+    };
+    mx_f32x4 greg[GLU ? kMxGluRegs : 1], vreg[GLU ? kMxGluRegs : 1];
+    if constexpr (GLU) {
 #pragma unroll
-    for (int i = 0; i < kMxStageRegs; ++i) {
-        const int t = threadIdx.x + i * (NW * kWave);
-        qreg[i] = *piece_src(0, min(t, mt0 * pieces - 1));
-        dreg[i] = *dx_src(0, min(t, mt0 * nb - 1));
+        for (int i = 0; i < kMxGluRegs; ++i) {
+            const int c = glu_chunk((int)threadIdx.x + i * (NW * kWave));
+            greg[i] = as_global<mx_f32x4>(glu.g)[c];
+            vreg[i] = as_global<mx_f32x4>(glu.v)[c];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kMxStageRegs; ++i) {
+            const int t = threadIdx.x + i * (NW * kWave);
+            qreg[i] = *piece_src(0, min(t, mt0 * pieces - 1));
+            dreg[i] = *dx_src(0, min(t, mt0 * nb - 1));
+        }
     }
     __builtin_amdgcn_sched_barrier(0);  // these loads are issued before the weights
+    // chunk c's h = silu(g) * v, quantized with its 8-lane group: the fp16
+    // quants and the scale into the token's record, h and the Q8 form to glu's
+    // outputs when given
+    auto glu_emit = [&](int c, mx_f32x4 g4, mx_f32x4 v4) __attribute__((always_inline)) {
+        float h[4] = {silu(g4.x) * v4.x, silu(g4.y) * v4.y, silu(g4.z) * v4.z, silu(g4.w) * v4.w};
+        int8_t q[4];
+        float d;
+        int32_t sum;
+        quantize_block_8lanes(h, q, &d, &sum);  // every lane takes part (shuffles)
+        const int blk = c >> 3, part = c & 7;
+        mx_half2 h01, h23;
+        h01.x = (_Float16)(float)q[0];
+        h01.y = (_Float16)(float)q[1];
+        h23.x = (_Float16)(float)q[2];
+        h23.y = (_Float16)(float)q[3];
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2 *>(smem + kMxBlockRec * blk + 8 * part) =
+            u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+        if (part == 0) put_dx(0, blk, d);
+        if (glu.ph) {
+            *reinterpret_cast<mx_f32x4 *>(glu.ph + 4 * c) = mx_f32x4{h[0], h[1], h[2], h[3]};
+            *reinterpret_cast<uint32_t *>(glu.pqx + 4 * c) = (uint32_t)(uint8_t)q[0] | ((uint32_t)(uint8_t)q[1] << 8) |
+                                                            ((uint32_t)(uint8_t)q[2] << 16) |
+                                                            ((uint32_t)(uint8_t)q[3] << 24);
+            if (part == 0) {
+                glu.pdx[blk] = d;
+                glu.psx[blk] = sum;
+            }
+        }
+    };
 
     // the wave's weight chunks and their scales (rows past N and chunks past
     // the row's end re-read the last ones and are not used)
@@ -276,13 +341,27 @@ __device__ __forceinline__ void mx_workgroup(const uint8_t *__restrict__ W, int 
         *reinterpret_cast<mx_u32x4 *>(lsc + lsc_off) = sreg;
     else
         lsc[lsc_off] = (uint8_t)sbyte;
+    if constexpr (GLU) {
 #pragma unroll
-    for (int i = 0; i < kMxStageRegs; ++i) {
-        const int tq = min((int)threadIdx.x + i * (NW * kWave), mt0 * pieces - 1);
-        put_piece(tq / pieces, tq - (tq / pieces) * pieces, qreg[i]);
-        put_dx(0, min((int)threadIdx.x + i * (NW * kWave), mt0 * nb - 1), dreg[i]);
+        for (int i = 0; i < kMxGluRegs; ++i)
+            glu_emit(glu_chunk((int)threadIdx.x + i * (NW * kWave)), greg[i], vreg[i]);
+        // chunks past the registers (rows longer than kMxGluRegs chunks per
+        // thread), whole waves at a time
+        for (int c0 = kMxGluRegs * (NW * kWave); c0 < gchunks; c0 += NW * kWave) {
+            if (c0 + wave * kWave < gchunks) {
+                const int c = c0 + (int)threadIdx.x;
+                glu_emit(c, as_global<mx_f32x4>(glu.g)[c], as_global<mx_f32x4>(glu.v)[c]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kMxStageRegs; ++i) {
+            const int tq = min((int)threadIdx.x + i * (NW * kWave), mt0 * pieces - 1);
+            put_piece(tq / pieces, tq - (tq / pieces) * pieces, qreg[i]);
+            put_dx(0, min((int)threadIdx.x + i * (NW * kWave), mt0 * nb - 1), dreg[i]);
+        }
+        stage(0, mt0, kMxStageRegs * (NW * kWave));
     }
-    stage(0, mt0, kMxStageRegs * (NW * kWave));
 
     // token mm of the chunk at m0 against every row of the wave
     auto token = [&](int m0, int mm) __attribute__((always_inline)) {

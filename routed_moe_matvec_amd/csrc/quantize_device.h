@@ -51,4 +51,9 @@ __device__ __forceinline__ void quantize_block_8lanes(const float v[4], int8_t q
     *s_out = s;
 }
 
+// SiLU, z * sigmoid(z), as z / (1 + e^-z) in fp32 (expf and a correctly
+// rounded division): the one definition every kernel that forms
+// h = silu(g) * v uses, so their h values agree bit for bit.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
 }  // namespace qg
