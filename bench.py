@@ -66,6 +66,9 @@ def kernel_source_hash(files=GEMV_SOURCES) -> str:
 
 # ----------------------------------------------------------------------------- timing helpers
 
+TRIALS = 7  # timed replays per measurement; the median is reported, with the interquartile range
+
+
 class Timer:
     """HIP-event timing of work enqueued on one stream."""
 
@@ -85,6 +88,19 @@ class Timer:
             e.record(self.stream)
         torch.cuda.synchronize()
         return s.elapsed_time(e) * 1e-3  # seconds
+
+    def trials(self, fn, per_trial: int, trials: int = TRIALS):
+        """One untimed call of fn, then `trials` timed calls; seconds per unit of work
+        (fn does per_trial units) of each trial."""
+        self.run(fn)
+        return [self.run(fn) / per_trial for _ in range(trials)]
+
+
+def spread(samples):
+    """Median and interquartile range (p25, p75) of a list of seconds, in microseconds."""
+    q = np.percentile(np.asarray(samples, np.float64) * 1e6, [25, 50, 75])
+    return {"median_us": round(float(q[1]), 3), "p25_us": round(float(q[0]), 3), "p75_us": round(float(q[2]), 3),
+            "trials": len(samples)}
 
 
 def capture(fn, n: int, stream):
@@ -181,28 +197,123 @@ class DecodeStep:
         self.qg.qgemv_q8_0(self.W[i % self.R], self.N, self.K, self.qx, self.dx, 1, self.y)
 
 
-def cpu_baseline(step: DecodeStep, budget_s: float = 12.0) -> dict:
+def host_threads() -> int:
+    """Host cores this process may use (its CPU affinity, capped by OMP_NUM_THREADS when set)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(step: DecodeStep, budget_s: float = 8.0) -> dict:
     """The CPU oracle, untuned, on the same step: quantize both activations and run the
-    three products in fp64 on all host cores; as many whole steps as fit in ~budget_s."""
+    three products in fp64, as many whole steps as fit in ~budget_s, once on all the
+    host cores this process may use (OpenMP over rows) and once on one thread."""
     import oracle
-    threads = max(1, os.cpu_count() or 1)
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        qx, dx, _ = oracle.quantize_act_q8(step.x_host)
-        oracle.gemv(oracle.FMT_Q8_0, step.W_host, step.N, step.K, qx, dx, nthreads=threads)
-        qx2, dx2, _ = oracle.quantize_act_q8(step.x2_host)
-        oracle.gemv(oracle.FMT_Q8_0, step.W1_host, step.N1, step.K2, qx2, dx2, nthreads=threads)
-        oracle.gemv(oracle.FMT_Q8_0, step.W2_host, step.N2, step.K2, qx2, dx2, nthreads=threads)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per_step = el / n
-    return {"value": round(step.step_bytes / per_step / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "ms_per_step": round(per_step * 1e3, 3),
-            "sample": "%d whole steps of the same decode workload (quantize 8192 + Q8_0 4096x8192 + quantize "
-                      "4096 + Q8_0 1024x4096 and 512x4096), fp64 oracle with OpenMP over rows" % n}
+
+    def leg(threads):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            qx, dx, _ = oracle.quantize_act_q8(step.x_host)
+            oracle.gemv(oracle.FMT_Q8_0, step.W_host, step.N, step.K, qx, dx, nthreads=threads)
+            qx2, dx2, _ = oracle.quantize_act_q8(step.x2_host)
+            oracle.gemv(oracle.FMT_Q8_0, step.W1_host, step.N1, step.K2, qx2, dx2, nthreads=threads)
+            oracle.gemv(oracle.FMT_Q8_0, step.W2_host, step.N2, step.K2, qx2, dx2, nthreads=threads)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                return n, el / n
+
+    threads = host_threads()
+    n_all, per_all = leg(threads)
+    n_one, per_one = leg(1)
+    return {"value": round(step.step_bytes / per_all / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "ms_per_step": round(per_all * 1e3, 3),
+            "value_1thread": round(step.step_bytes / per_one / 1e9, 3), "ms_per_step_1thread": round(per_one * 1e3, 3),
+            "cpu_model": cpu_model(),
+            "sample": "%d whole steps on %d threads and %d on 1 thread of the same decode workload (quantize 8192 + "
+                      "Q8_0 4096x8192 + quantize 4096 + Q8_0 1024x4096 and 512x4096), fp64 oracle, OpenMP over "
+                      "rows" % (n_all, threads, n_one)}
+
+
+def gpu_clocks() -> dict:
+    """The GPU's current clocks as the driver reports them (read only; nothing is changed):
+    the graphics clock of each XCD (min and max over them), memory and SoC clocks, and
+    whether any clock is locked."""
+    import subprocess
+    try:
+        p = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        clk = json.loads(p.stdout)["gpu_data"][0]["clock"]
+    except (OSError, subprocess.TimeoutExpired, ValueError, KeyError, IndexError, TypeError):
+        return {"tool": "amd-smi metric -c", "report": "not available"}
+
+    def mhz(v):
+        c = v.get("clk") if isinstance(v, dict) else None
+        return c.get("value") if isinstance(c, dict) else None
+
+    gfx = [mhz(v) for k, v in clk.items() if k.startswith("gfx_") and mhz(v) is not None]
+    out = {"tool": "amd-smi metric -c", "gfx_mhz_min": min(gfx) if gfx else None,
+           "gfx_mhz_max": max(gfx) if gfx else None, "xcds": len(gfx)}
+    for key in ("mem_0", "socclk_0", "fclk_0"):
+        if key in clk:
+            out[key.split("_")[0] + "_mhz"] = mhz(clk[key])
+    g0 = clk.get("gfx_0", {})
+    out["gfx_max_mhz"] = (g0.get("max_clk") or {}).get("value") if isinstance(g0.get("max_clk"), dict) else None
+    out["locked"] = sorted({str(v.get("clk_locked")) for v in clk.values() if isinstance(v, dict)})
+    return out
+
+
+def read_ceilings(qg, torch, stream, timer, same_bytes: int) -> dict:
+    """Measured read rates of this part, by qg_stream_read (the library's streaming-read
+    diagnostic): the rate over a 1 GiB buffer read in one launch, and the best time per
+    launch for reading `same_bytes` once per launch, back to back in a graph, from
+    rotating places in that buffer (so no launch reads bytes left in a cache)."""
+    big = 1 << 30
+    buf = torch.empty(big, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    out = {}
+    g_big = qg.qg_stream_read_groups(big, 4, 4)
+    sink = torch.empty(max(g_big, 1), dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        t = timer.trials(lambda: qg.qg_stream_read(buf, big, 4, 4, sink, g_big, stream=stream), 1)
+    sp = spread(t)
+    out["read_1gib"] = dict(sp, GB_s=round(big / (sp["median_us"] * 1e-6) / 1e9, 1), chunk_kib=4, waves=4)
+    R = big // same_bytes
+    best = None
+    for kib, waves in ((2, 4), (4, 4), (8, 4), (4, 8), (8, 8)):
+        groups = qg.qg_stream_read_groups(same_bytes, kib, waves)
+        sk = torch.empty(groups, dtype=torch.int32, device="cuda")
+        n = max(R, 100)
+        gr = capture(lambda i: qg.qg_stream_read(buf[(i % R) * same_bytes:], same_bytes, kib, waves, sk, groups,
+                                                 stream=stream), n, stream)
+        sp = spread(timer.trials(gr.replay, n))
+        if best is None or sp["median_us"] < best["median_us"]:
+            best = dict(sp, chunk_kib=kib, waves=waves)
+        del gr
+    best["GB_s"] = round(same_bytes / (best["median_us"] * 1e-6) / 1e9, 1)
+    best["bytes"] = same_bytes
+    out["read_same_bytes"] = best
+    del buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def load_traffic(kernel_key: str, src_hash: str):
@@ -254,11 +365,11 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
                 fn = lambda i: qg.qgemv_q4k(copies[i % R], N, K, qx, dx, sx, M, y)
             n = max(R, 64)
             g = capture(fn, n, stream)
-            timer.run(g.replay)
-            sec = timer.run(g.replay) / n
+            sp = spread(timer.trials(g.replay, n))
+            sec = sp["median_us"] * 1e-6
             byts = W_host.nbytes + G * (M * K + M * (K // 32) * (8 if fmt == 1 else 4) + M * N * 4)
-            res["M%d" % M] = {"us": round(sec * 1e6, 3), "GB_s": round(byts / sec / 1e9, 1),
-                              "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4)}
+            res["M%d" % M] = {"us": round(sec * 1e6, 3), "iqr_us": [sp["p25_us"], sp["p75_us"]],
+                              "GB_s": round(byts / sec / 1e9, 1), "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4)}
             del g
         del copies, base
         torch.cuda.empty_cache()
@@ -299,13 +410,14 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
 
         n = 2 * n_sets
         gr = capture(call, n, stream)
-        timer.run(gr.replay)
-        sec = timer.run(gr.replay) / n
+        sp = spread(timer.trials(gr.replay, n))
+        sec = sp["median_us"] * 1e-6
         expert_bytes = 2 * qg.qg_matrix_bytes(fmt, F, D) + qg.qg_matrix_bytes(fmt, D, F)
         uniq = np.mean([len(np.unique(i)) for i in ids])
         byts = uniq * expert_bytes + T * D * 4 * 2 + T * topk * 8
         out["moe_" + key.split("_", 1)[1]] = {
-            "tokens_per_s": round(T / sec, 1), "us_per_call": round(sec * 1e6, 3), "mean_distinct_experts": float(uniq),
+            "tokens_per_s": round(T / sec, 1), "us_per_call": round(sec * 1e6, 3),
+            "iqr_us": [sp["p25_us"], sp["p75_us"]], "mean_distinct_experts": float(uniq),
             "GB_s": round(byts / sec / 1e9, 1), "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4),
             "includes": ("quantize_act_q8 of the T tokens + moe_routed_qgemv (3 launches at T=1, the table built "
                          "in the gate/up launch; 5 for 2-8 tokens; 7 from 9 tokens: the popular experts' "
@@ -336,9 +448,10 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
                 ("qgemm_prefill_ws", lambda i: qg.qgemm_prefill_ws(qg.FMT_Q4K, copies[i % R], N, K, xb, M, y, ws,
                                                                    nb))]:
             gr = capture(fn, R, stream)
-            timer.run(gr.replay)
-            sec = timer.run(gr.replay) / R
-            res[name] = {"us": round(sec * 1e6, 3), "TFLOP_s": round(flops / sec / 1e12, 1),
+            sp = spread(timer.trials(gr.replay, R))
+            sec = sp["median_us"] * 1e-6
+            res[name] = {"us": round(sec * 1e6, 3), "iqr_us": [sp["p25_us"], sp["p75_us"]],
+                         "TFLOP_s": round(flops / sec / 1e12, 1),
                          "mfma_frac": round(flops / sec / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4)}
             del gr
         res["includes"] = "qgemm_prefill_ws: the bf16 -> fp16 pre-pass and the GEMM"
@@ -360,10 +473,11 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
     yq = torch.empty(1, w["N"], dtype=torch.float32, device=dev)
     n = max(R, 64)
     gr = capture(lambda i: qg.qgemv_q8_0_quality(copies[i % R], w["N"], w["K"], xq, 1, yq), n, stream)
-    timer.run(gr.replay)
-    sec = timer.run(gr.replay) / n
+    sp = spread(timer.trials(gr.replay, n))
+    sec = sp["median_us"] * 1e-6
     byts = Wq.nbytes + w["K"] * 4 + w["N"] * 4
-    out["quality_q8_0_4096x8192"] = {"us": round(sec * 1e6, 3), "GB_s": round(byts / sec / 1e9, 1),
+    out["quality_q8_0_4096x8192"] = {"us": round(sec * 1e6, 3), "iqr_us": [sp["p25_us"], sp["p75_us"]],
+                                     "GB_s": round(byts / sec / 1e9, 1),
                                      "hbm_frac": round(byts / sec / 1e9 / HBM_PEAK_GBS, 4),
                                      "includes": "qgemv_q8_0_quality: fp32 activation, no quantization"}
     del gr, copies, base
@@ -398,11 +512,11 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
         qg.quantize_act_q8(xp, M, K, qx, dx, sx)
         qg.qgemm_q8_0(copies[i % R], N, K, qx, dx, M, yp)
     gr = capture(q8_prefill, R, stream)
-    timer.run(gr.replay)
-    sec = timer.run(gr.replay) / R
+    sp = spread(timer.trials(gr.replay, R))
+    sec = sp["median_us"] * 1e-6
     ops = 2.0 * M * N * K
     out["prefill_q8_0_512x8192x4096"] = {
-        "us": round(sec * 1e6, 3), "TOP_s": round(ops / sec / 1e12, 1),
+        "us": round(sec * 1e6, 3), "iqr_us": [sp["p25_us"], sp["p75_us"]], "TOP_s": round(ops / sec / 1e12, 1),
         "mfma_frac": round(ops / sec / 1e12 / MFMA_INT8_PEAK_TOPS, 4),
         "includes": "quantize_act_q8 of the 512 tokens + qgemm_q8_0 (int8 MFMA; rows equal the decode call)"}
     del gr, copies, base
@@ -678,25 +792,29 @@ def main():
     timer = Timer(stream)
     step = DecodeStep(qg, torch)
 
-    # warmup: W eager steps, then the graph of K steps replayed once untimed
+    clocks_before = gpu_clocks()
+    # warmup: W eager steps, then the graph of K steps replayed once untimed;
+    # then TRIALS timed replays of the K steps (the median is reported)
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step.step(i)
     torch.cuda.synchronize()
     g_steps = capture(step.step, args.steps, stream)
-    timer.run(g_steps.replay)
-    sec = timer.run(g_steps.replay)
-    ms_per_step = sec / args.steps * 1e3
-    value = step.step_bytes / (sec / args.steps) / 1e9
+    step_t = timer.trials(g_steps.replay, args.steps)
+    step_sp = spread(step_t)
+    ms_per_step = step_sp["median_us"] * 1e-3
+    value = step.step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # dominant kernel: the 4096 x 8192 Q8_0 GEMV, timed alone over a rotation of weights
     n_k = max(step.R, 100)
     g_k = capture(step.out_gemv, n_k, stream)
-    timer.run(g_k.replay)
-    ksec = timer.run(g_k.replay) / n_k
+    k_sp = spread(timer.trials(g_k.replay, n_k))
+    ksec = k_sp["median_us"] * 1e-6
     achieved = step.out_gemv_bytes / ksec / 1e9
     src_hash = kernel_source_hash()
     traffic = load_traffic("qgemv_q8_0_4096x8192", src_hash)
+    ceil = read_ceilings(qg, torch, stream, timer, step.W_host.nbytes)
+    floor_us = ceil["read_same_bytes"]["median_us"]
 
     result = {
         "metric": METRIC,
@@ -718,6 +836,7 @@ def main():
             "algorithmic_bytes_per_step": step.step_bytes,
             "weight_rotation_copies": step.R,
             "us_per_step": round(ms_per_step * 1e3, 3),
+            "step_spread": step_sp,
             "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         },
         "roofline": {
@@ -729,17 +848,23 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "avg_launch_us": round(ksec * 1e6, 3),
+            "launch_spread": k_sp,
             "algorithmic_bytes_per_launch": step.out_gemv_bytes,
+            "read_ceiling_gbs": ceil["read_1gib"]["GB_s"],
+            "frac_of_read_ceiling": round(achieved / ceil["read_1gib"]["GB_s"], 4),
+            "read_floor_same_bytes_us": floor_us,
+            "frac_of_read_floor": round(floor_us / (ksec * 1e6), 4),
+            "read_probe": ceil,
             "source_hash": src_hash,
         },
     }
     g_f = capture(step.step_fused, args.steps, stream)
-    timer.run(g_f.replay)
-    fsec = timer.run(g_f.replay) / args.steps
+    fsp = spread(timer.trials(g_f.replay, args.steps))
     del g_steps, g_k, g_f
-    result["config"]["fused_quantize_step_us"] = round(fsec * 1e6, 3)
+    result["config"]["fused_quantize_step_us"] = fsp["median_us"]
     if not args.no_extra:
         result["extra"] = extra_measurements(qg, torch, stream, timer)
+    result["clocks"] = {"before": clocks_before, "after": gpu_clocks()}
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(step)
     print(json.dumps(result), flush=True)

@@ -41,10 +41,13 @@
  *    and no output was touched.  QG_ERR_LAUNCH reports a failed launch.
  *  - Data errors that only the device can see (expert ids) are reported in a
  *    caller-provided device int32 status word (see moe_routed_qgemv).
- *  - The library keeps no global mutable state; calls on different streams
- *    may run concurrently.  Results are deterministic: the same inputs give
- *    bit-identical outputs, and row t of a batched call equals the M = 1 call
- *    on token t.
+ *  - The library's only process-wide state is set-up done once per device
+ *    (the device's compute-unit count, kernels' dynamic-LDS limits), kept per
+ *    device behind one lock, so calls from several host threads, on several
+ *    streams or devices, may run concurrently (calls that share an output or
+ *    a workspace must be ordered by the caller).  Results are deterministic:
+ *    the same inputs give bit-identical outputs, and row t of a batched call
+ *    equals the M = 1 call on token t.
  *
  * Weight formats (the pages name Q8_0 and Q4_K but print no byte layout; this
  * library defines its own, "Q4_K-style"):
@@ -415,6 +418,26 @@ const char *qg_status_string(int status);
  */
 int qgemv_debug_block_isums(int fmt, const void *W, int N, int K, const int8_t *qx, int M, int32_t *isum,
                             void *stream);
+
+/*
+ * qg_stream_read, qg_stream_read_groups -- diagnostic: the HBM read rate that
+ * the decode mat-vecs are measured against (the pages report mat-vec time
+ * against the memory it streams, [SOOT] "Why I did not keep a ROCm kernel
+ * patch"; this call gives the same part's own ceiling for a given byte count).
+ * Reads bytes bytes of buf once, the way the mat-vec kernels stream weights:
+ * each wave one burst of chunk_kib KiB of consecutive 16-byte non-temporal
+ * loads (chunk_kib in {1, 2, 4, 8, 16}), waves waves (1..16) per workgroup,
+ * and does no other work.  Workgroup g writes the XOR of the 32-bit words it
+ * read to wg_xor[g] (uint32, device), so the XOR of all wg_xor entries is the
+ * XOR of the buffer's words.  qg_stream_read_groups returns the number of
+ * workgroups (the length wg_xor needs), 0 for invalid arguments.
+ * Errors: QG_ERR_NULL; QG_ERR_SHAPE unless bytes is a non-zero multiple of 16,
+ * chunk_kib and waves are as above and wg_xor_len >= the group count;
+ * QG_ERR_ALIGN (buf 16-byte, wg_xor 4-byte aligned); QG_ERR_LAUNCH.
+ */
+size_t qg_stream_read_groups(size_t bytes, int chunk_kib, int waves);
+int qg_stream_read(const void *buf, size_t bytes, int chunk_kib, int waves, uint32_t *wg_xor, size_t wg_xor_len,
+                   void *stream);
 
 #ifdef __cplusplus
 }

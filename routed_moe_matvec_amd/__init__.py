@@ -20,7 +20,7 @@ __all__ = [
     "qgemm_prefill", "qg_status_string", "qgemv_debug_block_isums", "pointer_table", "WS_REGIONS",
     "qgemv_q8_0_f32", "qgemv_q4k_f32", "qgemv_paired_f32", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
     "qgemv_grouped", "qgemv_q8_0_quality", "FMT_FP8_E4M3_B128", "FMT_FP4_E2M1_MX", "qg_matrix_bytes", "qgemv_mx",
-    "moe_routed_qgemv_fmt", "qgemm_q8_0",
+    "moe_routed_qgemv_fmt", "qgemm_q8_0", "qg_stream_read_groups", "qg_stream_read",
 ]
 
 FMT_Q8_0 = 0
@@ -77,6 +77,8 @@ _c_qgemm_q8_0 = _sig("qgemm_q8_0", _i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp])
 _c_prefill = _sig("qgemm_prefill", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
 _c_prefill_ws_bytes = _sig("qgemm_prefill_workspace_bytes", _sz, [_i, _i])
 _c_prefill_ws = _sig("qgemm_prefill_ws", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp, _sz, _vp])
+_c_read_groups = _sig("qg_stream_read_groups", _sz, [_sz, _i, _i])
+_c_read = _sig("qg_stream_read", _i, [_vp, _sz, _i, _i, _vp, _sz, _vp])
 
 
 class QGError(RuntimeError):
@@ -216,3 +218,13 @@ def qgemm_prefill_workspace_bytes(M: int, K: int) -> int:
 def qgemm_prefill_ws(fmt: int, W, N: int, K: int, x_bf16, M: int, y, ws, ws_bytes: int, stream=None) -> None:
     _ok(_c_prefill_ws(fmt, _ptr(W), N, K, _ptr(x_bf16), M, _ptr(y), _ptr(ws), ws_bytes, _stream(stream, W)),
         "qgemm_prefill_ws")
+
+
+def qg_stream_read_groups(nbytes: int, chunk_kib: int, waves: int) -> int:
+    return int(_c_read_groups(nbytes, chunk_kib, waves))
+
+
+def qg_stream_read(buf, nbytes: int, chunk_kib: int, waves: int, wg_xor, wg_xor_len: int, stream=None) -> None:
+    _ok(_c_read(_ptr(buf), nbytes, chunk_kib, waves, _ptr(wg_xor), wg_xor_len, _stream(stream, buf)),
+        "qg_stream_read")
+

@@ -83,6 +83,17 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Host-side state (api.hip), all of it per device and behind one lock:
+//  - once_per_device runs init(key, arg) once per (key, current device) and
+//    remembers its success (a failure is retried on the next call);
+//  - ensure_lds_limit raises a kernel's dynamic-LDS limit that way;
+//  - device_cu_count gives the current device's compute units.
+// Each returns QG_OK or QG_ERR_LAUNCH.
+int current_device(int *dev);
+int once_per_device(const void *key, int (*init)(const void *key, int arg), int arg);
+int ensure_lds_limit(const void *kern, int bytes);
+int device_cu_count();
+
 template <class T>
 __device__ __forceinline__ T shfl_xor(T v, int mask) {
     return __shfl_xor(v, mask, kWave);

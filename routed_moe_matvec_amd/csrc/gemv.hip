@@ -68,13 +68,9 @@ static inline bool misaligned(const void *p) { return ((uintptr_t)p & 15) != 0; 
 
 template <int FMT, int NB, bool DEBUG_ISUM, bool PIPE, bool ONE, bool F32, int RC = kActRegChunks>
 static int launch_kernel(const GemvArgs &a, int grid, size_t lds, hipStream_t stream) {
-    static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32, RC>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
-            return QG_ERR_LAUNCH;
-        attr_set = true;
-    }
+    if (ensure_lds_limit(reinterpret_cast<const void *>(&qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32, RC>),
+                         kLdsBytes) != QG_OK)
+        return QG_ERR_LAUNCH;
     hipLaunchKernelGGL((qgemv_kernel<FMT, NB, DEBUG_ISUM, PIPE, ONE, F32, RC>), dim3(grid, a.G),
                        dim3(a.waves * kWave), lds, stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;

@@ -700,9 +700,6 @@ inline int tiles_per_wave(int ntiles, int resident_waves, bool single_chunk) {
     return t < 1 ? 1 : (t > 4 ? 4 : t);
 }
 
-// Compute units of the current device (queried once per process and device).
-int device_cu_count();
-
 // The matrix-core form of the Q8_0 / Q4_K mat-vec on a Q8 activation
 // (gemv_mm.hip): same arguments and results, bit for bit, as the engine above
 // for one matrix (W1 = NULL) or a pair, G groups, M tokens (sx: Q4_K only).

@@ -91,13 +91,8 @@ constexpr size_t mm_lds_bytes(int gps, int ks, int tt) {
 
 template <int FMT, int NB, int GPS, int TT>
 static int launch_mm_gps(const MmArgs &a, int nt1, hipStream_t stream) {
-    static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_mm_kernel<FMT, NB, GPS, TT>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
-            return QG_ERR_LAUNCH;
-        attr_set = true;
-    }
+    if (ensure_lds_limit(reinterpret_cast<const void *>(&qgemv_mm_kernel<FMT, NB, GPS, TT>), kLdsBytes) != QG_OK)
+        return QG_ERR_LAUNCH;
     hipLaunchKernelGGL((qgemv_mm_kernel<FMT, NB, GPS, TT>), dim3((a.nt0 + nt1) * a.ntok, a.G),
                        dim3(a.KS * TT * kWave), mm_lds_bytes<FMT>(GPS, a.KS, TT), stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;

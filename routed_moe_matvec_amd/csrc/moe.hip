@@ -809,12 +809,24 @@ static bool raise_lds_limit(Kern *k, size_t bytes) {
                                (int)bytes) == hipSuccess;
 }
 
+// Every block-scaled expert kernel of format FMT (all chunk counts, both
+// table and h forms).
+template <int FMT, int CPL>
+static bool raise_mx_cpl() {
+    return raise_lds_limit(moe_gate_up_mx_kernel<FMT, CPL, false>, kMxLdsMax) &&
+           raise_lds_limit(moe_gate_up_mx_kernel<FMT, CPL, true>, kMxLdsMax) &&
+           raise_lds_limit(moe_down_mx_kernel<FMT, CPL, false>, kMxLdsMax) &&
+           raise_lds_limit(moe_down_mx_kernel<FMT, CPL, true>, kMxLdsMax);
+}
+template <int FMT>
+static bool raise_mx_all() {
+    return raise_mx_cpl<FMT, 1>() && raise_mx_cpl<FMT, 2>() && raise_mx_cpl<FMT, 4>() && raise_mx_cpl<FMT, 8>() &&
+           raise_mx_cpl<FMT, 16>();
+}
+
 // gate/up (K = D, F rows each) and down (K = F, D rows) on the mx engine.
 template <int FMT, int CPL, bool OWN>
 static int launch_moe_gate_up_mx_own(MoeArgs a, int Ucap, hipStream_t st) {
-    static bool raised = false;
-    if (!raised) raised = raise_lds_limit(moe_gate_up_mx_kernel<FMT, CPL, OWN>, kMxLdsMax);
-    if (!raised) return QG_ERR_LAUNCH;
     const int rows_per_wg = mx_routed_waves(FMT) * mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int nwg = (a.F + rows_per_wg - 1) / rows_per_wg;
     a.mt = mx_tokens_per_chunk(a.D, QG_MAX_MOE_PAIRS);
@@ -835,9 +847,6 @@ static int launch_moe_gate_up_mx(const MoeArgs &a, int Ucap, bool own, hipStream
 
 template <int FMT, int CPL, bool GLU>
 static int launch_moe_down_mx_glu(MoeArgs a, int Ucap, hipStream_t st) {
-    static bool raised = false;
-    if (!raised) raised = raise_lds_limit(moe_down_mx_kernel<FMT, CPL, GLU>, kMxLdsMax);
-    if (!raised) return QG_ERR_LAUNCH;
     const int rows_per_wg = mx_routed_waves(FMT) * mx_rows_per_wave(kMxLoadsRouted, CPL);
     const int nwg = (a.D + rows_per_wg - 1) / rows_per_wg;
     a.mt = mx_tokens_per_chunk(a.F, QG_MAX_MOE_PAIRS);
@@ -887,14 +896,7 @@ namespace qg {
 // projection's input width, tiles = 32-row tiles per item.
 template <bool DOWN, int GPS>
 static int launch_moe_mm_gps(const MoeArgs &a, int tiles, int cap, int ks, hipStream_t st) {
-    static bool raised = false;  // idempotent: raising the dynamic-LDS limit once per kernel
     auto kern = DOWN ? moe_mm_down_kernel<GPS> : moe_mm_gate_up_kernel<GPS>;
-    if (!raised) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kMmMaxSlices * mm_wave_lds<QG_FMT_Q4K>(GPS)) != hipSuccess)
-            return QG_ERR_LAUNCH;
-        raised = true;
-    }
     hipLaunchKernelGGL(kern, dim3(tiles, cap), dim3(ks * kWave), (size_t)ks * mm_wave_lds<QG_FMT_Q4K>(GPS), st, a, ks);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
@@ -924,6 +926,28 @@ bool raise_moe_lds() {
            raise_lds_limit(moe_gate_up_kernel<true, RC, true>, kLdsBytes) &&
            raise_lds_limit(moe_down_kernel<false, RC>, kLdsBytes) && raise_lds_limit(moe_down_kernel<true, RC>, kLdsBytes);
 }
+
+template <int GPS>
+bool raise_moe_mm() {
+    return raise_lds_limit(moe_mm_gate_up_kernel<GPS>, kMmMaxSlices * mm_wave_lds<QG_FMT_Q4K>(GPS)) &&
+           raise_lds_limit(moe_mm_down_kernel<GPS>, kMmMaxSlices * mm_wave_lds<QG_FMT_Q4K>(GPS));
+}
+
+// Raise the dynamic-LDS limit of every expert kernel of one format on the
+// current device (run once per device and format by once_per_device, before
+// a call enqueues anything).
+static int moe_kernels_init(const void *, int fmt) {
+    bool ok;
+    if (fmt == QG_FMT_Q4K)
+        ok = raise_moe_lds<1>() && raise_moe_lds<2>() && raise_moe_lds<kActRegChunks>() && raise_moe_mm<1>() &&
+             raise_moe_mm<2>() && raise_moe_mm<4>() && raise_moe_mm<8>();
+    else if (fmt == QG_FMT_FP8_E4M3_B128)
+        ok = raise_mx_all<QG_FMT_FP8_E4M3_B128>();
+    else
+        ok = raise_mx_all<QG_FMT_FP4_E2M1_MX>();
+    return ok ? QG_OK : QG_ERR_LAUNCH;
+}
+static const char g_moe_init_key[4] = {0, 0, 0, 0};  // one key per format (its address)
 
 template <bool DOWN, bool ONE, int RC, bool OWN>
 void launch_moe_dot_rc(dim3 grid, size_t lds, hipStream_t st, const MoeArgs &a) {
@@ -986,6 +1010,8 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     const uintptr_t a8 = (uintptr_t)gate | (uintptr_t)up | (uintptr_t)down;
     if ((a16 & 15) || (a8 & 7) || ((uintptr_t)ids & 3) || ((uintptr_t)rw & 3) || ((uintptr_t)d_status & 3))
         return QG_ERR_ALIGN;
+    // every kernel this call may use gets its LDS limit before the first launch
+    if (once_per_device(&g_moe_init_key[fmt], moe_kernels_init, fmt) != QG_OK) return QG_ERR_LAUNCH;
     hipStream_t st = (hipStream_t)stream;
     const int P = T * topk;
     const int Ucap = P < E ? P : E;
@@ -1045,9 +1071,6 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     }
     const bool one = T == 1;  // every expert then has a single pair (a few if the token repeats an id)
     constexpr int threads = kMoeWaves * kWave;
-    static bool lds_raised = false;  // idempotent: raise the dynamic-LDS limit once
-    if (!lds_raised)
-        lds_raised = raise_moe_lds<1>() && raise_moe_lds<2>() && raise_moe_lds<kActRegChunks>();
 
     // gate/up: K = D, Q8 activation of the tokens
     a.tg = make_tile_geom<QU>(D);

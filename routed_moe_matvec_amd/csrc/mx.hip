@@ -29,13 +29,8 @@ __global__ __launch_bounds__(kMxWaves *kWave) void qgemv_mx_kernel(MxArgs a) {
 template <int FMT, int CPL>
 static int launch_mx_cpl(MxArgs &a, hipStream_t stream) {
     constexpr int rows_per_wg = kMxWaves * mx_rows_per_wave(mx_loads(FMT), CPL);
-    static bool attr_set = false;  // idempotent: raising the dynamic-LDS limit once per kernel
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_mx_kernel<FMT, CPL>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kMxLdsMax) != hipSuccess)
-            return QG_ERR_LAUNCH;
-        attr_set = true;
-    }
+    if (ensure_lds_limit(reinterpret_cast<const void *>(&qgemv_mx_kernel<FMT, CPL>), kMxLdsMax) != QG_OK)
+        return QG_ERR_LAUNCH;
     const int grid = (a.N + rows_per_wg - 1) / rows_per_wg;
     hipLaunchKernelGGL((qgemv_mx_kernel<FMT, CPL>), dim3(grid), dim3(kMxWaves * kWave),
                        (size_t)a.mt * mx_token_rec(a.K) + mx_scale_lds<FMT>(a.K, CPL, mx_loads(FMT)), stream, a);

@@ -138,13 +138,8 @@ static int launch_fx(FxArgs &a, hipStream_t stream) {
     if (a.mt < 1) a.mt = 1;
     if (a.mt > a.M) a.mt = a.M;
     const size_t lds = tiles_lds + (size_t)a.mt * per_token;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&qgemv_fx_kernel<NB>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
-            return QG_ERR_LAUNCH;
-        attr_set = true;
-    }
+    if (ensure_lds_limit(reinterpret_cast<const void *>(&qgemv_fx_kernel<NB>), kLdsBytes) != QG_OK)
+        return QG_ERR_LAUNCH;
     const int grid = (a.ntiles + a.waves - 1) / a.waves;
     hipLaunchKernelGGL(qgemv_fx_kernel<NB>, dim3(grid), dim3(a.waves * kWave), lds, stream, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
