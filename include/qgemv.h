@@ -363,6 +363,30 @@ int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, const int32
                          const void *const *up, const void *const *down, float *y, void *ws, size_t ws_bytes,
                          int32_t *d_status, void *stream);
 
+/*
+ * moe_routed_qgemv_noalloc -- moe_routed_qgemv_fmt for callers that cannot
+ * allocate device memory (work recorded under HIP graph capture, serving loops
+ * that must not allocate, hosts that forbid it): the same call, arguments and
+ * results, with no workspace argument.  Its workspace is a fixed array of
+ * QG_MOE_SCRATCH_BYTES in device memory that the library holds on every
+ * device it runs on, from its first call there until the process ends; the
+ * call itself allocates nothing.  Calls whose workspace
+ * (moe_routed_workspace_bytes) exceeds QG_MOE_SCRATCH_BYTES are rejected with
+ * QG_ERR_WORKSPACE before anything is launched (with 6 experts per token,
+ * D = 4096 and F = 2048: up to 32 tokens).  Every call on one device shares
+ * that device's array: calls that may overlap on one device (several streams
+ * or host threads) race and must be ordered by the caller.  Nothing in the
+ * array needs to start at zero; its contents after a call are those of the
+ * workspace of moe_routed_qgemv (moe_routed_workspace_layout) until the next
+ * call.
+ * Errors: as moe_routed_qgemv_fmt (QG_ERR_WORKSPACE as above).
+ */
+#define QG_MOE_SCRATCH_BYTES (8u << 20)
+int moe_routed_qgemv_noalloc(int fmt, const int8_t *qx, const float *dx, const int32_t *sx, int T, int D, int F,
+                             int E, int topk, const int32_t *ids, const float *rw, const void *const *gate,
+                             const void *const *up, const void *const *down, float *y, int32_t *d_status,
+                             void *stream);
+
 /* ---- prefill ----------------------------------------------------------- */
 /*
  * qgemm_prefill -- [PR621] the dequantize-then-GEMM path for prefill batches

@@ -20,7 +20,8 @@ __all__ = [
     "qgemm_prefill", "qg_status_string", "qgemv_debug_block_isums", "pointer_table", "WS_REGIONS",
     "qgemv_q8_0_f32", "qgemv_q4k_f32", "qgemv_paired_f32", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
     "qgemv_grouped", "qgemv_q8_0_quality", "FMT_FP8_E4M3_B128", "FMT_FP4_E2M1_MX", "qg_matrix_bytes", "qgemv_mx",
-    "moe_routed_qgemv_fmt", "qgemm_q8_0", "qg_stream_read_groups", "qg_stream_read",
+    "moe_routed_qgemv_fmt", "qgemm_q8_0", "qg_stream_read_groups", "qg_stream_read", "moe_routed_qgemv_noalloc",
+    "MOE_SCRATCH_BYTES",
 ]
 
 FMT_Q8_0 = 0
@@ -31,6 +32,7 @@ DEV_OK, DEV_BAD_EXPERT, DEV_NULL_EXPERT = 0, 1, 2
 MAX_K, MAX_M, MAX_MOE_PAIRS, MAX_EXPERTS = 16384, 32, 8192, 4096
 WS_REGIONS = ["NUNIQ", "UNIQ", "SLOT", "PAIR_OFF", "PAIRS", "G", "V", "H", "HQ", "HD", "HS", "O", "HOT"]
 MOE_MM_PAIRS = 9  # QG_MOE_MM_PAIRS
+MOE_SCRATCH_BYTES = 8 << 20  # QG_MOE_SCRATCH_BYTES
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqgemv.so")
@@ -79,6 +81,8 @@ _c_prefill_ws_bytes = _sig("qgemm_prefill_workspace_bytes", _sz, [_i, _i])
 _c_prefill_ws = _sig("qgemm_prefill_ws", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp, _sz, _vp])
 _c_read_groups = _sig("qg_stream_read_groups", _sz, [_sz, _i, _i])
 _c_read = _sig("qg_stream_read", _i, [_vp, _sz, _i, _i, _vp, _sz, _vp])
+_c_moe_noalloc = _sig("moe_routed_qgemv_noalloc", _i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                                      _vp, _vp, _vp, _vp])
 
 
 class QGError(RuntimeError):
@@ -228,3 +232,8 @@ def qg_stream_read(buf, nbytes: int, chunk_kib: int, waves: int, wg_xor, wg_xor_
     _ok(_c_read(_ptr(buf), nbytes, chunk_kib, waves, _ptr(wg_xor), wg_xor_len, _stream(stream, buf)),
         "qg_stream_read")
 
+
+def moe_routed_qgemv_noalloc(fmt: int, qx, dx, sx, T: int, D: int, F: int, E: int, topk: int, ids, rw, gate, up,
+                             down, y, d_status, stream=None) -> None:
+    _ok(_c_moe_noalloc(fmt, _ptr(qx), _ptr(dx), _ptr(sx), T, D, F, E, topk, _ptr(ids), _ptr(rw), _ptr(gate),
+                       _ptr(up), _ptr(down), _ptr(y), _ptr(d_status), _stream(stream, qx)), "moe_routed_qgemv_noalloc")
