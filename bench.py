@@ -290,19 +290,20 @@ def read_ceilings(qg, torch, stream, timer, same_bytes: int) -> dict:
     buf = torch.empty(big, dtype=torch.uint8, device="cuda")
     buf.fill_(0x5A)
     out = {}
-    g_big = qg.qg_stream_read_groups(big, 4, 4)
-    sink = torch.empty(max(g_big, 1), dtype=torch.int32, device="cuda")
-    with torch.cuda.stream(stream):
-        t = timer.trials(lambda: qg.qg_stream_read(buf, big, 4, 4, sink, g_big, stream=stream), 1)
-    sp = spread(t)
-    out["read_1gib"] = dict(sp, GB_s=round(big / (sp["median_us"] * 1e-6) / 1e9, 1), chunk_kib=4, waves=4)
+    # (no output array: the read alone; the tests check what it reads)
+    best_big = None
+    for kib, waves in ((4, 4), (8, 4)):
+        with torch.cuda.stream(stream):
+            sp = spread(timer.trials(lambda: qg.qg_stream_read(buf, big, kib, waves, None, 0, stream=stream), 1))
+        if best_big is None or sp["median_us"] < best_big["median_us"]:
+            best_big = dict(sp, chunk_kib=kib, waves=waves)
+    best_big["GB_s"] = round(big / (best_big["median_us"] * 1e-6) / 1e9, 1)
+    out["read_1gib"] = best_big
     R = big // same_bytes
     best = None
     for kib, waves in ((2, 4), (4, 4), (8, 4), (4, 8), (8, 8)):
-        groups = qg.qg_stream_read_groups(same_bytes, kib, waves)
-        sk = torch.empty(groups, dtype=torch.int32, device="cuda")
         n = max(R, 100)
-        gr = capture(lambda i: qg.qg_stream_read(buf[(i % R) * same_bytes:], same_bytes, kib, waves, sk, groups,
+        gr = capture(lambda i: qg.qg_stream_read(buf[(i % R) * same_bytes:], same_bytes, kib, waves, None, 0,
                                                  stream=stream), n, stream)
         sp = spread(timer.trials(gr.replay, n))
         if best is None or sp["median_us"] < best["median_us"]:

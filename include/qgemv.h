@@ -38,7 +38,9 @@
  *  - Outputs are overwritten, never accumulated into.
  *  - Return value: QG_OK (0) when the work was enqueued; a negative QG_ERR_*
  *    code when the host-side checks fail, in which case NOTHING was launched
- *    and no output was touched.  QG_ERR_LAUNCH reports a failed launch.
+ *    and no output was touched.  QG_ERR_LAUNCH reports a failed launch of
+ *    the call's own kernels (an error that an earlier, unrelated HIP call
+ *    left for the calling thread is cleared before the first launch).
  *  - Data errors that only the device can see (expert ids) are reported in a
  *    caller-provided device int32 status word (see moe_routed_qgemv).
  *  - The library's only process-wide state is set-up done once per device
@@ -444,24 +446,27 @@ int qgemv_debug_block_isums(int fmt, const void *W, int N, int K, const int8_t *
                             void *stream);
 
 /*
- * qg_stream_read, qg_stream_read_groups -- diagnostic: the HBM read rate that
+ * qg_stream_read, qg_stream_read_bursts -- diagnostic: the HBM read rate that
  * the decode mat-vecs are measured against (the pages report mat-vec time
  * against the memory it streams, [SOOT] "Why I did not keep a ROCm kernel
  * patch"; this call gives the same part's own ceiling for a given byte count).
  * Reads bytes bytes of buf once, the way the mat-vec kernels stream weights:
- * each wave one burst of chunk_kib KiB of consecutive 16-byte non-temporal
- * loads (chunk_kib in {1, 2, 4, 8, 16}), waves waves (1..16) per workgroup,
- * and does no other work.  Workgroup g writes the XOR of the 32-bit words it
- * read to wg_xor[g] (uint32, device), so the XOR of all wg_xor entries is the
- * XOR of the buffer's words.  qg_stream_read_groups returns the number of
- * workgroups (the length wg_xor needs), 0 for invalid arguments.
- * Errors: QG_ERR_NULL; QG_ERR_SHAPE unless bytes is a non-zero multiple of 16,
- * chunk_kib and waves are as above and wg_xor_len >= the group count;
- * QG_ERR_ALIGN (buf 16-byte, wg_xor 4-byte aligned); QG_ERR_LAUNCH.
+ * the buffer is cut into bursts of chunk_kib KiB (chunk_kib in {1, 2, 4, 8,
+ * 16}; the last one may be short), each read by one wave as one run of
+ * 16-byte non-temporal loads, 1 KiB per instruction, waves waves (1..16) per
+ * workgroup, and no other work.  Burst b writes the XOR of the 32-bit words it
+ * read to burst_xor[b] (uint32, device), so the XOR of all entries is the XOR
+ * of the buffer's words; with burst_xor NULL nothing is written (the read
+ * alone, for timing).  qg_stream_read_bursts returns the number of bursts
+ * (the length burst_xor needs), 0 for invalid arguments.
+ * Errors: QG_ERR_NULL (buf); QG_ERR_SHAPE unless bytes is a non-zero multiple
+ * of 16, chunk_kib and waves are as above and, when burst_xor is given,
+ * burst_xor_len >= the burst count;
+ * QG_ERR_ALIGN (buf 16-byte, burst_xor 4-byte aligned); QG_ERR_LAUNCH.
  */
-size_t qg_stream_read_groups(size_t bytes, int chunk_kib, int waves);
-int qg_stream_read(const void *buf, size_t bytes, int chunk_kib, int waves, uint32_t *wg_xor, size_t wg_xor_len,
-                   void *stream);
+size_t qg_stream_read_bursts(size_t bytes, int chunk_kib);
+int qg_stream_read(const void *buf, size_t bytes, int chunk_kib, int waves, uint32_t *burst_xor,
+                   size_t burst_xor_len, void *stream);
 
 #ifdef __cplusplus
 }

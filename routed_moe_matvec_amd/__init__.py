@@ -20,7 +20,7 @@ __all__ = [
     "qgemm_prefill", "qg_status_string", "qgemv_debug_block_isums", "pointer_table", "WS_REGIONS",
     "qgemv_q8_0_f32", "qgemv_q4k_f32", "qgemv_paired_f32", "qgemm_prefill_workspace_bytes", "qgemm_prefill_ws",
     "qgemv_grouped", "qgemv_q8_0_quality", "FMT_FP8_E4M3_B128", "FMT_FP4_E2M1_MX", "qg_matrix_bytes", "qgemv_mx",
-    "moe_routed_qgemv_fmt", "qgemm_q8_0", "qg_stream_read_groups", "qg_stream_read", "moe_routed_qgemv_noalloc",
+    "moe_routed_qgemv_fmt", "qgemm_q8_0", "qg_stream_read_bursts", "qg_stream_read", "moe_routed_qgemv_noalloc",
     "MOE_SCRATCH_BYTES",
 ]
 
@@ -44,6 +44,14 @@ def library_path() -> str:
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError("libqgemv.so is not built (run __graft_entry__.build()); there is no fallback path")
+
+# torch ships its own HIP runtime under the same soname (libamdhip64.so.7).  It is
+# loaded first, so that the library binds to it: with the system runtime loaded
+# first, torch and the library would not share streams.
+try:
+    import torch  # noqa: F401
+except ImportError:  # the library alone, on the system HIP runtime
+    pass
 
 _lib = ctypes.CDLL(_LIB_PATH)
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -79,7 +87,7 @@ _c_qgemm_q8_0 = _sig("qgemm_q8_0", _i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp])
 _c_prefill = _sig("qgemm_prefill", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp])
 _c_prefill_ws_bytes = _sig("qgemm_prefill_workspace_bytes", _sz, [_i, _i])
 _c_prefill_ws = _sig("qgemm_prefill_ws", _i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp, _sz, _vp])
-_c_read_groups = _sig("qg_stream_read_groups", _sz, [_sz, _i, _i])
+_c_read_bursts = _sig("qg_stream_read_bursts", _sz, [_sz, _i])
 _c_read = _sig("qg_stream_read", _i, [_vp, _sz, _i, _i, _vp, _sz, _vp])
 _c_moe_noalloc = _sig("moe_routed_qgemv_noalloc", _i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                                       _vp, _vp, _vp, _vp])
@@ -224,12 +232,12 @@ def qgemm_prefill_ws(fmt: int, W, N: int, K: int, x_bf16, M: int, y, ws, ws_byte
         "qgemm_prefill_ws")
 
 
-def qg_stream_read_groups(nbytes: int, chunk_kib: int, waves: int) -> int:
-    return int(_c_read_groups(nbytes, chunk_kib, waves))
+def qg_stream_read_bursts(nbytes: int, chunk_kib: int) -> int:
+    return int(_c_read_bursts(nbytes, chunk_kib))
 
 
-def qg_stream_read(buf, nbytes: int, chunk_kib: int, waves: int, wg_xor, wg_xor_len: int, stream=None) -> None:
-    _ok(_c_read(_ptr(buf), nbytes, chunk_kib, waves, _ptr(wg_xor), wg_xor_len, _stream(stream, buf)),
+def qg_stream_read(buf, nbytes: int, chunk_kib: int, waves: int, burst_xor, burst_xor_len: int, stream=None) -> None:
+    _ok(_c_read(_ptr(buf), nbytes, chunk_kib, waves, _ptr(burst_xor), burst_xor_len, _stream(stream, buf)),
         "qg_stream_read")
 
 

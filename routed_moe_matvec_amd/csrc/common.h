@@ -90,6 +90,9 @@ __device__ __forceinline__ void lds_barrier() {
 //  - device_cu_count gives the current device's compute units.
 // Each returns QG_OK or QG_ERR_LAUNCH.
 int current_device(int *dev);
+// Clears an error that an earlier, unrelated HIP call left for this thread, so
+// that the check after a launch (hipGetLastError) reports that launch only.
+inline void clear_stale_error() { (void)hipGetLastError(); }
 int once_per_device(const void *key, int (*init)(const void *key, int arg), int arg);
 int ensure_lds_limit(const void *kern, int bytes);
 int device_cu_count();

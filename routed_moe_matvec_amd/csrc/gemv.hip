@@ -163,6 +163,7 @@ static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2
     a.M = M;
     a.isum = isum;
     a.G = G;
+    clear_stale_error();
     // larger batches go to the matrix cores (same results bit for bit)
     if (!f32 && !isum && M >= (fmt == QG_FMT_Q8_0 ? kMmMinTokens : kMmMinTokensQ4K))
         return gemv_mm(fmt, a.W0, N1, y1, a.W1, N2, y2, K, act.qx, act.dx, act.sx, M, G, stream);

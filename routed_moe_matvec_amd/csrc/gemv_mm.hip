@@ -133,6 +133,7 @@ static int launch_mm(MmArgs &a, hipStream_t stream) {
 
 int gemv_mm(int fmt, const uint8_t *W0, int N0, float *y0, const uint8_t *W1, int N1, float *y1, int K,
             const int8_t *qx, const float *dx, const int32_t *sx, int M, int G, hipStream_t stream) {
+    clear_stale_error();
     MmArgs a{};
     a.W0 = W0;
     a.N0 = N0;

@@ -1010,6 +1010,7 @@ extern "C" int moe_routed_qgemv_fmt(int fmt, const int8_t *qx, const float *dx, 
     const uintptr_t a8 = (uintptr_t)gate | (uintptr_t)up | (uintptr_t)down;
     if ((a16 & 15) || (a8 & 7) || ((uintptr_t)ids & 3) || ((uintptr_t)rw & 3) || ((uintptr_t)d_status & 3))
         return QG_ERR_ALIGN;
+    clear_stale_error();
     // every kernel this call may use gets its LDS limit before the first launch
     if (once_per_device(&g_moe_init_key[fmt], moe_kernels_init, fmt) != QG_OK) return QG_ERR_LAUNCH;
     hipStream_t st = (hipStream_t)stream;

@@ -79,6 +79,7 @@ extern "C" int qgemv_mx(int fmt, const void *W, int N, int K, const int8_t *qx, 
     a.qx = qx;
     a.dx = dx;
     a.y = y;
+    qg::clear_stale_error();
     if (fmt == QG_FMT_FP8_E4M3_B128) return qg::launch_mx<QG_FMT_FP8_E4M3_B128>(a, (hipStream_t)stream);
     return qg::launch_mx<QG_FMT_FP4_E2M1_MX>(a, (hipStream_t)stream);
 }

@@ -804,6 +804,7 @@ extern "C" int qgemm_prefill(int fmt, const void *W, int N, int K, const uint16_
                              void *stream) {
     const int rc = qg::prefill_check(fmt, W, N, K, x_bf16, M, y);
     if (rc) return rc;
+    qg::clear_stale_error();
     dim3 grid((N + qg::kPfBN - 1) / qg::kPfBN, (M + qg::kPfBM - 1) / qg::kPfBM);
     hipLaunchKernelGGL(qg::qgemm_prefill_q4k_kernel, grid, dim3(256), 0, (hipStream_t)stream,
                        reinterpret_cast<const uint8_t *>(W), N, K, x_bf16, M, y);
@@ -826,6 +827,7 @@ extern "C" int qgemm_prefill_ws(int fmt, const void *W, int N, int K, const uint
     uint8_t *b = reinterpret_cast<uint8_t *>(ws);
     _Float16 *x16 = reinterpret_cast<_Float16 *>(b);
     int32_t *ex = reinterpret_cast<int32_t *>(b + lay.off_e);
+    qg::clear_stale_error();
     hipLaunchKernelGGL(qg::prefill_prepass_kernel, dim3(M), dim3(qg::kPfPreThreads), 0, (hipStream_t)stream, x_bf16,
                        K, x16, ex);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;

@@ -159,6 +159,7 @@ extern "C" int qgemv_q8_0_quality(const void *W, int N, int K, const float *x, i
     a.N = N;
     a.K = K;
     a.M = M;
+    qg::clear_stale_error();
     if (K <= 8192) return qg::launch_fx<4>(a, (hipStream_t)stream);
     return qg::launch_fx<8>(a, (hipStream_t)stream);
 }

@@ -46,6 +46,7 @@ extern "C" int quantize_act_q8(const float *x, int M, int K, int8_t *qx, float *
     if (nblocks * 8 > 0x7fffffffLL) return QG_ERR_SHAPE;
     const int threads = 256;
     const int grid = (int)((nblocks * 8 + threads - 1) / threads);
+    qg::clear_stale_error();
     hipLaunchKernelGGL(qg::quantize_act_q8_kernel, dim3(grid), dim3(threads), 0, (hipStream_t)stream, x,
                        (int)nblocks, qx, dx, sx);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;

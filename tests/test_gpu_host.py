@@ -21,7 +21,7 @@ def test_stream_read_xor(nbytes, kib, waves):
     g = np.random.default_rng(nbytes)
     words = g.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
     buf = dev(words.view(np.int32))
-    groups = qg.qg_stream_read_groups(nbytes, kib, waves)
+    groups = qg.qg_stream_read_bursts(nbytes, kib)
     out = empty((groups,), __import__("torch").int32)
     qg.qg_stream_read(buf, nbytes, kib, waves, out, groups)
     got = np.bitwise_xor.reduce(host(out).view(np.uint32))

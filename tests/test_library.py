@@ -161,20 +161,21 @@ def test_workspace_regions_match_header():
 
 
 def test_stream_read_validation_without_gpu(lib):
-    """The streaming-read diagnostic's group count and argument checks."""
+    """The streaming-read diagnostic's burst count and argument checks."""
     import routed_moe_matvec_amd as qg
-    assert qg.qg_stream_read_groups(1 << 30, 4, 4) == (1 << 30) // (4 * 4096)
-    assert qg.qg_stream_read_groups(35651584, 8, 8) == -(-35651584 // (8 * 8192))
-    assert qg.qg_stream_read_groups(16, 16, 16) == 1
-    for args in [(0, 4, 4), (1000, 4, 4), (4096, 3, 4), (4096, 32, 4), (4096, 4, 0), (4096, 4, 17)]:
-        assert qg.qg_stream_read_groups(*args) == 0, args
+    assert qg.qg_stream_read_bursts(1 << 30, 4) == (1 << 30) // 4096
+    assert qg.qg_stream_read_bursts(35651584, 8) == -(-35651584 // 8192)
+    assert qg.qg_stream_read_bursts(16, 16) == 1
+    for args in [(0, 4), (1000, 4), (4096, 3), (4096, 32)]:
+        assert qg.qg_stream_read_bursts(*args) == 0, args
     vp = ctypes.c_void_p
     fake = vp(1 << 40)
     f = lib.qg_stream_read
     f.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
     assert f(None, 4096, 4, 4, fake, 16, None) == -1
-    assert f(fake, 4096, 4, 4, None, 16, None) == -1
-    assert f(fake, 4096 * 64, 4, 4, fake, 3, None) == -2  # needs 4 groups
+    assert f(fake, 4096 * 4, 1, 4, fake, 3, None) == -2  # needs 4 bursts
     assert f(fake, 4100, 4, 4, fake, 16, None) == -2
+    assert f(fake, 4096, 4, 0, fake, 16, None) == -2
+    assert f(fake, 4096, 4, 17, fake, 16, None) == -2
     assert f(vp((1 << 40) + 8), 4096, 4, 4, fake, 16, None) == -3
     assert f(fake, 4096, 4, 4, vp((1 << 40) + 2), 16, None) == -3
