@@ -598,6 +598,24 @@ def run_probe(name: str, steps: int, warmup: int, qg, torch) -> None:
 
         def fn(i):
             qg.qgemv_q8_0(copies[i % R], N, K, qx, dx, M, y)
+    elif name == "q4k":
+        # the one-token Q4_K projection 4096 -> 8192
+        w = synth.WORKLOADS["q4k_8192x4096"]
+        g = synth.rng(w["seed"])
+        N, K = w["N"], w["K"]
+        W_host = synth.q4k_weight(g, N, K)
+        R = rotation_count(W_host.nbytes)
+        base = torch.from_numpy(W_host).to("cuda")
+        copies = [base] + [base.clone() for _ in range(R - 1)]
+        x = torch.from_numpy(synth.activations(g, 1, K)).to("cuda")
+        qx = torch.empty(1, K, dtype=torch.int8, device="cuda")
+        dx = torch.empty(1, K // 32, dtype=torch.float32, device="cuda")
+        sx = torch.empty(1, K // 32, dtype=torch.int32, device="cuda")
+        qg.quantize_act_q8(x, 1, K, qx, dx, sx)
+        y = torch.empty(1, N, dtype=torch.float32, device="cuda")
+
+        def fn(i):
+            qg.qgemv_q4k(copies[i % R], N, K, qx, dx, sx, 1, y)
     elif name in ("fp8_16384x4096", "fp4_16384x4096"):
         w = synth.WORKLOADS[name]
         g = synth.rng(w["seed"])
@@ -756,6 +774,45 @@ def summarize_pmc(gf: str, gw: str, cf: str, cw: str) -> str:
         f.write("\n")
     return json.dumps(ent, indent=1)
 
+SQ_PASSES = (
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_WAIT_INST_LDS SQ_INSTS_SALU",
+    "SQ_LDS_BANK_CONFLICT SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_ANY "
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES",
+)
+
+
+def summarize_sq(d1: str, d2: str, kernel: str, probe: str, steps: int) -> str:
+    """SQ counter summary of one kernel from two rocprofv3 --pmc passes (SQ_PASSES) of
+    `bench.py --probe PROBE`: mean per dispatch of the dispatches whose kernel name starts
+    with `kernel`, and the ratios used to read them."""
+    vals = {}
+    for d in (d1, d2):
+        for (name, counter), v in pmc_values(d).items():
+            if name.startswith(kernel):
+                vals.setdefault(counter, []).append(v)
+    v = {c: sum(x) / len(x) for c, x in vals.items()}
+    lines = ["# rocprofv3 SQ counters of %s (probe %s)" % (kernel, probe)]
+    for i, counters in enumerate(SQ_PASSES):
+        lines.append("# pass %d: rocprofv3 --output-format csv --pmc %s -d %s -o run -- python3 -u bench.py "
+                     "--probe %s --steps %d --warmup 2" % (i + 1, counters, (d1, d2)[i], probe, steps))
+    lines.append("# summary: python3 bench.py --summarize-sq %s %s '%s' %s %d" % (d1, d2, kernel, probe, steps))
+    lines.append("%-28s %16s" % ("counter", "per dispatch"))
+    for c in sorted(v):
+        lines.append("%-28s %16.1f" % (c, v[c]))
+    w = v.get("SQ_WAVES", 0.0)
+    if w:
+        lines.append("# per wave: VALU %.0f, MFMA %.0f, LDS %.0f, SALU %.0f instructions" % (
+            v.get("SQ_INSTS_VALU", 0) / w, v.get("SQ_INSTS_MFMA", 0) / w, v.get("SQ_INSTS_LDS", 0) / w,
+            v.get("SQ_INSTS_SALU", 0) / w))
+    if v.get("SQ_WAVE_CYCLES") and v.get("SQ_BUSY_CU_CYCLES"):
+        lines.append("# SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES = %.2f (share of wave time waiting on a dependency); "
+                     "SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES = %.2f; SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES "
+                     "= %.2f" % (v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"],
+                                 v["SQ_ACTIVE_INST_VALU"] / v["SQ_BUSY_CU_CYCLES"],
+                                 v["SQ_VALU_MFMA_BUSY_CYCLES"] / v["SQ_BUSY_CU_CYCLES"]))
+    return "\n".join(lines)
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -768,6 +825,7 @@ def main():
     ap.add_argument("--summarize-rocprof", default=None)
     ap.add_argument("--probe", default=None)
     ap.add_argument("--summarize-pmc", nargs=4, default=None)
+    ap.add_argument("--summarize-sq", nargs=5, default=None, metavar=("PASS1", "PASS2", "KERNEL", "PROBE", "STEPS"))
     args = ap.parse_args()
 
     if args.summarize_rocprof:
@@ -775,6 +833,10 @@ def main():
         return 0
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc))
+        return 0
+    if args.summarize_sq:
+        d1, d2, kern, probe, steps = args.summarize_sq
+        print(summarize_sq(d1, d2, kern, probe, int(steps)))
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the decode mat-vec would "

@@ -10,8 +10,8 @@
  *          output projections; the compact selected-expert table staged before
  *          the pointer-backed routed-MoE launch), Correctness (the missing
  *          compact table is a hard error) and the review comments (per-stage
- *          timing of the Q8_0 entry points; "selected expert id -1 outside
- *          0..256" as a failed decode).
+ *          timing of the Q8_0 entry points; a decode log in which an expert id
+ *          of -1, out of the range 0..256, fails the decode).
  *  [PR621] "Support AProjQ4 GGUFs: Q4_K dense attention projections ...",
  *          antirez/ds4 pull request 621 -- Q4_K dense attention projections
  *          and the dequantize + GEMM prefill path.
@@ -306,7 +306,7 @@ int moe_routed_workspace_layout(int T, int topk, int E, int D, int F, size_t *of
 /*
  * moe_routed_qgemv -- [PR623] routed-MoE decode driven by a compact
  * selected-expert table built on the device before the pointer-backed expert
- * launches (Summary; "missing compact selected experts" was the failure it
+ * launches (Summary; the missing compact table of selected experts was the failure it
  * fixes); [ATOM] top-6 sigmoid-normalized routing.
  *
  * For T tokens with Q8 activations qx/dx/sx ([T, D]) and selected experts
@@ -418,10 +418,14 @@ size_t qgemm_prefill_workspace_bytes(int M, int K);
 /*
  * qgemm_prefill_ws -- [PR621] the same product as qgemm_prefill, with the
  * bf16 -> fp16 conversion of x done once by a separate pass into the caller's
- * workspace, each token scaled by a power of two so that any finite bf16
- * activation converts exactly (qgemm_prefill needs |x| <= 65504), and a
- * faster GEMM that reads it.  Results agree with qgemm_prefill to rounding
- * (the same error bound).  ws is device memory owned by the caller (at least
+ * workspace, and a faster GEMM that reads it.  Each token is scaled by a
+ * power of two that puts its largest |x| in [2^15, 2^16), so any finite bf16
+ * row can be given (qgemm_prefill needs |x| <= 65504).  The conversion is
+ * exact for every element within about 2^32 of the token's largest |x|;
+ * smaller elements become fp16 subnormals and keep fewer bits (below about
+ * 2^-40 of it they become 0), an error far inside the bound, since they
+ * weigh that much less in sum |w * x|.  Results agree with qgemm_prefill to
+ * rounding (the same error bound).  ws is device memory owned by the caller (at least
  * qgemm_prefill_workspace_bytes(M, K) bytes, 16-byte aligned); its contents on
  * entry are ignored and on return are unspecified.  Calls that share a
  * workspace must be ordered on one stream.

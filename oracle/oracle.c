@@ -409,8 +409,8 @@ int oracle_block_isums(int fmt, const uint8_t *W, int64_t N, int64_t K, const in
  *   pair_off[0..U]  CSR offsets: pairs of uniq[u] are pairs[pair_off[u] .. pair_off[u+1])
  *   pairs[]         pair indices grouped by expert, ascending p within a group
  *   *status         0, or ORACLE_BAD_EXPERT if any id is outside [0, E)
- * An id outside [0, E) is a data error (the pages report "selected expert id
- * -1 outside 0..256" as a failed decode); such a pair belongs to no expert.
+ * An id outside [0, E) is a data error (the pages show a decode that fails on
+ * an expert id of -1, out of the range 0..256); such a pair belongs to no expert.
  */
 int oracle_moe_table(const int32_t *ids, int64_t T, int64_t topk, int64_t E, int32_t *uniq, int32_t *n_uniq,
                      int32_t *slot, int32_t *pair_off, int32_t *pairs, int32_t *status) {

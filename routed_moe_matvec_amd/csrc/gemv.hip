@@ -88,6 +88,8 @@ static int launch_gemv(GemvArgs &a, hipStream_t stream) {
     // every CU, else fewer so that the grid still spreads over the CUs
     a.waves = kGemvMaxWaves;
     while (a.waves > 1 && tiles < a.waves * cus) a.waves >>= 1;
+    // one-token Q4_K: 4-wave workgroups (8192 x 4096: 5.92 -> 5.57 us)
+    if (FMT == QG_FMT_Q4K && a.M == 1 && a.waves > 4) a.waves = 4;
     const int threads = a.waves * kWave;
     a.mt = tokens_per_chunk<U>(a.K, a.M, threads, F32);
     const size_t lds = gemv_lds_bytes<U>(a.waves, a.K, a.mt);

@@ -74,6 +74,25 @@ def test_prefill_ws_activation_range(qg, orc, scale):
     assert np.all(y[7] == 0.0)
 
 
+def test_prefill_ws_rows_spanning_wide_magnitudes(qg, orc):
+    """Rows whose elements span 2^60: those more than ~2^32 below the row's largest become
+    fp16 subnormals (or 0) after the per-token power of two; the product stays within the
+    bound, which they barely touch."""
+    progress("prefill ws rows spanning 2^60")
+    g = np.random.default_rng(91)
+    N, K, M = 96, 1024, 20
+    W = synth.q4k_weight(g, N, K)
+    xb = synth.bf16_activations(g, M, K)
+    # per element a power of two between 2^-30 and 2^30 (bf16 keeps it exactly)
+    exps = g.integers(-30, 31, size=(M, K)).astype(np.float64)
+    import torch
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).double().numpy() * np.exp2(exps)
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    y = run_prefill(qg, W, N, K, xb, M, "ws")
+    ref, bound = orc.prefill(orc.FMT_Q4K, W, N, K, xb, nthreads=oracle_threads())
+    assert_within_bound(y, ref, bound, what="prefill ws wide rows")
+
+
 def set_scales(W, N, K, d, dmin):
     """Overwrite the fp16 d and dmin of every superblock of a Q4_K matrix."""
     sb = W.reshape(N, K // 256, 144)

@@ -510,7 +510,7 @@ def test_golden_q4k_expert_bytes(orc):
 
 
 def test_golden_expert_id_range(orc):
-    """The pages report id -1 'outside 0..256' as a failed decode with 256 experts."""
+    """The pages show a decode with 256 experts failing on an expert id of -1, out of the range 0..256."""
     with open(os.path.join(GOLDEN, "expert_id_range.json")) as f:
         fact = json.load(f)
     E = fact["experts"]
