@@ -488,7 +488,8 @@ def extra_measurements(qg, torch, stream, timer) -> dict:
     gemv_rate(0, np.concatenate([synth.q8_0_weight(gw, w["N"], w["K"]) for _ in range(w["G"])], axis=0), w["N"],
               w["K"], [1], "q8_0_grouped_8x1024x4096", G=w["G"])
     w = synth.WORKLOADS["q4k_8192x4096"]
-    gemv_rate(1, synth.q4k_weight(synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], [1], "q4k_8192x4096")
+    gemv_rate(1, synth.q4k_weight(synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], [1, 8, 16, 32],
+              "q4k_8192x4096")
     w = synth.WORKLOADS["q8_0_16384x4096"]
     gemv_rate(0, synth.q8_0_weight(synth.rng(w["seed"]), w["N"], w["K"]), w["N"], w["K"], list(w["Ms"]),
               "q8_0_16384x4096")
@@ -553,6 +554,23 @@ def summarize_rocprof(path: str) -> str:
         for (name, grid), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
             lines.append("%-56s %9s %6d %10.3f %10.3f %10.3f %10.3f" % (
                 name[:56], grid, len(ds), sum(ds) / len(ds), statistics.median(ds), min(ds), max(ds)))
+        # The busiest (kernel, grid) split by the kernel dispatched just before it:
+        # one kernel replayed back to back and the same kernel inside a longer
+        # sequence of launches run at different speeds.
+        if groups:
+            top = max(groups, key=lambda k: sum(groups[k]))
+            rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+            after = {}
+            for prev, r in zip([None] + rows[:-1], rows):
+                if (r.get("Kernel_Name", "?"), r.get("Grid_Size_X", r.get("Grid_Size", "?"))) != top:
+                    continue
+                pk = "-" if prev is None else "%s grid_x %s" % (prev.get("Kernel_Name", "?")[:48],
+                                                                 prev.get("Grid_Size_X", prev.get("Grid_Size", "?")))
+                after.setdefault(pk, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            lines.append("# %s grid_x %s by the dispatch before it" % (top[0][:56], top[1]))
+            for pk, ds in sorted(after.items(), key=lambda kv: -len(kv[1])):
+                lines.append("  after %-66s calls=%d avg_us=%.3f median_us=%.3f" % (
+                    pk, len(ds), sum(ds) / len(ds), statistics.median(ds)))
     for s in sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)):
         with open(s) as f:
             rows = list(csv.DictReader(f))
@@ -580,11 +598,13 @@ def run_probe(name: str, steps: int, warmup: int, qg, torch) -> None:
         step = DecodeStep(qg, torch)
         step.step(0)  # quantized activations for the projection
         fn = step.out_gemv
-    elif name == "gemv_batch":
-        # the batched Q8_0 sweep's largest batch: 16384 x 4096, 32 tokens
+    elif name.startswith("gemv_batch"):
+        # the batched Q8_0 sweep: 16384 x 4096, 32 tokens (gemv_batch) or the
+        # number of tokens after the name (gemv_batch8: 8 tokens)
         w = synth.WORKLOADS["q8_0_16384x4096"]
         g = synth.rng(w["seed"])
-        N, K, M = w["N"], w["K"], max(w["Ms"])
+        N, K = w["N"], w["K"]
+        M = int(name[len("gemv_batch"):]) if name != "gemv_batch" else max(w["Ms"])
         W_host = synth.q8_0_weight(g, N, K)
         R = rotation_count(W_host.nbytes)
         base = torch.from_numpy(W_host).to("cuda")
