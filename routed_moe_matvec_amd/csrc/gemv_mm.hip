@@ -56,8 +56,16 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_kernel(MmArgs a)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     // token tiles of one row tile are neighbours in the launch order, so the
     // row tile's weights are still in the caches when the next token tile
-    // reads them
-    const int rtile = (int)blockIdx.x / a.ntok;
+    // reads them.  With several token tiles per row tile, work item wi of
+    // workgroup x goes to the XCD that runs x (workgroups are dealt to the 8
+    // XCDs in turn): XCD j takes items j * n / 8 onwards, so a row tile's
+    // token tiles share one XCD's L2 instead of each XCD fetching the row
+    // tile (512 x 8192 x 4096: 123 -> 111 us; one token tile: unchanged or
+    // slower, so kept in launch order)
+    const int nblk = (int)gridDim.x;
+    int wi = (int)blockIdx.x;
+    if (a.ntok > 1 && (nblk & 7) == 0) wi = (wi & 7) * (nblk >> 3) + (wi >> 3);
+    const int rtile = wi / a.ntok;
     const bool second = rtile >= a.nt0;
     const int g = blockIdx.y;  // grouped call: matrix g against activation slice g
     const int G = a.G;
@@ -65,7 +73,7 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_kernel(MmArgs a)
     t.N = second ? a.N1 : a.N0;
     t.W = (second ? a.W1 : a.W0) + (size_t)g * t.N * a.row_bytes;
     t.row0 = (second ? rtile - a.nt0 : rtile) * kMmRows;
-    t.m0 = ((int)blockIdx.x - rtile * a.ntok) * kMmTokens * TT;
+    t.m0 = (wi - rtile * a.ntok) * kMmTokens * TT;
     t.M = a.M;
     t.qx = a.qx;
     t.dx = a.dx;

@@ -61,6 +61,16 @@ struct MmTile {
     int K, row_bytes, groups, gps, KS;
 };
 
+// An empty statement that reads and writes 16 registers: the values are
+// computed before it, and it keeps its place among the statements with side
+// effects (memory operations, scheduling barriers).
+__device__ __forceinline__ void pin16(float (&v)[16]) {
+    asm volatile(""
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+                   "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),
+                   "+v"(v[15]));
+}
+
 template <int FMT, int NB, int GPS, int TT, class ActRow, class Out>
 __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out, uint8_t *smem) {
     using F = MmFmt<FMT>;
@@ -154,12 +164,13 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     const int slot = ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
     auto build_scales = [&](const uint8_t *stage) __attribute__((always_inline)) {
         if constexpr (FMT == QG_FMT_Q8_0) {
+            // (all four reads before the writes: one LDS round trip)
+            uint16_t v[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int bb = 4 * half + j;
-                const uint16_t v = *reinterpret_cast<const uint16_t *>(stage + kParts * 16 * r32 + 34 * bb);
-                *reinterpret_cast<uint16_t *>(stab + 2 * (bb * 32 + slot)) = v;
-            }
+            for (int j = 0; j < 4; ++j)
+                v[j] = *reinterpret_cast<const uint16_t *>(stage + kParts * 16 * r32 + 34 * (4 * half + j));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *reinterpret_cast<uint16_t *>(stab + 2 * ((4 * half + j) * 32 + slot)) = v[j];
         } else {
             const u32x4 hd = *reinterpret_cast<const u32x4 *>(stage + kParts * 16 * r32);
             const float d = half_bits_to_float(hd.x), dmin = half_bits_to_float(hd.x >> 16);
@@ -223,30 +234,48 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     };
 
     // Group j of the slice, clamped to the slice's last group (and to the
-    // row's last group for an empty slice): loads past the slice's end re-read
-    // a valid group and are not used.
+    // row's last group for an empty slice): steps past the slice's end re-read
+    // a valid group.
     auto gclamp = [&](int j) __attribute__((always_inline)) {
-        // (slices past the row's end re-read its last group: loads only)
         return min(grp0 + min(j, max(ngroups - 1, 0)), t.groups - 1);
     };
     // Weights are requested two groups ahead (two register sets), activations
-    // and their scales one group ahead.
+    // and their scales one group ahead.  A step's weight request for the group
+    // after next is issued after its activation requests for the next group:
+    // loads complete in order, so the next step's activation waits do not
+    // wait for those weights.
     // dxv: the token's 8 block scales, then (Q4_K) its 8 block sums as floats
     constexpr int DXV = FMT == QG_FMT_Q4K ? 4 : 2;
     u32x4 wreg[2][kLoads];
     float4 dxv[4];
     i32x4 act[8];
-    load_w(gclamp(0), wreg[0]);
-    if constexpr (GPS > 1) load_w(gclamp(1), wreg[1]);
     load_dx(gclamp(0), dxv);
 #pragma unroll
     for (int b = 0; b < 8; ++b) act[b] = load_act(gclamp(0), b);
+    load_w(gclamp(0), wreg[0]);
+    if constexpr (GPS > 1) load_w(gclamp(1), wreg[1]);
 
-    // Step s multiplies group grp0 + s.
+    // LDS reads of one block of a stage: the 16-byte parts of the A operand
+    // and the block's scale-table entries (Q8_0: 32 fp16 scales; Q4_K: 32
+    // d*sc and 32 dmin*m)
+    struct ARaw {
+        u32x4 c0, c1;
+    };
+    struct SRaw {
+        u32x4 v[FMT == QG_FMT_Q4K ? 8 : 2];
+    };
+
+    // Step s multiplies group grp0 + s.  Every step runs, also past the end of
+    // a partial slice, where it re-reads the slice's last group and enters a
+    // zero leaf (the one-token engine pads its tree with zeros): with no
+    // branch around a step, each wait for a group's weights counts only the
+    // loads issued before them (a step behind a branch made it wait for every
+    // load in flight).
     auto step = [&](auto index) __attribute__((always_inline)) {
         constexpr int s = decltype(index)::value;
         constexpr bool PF = s + 1 < GPS;   // activation of the next group
         constexpr bool PF2 = s + 2 < GPS;  // weights of the group after it
+        const bool real = s < ngroups;
         const int gnext = gclamp(s + 1);
         // steps are not interleaved by the scheduler (registers)
         __builtin_amdgcn_sched_barrier(0);
@@ -255,28 +284,55 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
         if constexpr (TT > 1) lds_barrier();  // the slice's whole group is staged
         build_scales(stage);
         float4 dxn[4];
-        if constexpr (PF2) load_w(gclamp(s + 2), wreg[s & 1]);
         if constexpr (PF) load_dx(gnext, dxn);
+        auto a_read = [&](auto bi) __attribute__((always_inline)) {
+            constexpr int b = decltype(bi)::value;
+            ARaw r;
+            if constexpr (FMT == QG_FMT_Q8_0) {
+                constexpr int o = 34 * b + 2;
+                constexpr int p0 = o >> 4, sh = o & 15;
+                r.c0 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * p0);
+                r.c1 = r.c0;
+                if constexpr (sh != 0) r.c1 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * (p0 + 1));
+            } else {
+                r.c0 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * (1 + 2 * (b >> 1)));
+                r.c1 = r.c0;
+            }
+            return r;
+        };
+        auto s_read = [&](auto bi) __attribute__((always_inline)) {
+            constexpr int b = decltype(bi)::value;
+            SRaw r;
+            if constexpr (FMT == QG_FMT_Q4K) {
+                const u32x4 *x = reinterpret_cast<const u32x4 *>(stab + 4 * ((2 * b) * 32 + 16 * half));
+                const u32x4 *y = reinterpret_cast<const u32x4 *>(stab + 4 * ((2 * b + 1) * 32 + 16 * half));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    r.v[q] = x[q];
+                    r.v[4 + q] = y[q];
+                }
+            } else {
+                r.v[0] = *reinterpret_cast<const u32x4 *>(stab + 64 * b + 32 * half);
+                r.v[1] = *reinterpret_cast<const u32x4 *>(stab + 64 * b + 32 * half + 16);
+            }
+            return r;
+        };
         // block b's integer sums: A operand = quants 16 half .. 16 half + 15 of
-        // block (Q4_K: sub-block) b of row lane % 32 from the stage (Q8_0:
-        // realigned bytes; Q4_K: the low / high nibbles of the 32 bytes that
-        // sub-blocks 2p and 2p + 1 share); then the next group's activation
-        // for block b is requested
-        auto block_sums = [&](auto bi) __attribute__((always_inline)) {
+        // block (Q4_K: sub-block) b of row lane % 32 (Q8_0: realigned bytes;
+        // Q4_K: the low / high nibbles of the 32 bytes that sub-blocks 2p and
+        // 2p + 1 share); then the next group's activation for block b is
+        // requested
+        auto block_sums = [&](auto bi, const ARaw &r) __attribute__((always_inline)) {
             constexpr int b = decltype(bi)::value;
             i32x4 A;
             if constexpr (FMT == QG_FMT_Q8_0) {
                 constexpr int o = 34 * b + 2;
-                constexpr int p0 = o >> 4, sh = o & 15, wd = sh >> 2, bs = sh & 3;
-                const u32x4 c0 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * p0);
-                u32x4 c1 = c0;
-                if constexpr (sh != 0) c1 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * (p0 + 1));
-                const uint32_t D[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                constexpr int sh = o & 15, wd = sh >> 2, bs = sh & 3;
+                const uint32_t D[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) A[k] = (int)(bs ? align_bytes(D[wd + k + 1], D[wd + k], bs) : D[wd + k]);
             } else {
-                const u32x4 c = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * (1 + 2 * (b >> 1)));
-                const uint32_t D[4] = {c.x, c.y, c.z, c.w};
+                const uint32_t D[4] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) A[k] = (int)(((b & 1) ? (D[k] >> 4) : D[k]) & 0x0F0F0F0Fu);
             }
@@ -287,20 +343,20 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
         };
         float acc[16], acc2[16];
         // scale and accumulate block b (the next block's product is already issued)
-        auto block_scale = [&](auto bi, const i32x16 &is) __attribute__((always_inline)) {
+        auto block_scale = [&](auto bi, const i32x16 &is, const SRaw &sr) __attribute__((always_inline)) {
             constexpr int b = decltype(bi)::value;
             if constexpr (FMT == QG_FMT_Q4K) {
                 // the one-token engine's sub-block step: inner = d sc_j isum -
                 // dmin m_j sx_j (one fma on the rounded product), then
                 // acc = fma(inner, dx_j, acc) from +0
-                const float *tab = reinterpret_cast<const float *>(stab);
                 float av[16], bv[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 x = reinterpret_cast<const float4 *>(tab + (2 * b) * 32 + 16 * half)[q];
-                    const float4 y = reinterpret_cast<const float4 *>(tab + (2 * b + 1) * 32 + 16 * half)[q];
-                    av[4 * q] = x.x, av[4 * q + 1] = x.y, av[4 * q + 2] = x.z, av[4 * q + 3] = x.w;
-                    bv[4 * q] = y.x, bv[4 * q + 1] = y.y, bv[4 * q + 2] = y.z, bv[4 * q + 3] = y.w;
+                    const u32x4 x = sr.v[q], y = sr.v[4 + q];
+                    av[4 * q] = __uint_as_float(x.x), av[4 * q + 1] = __uint_as_float(x.y);
+                    av[4 * q + 2] = __uint_as_float(x.z), av[4 * q + 3] = __uint_as_float(x.w);
+                    bv[4 * q] = __uint_as_float(y.x), bv[4 * q + 1] = __uint_as_float(y.y);
+                    bv[4 * q + 2] = __uint_as_float(y.z), bv[4 * q + 3] = __uint_as_float(y.w);
                 }
                 const float dxb = dxv[b >> 2][b & 3], sxb = dxv[2 + (b >> 2)][b & 3];
 #pragma unroll
@@ -309,33 +365,51 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
                     acc[e] = fmaf_exact(inner, dxb, b == 0 ? 0.0f : acc[e]);
                 }
             } else {
-            const u32x4 s0 = *reinterpret_cast<const u32x4 *>(stab + 64 * b + 32 * half);
-            const u32x4 s1 = *reinterpret_cast<const u32x4 *>(stab + 64 * b + 32 * half + 16);
-            const uint32_t S[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-            const float dxb = b < 4 ? dxv[0][b & 3] : dxv[1][b & 3];
-            float *ac = (NB == 4 && b >= 4) ? acc2 : acc;
+                const uint32_t S[8] = {sr.v[0].x, sr.v[0].y, sr.v[0].z, sr.v[0].w,
+                                       sr.v[1].x, sr.v[1].y, sr.v[1].z, sr.v[1].w};
+                const float dxb = b < 4 ? dxv[0][b & 3] : dxv[1][b & 3];
+                float *ac = (NB == 4 && b >= 4) ? acc2 : acc;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const uint32_t pair = S[e >> 1];
-                const half2v h = __builtin_bit_cast(half2v, pair);
-                const float dw = (float)((e & 1) ? h.y : h.x);
-                // fp32 product dw * dx (the +0 addend lets it issue as one
-                // mixed-precision fma; a -0 product would become +0, which
-                // no later sum can tell apart, since no sum starts at -0)
-                const float sc = __builtin_fmaf(dw, dxb, 0.0f);
-                const float prev = (b % NB == 0) ? 0.0f : ac[e];
-                ac[e] = fmaf_exact((float)is[e], sc, prev);
-            }
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t pair = S[e >> 1];
+                    const half2v h = __builtin_bit_cast(half2v, pair);
+                    const float dw = (float)((e & 1) ? h.y : h.x);
+                    // fp32 product dw * dx (the +0 addend lets it issue as one
+                    // mixed-precision fma; a -0 product would become +0, which
+                    // no later sum can tell apart, since no sum starts at -0)
+                    const float sc = __builtin_fmaf(dw, dxb, 0.0f);
+                    const float prev = (b % NB == 0) ? 0.0f : ac[e];
+                    ac[e] = fmaf_exact((float)is[e], sc, prev);
+                }
             }
         };
-        using I = std::integral_constant<int, 0>;
-        i32x16 cur = block_sums(I{});
+        // LDS reads run ahead of their use: block b + 2's A operand, and
+        // (Q8_0) block b + 1's scales, are read while block b is scaled; Q4_K
+        // reads a block's 32 table entries with it (a second set would not
+        // fit the registers of two waves per SIMD)
+        constexpr bool kScalesAhead = FMT == QG_FMT_Q8_0;
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        ARaw an = a_read(I0{});
+        SRaw sn;
+        if constexpr (kScalesAhead) sn = s_read(I0{});
+        i32x16 cur = block_sums(I0{}, an);
+        an = a_read(I1{});
         auto body = [&](auto bi) __attribute__((always_inline)) {
             constexpr int b = decltype(bi)::value;
+            SRaw sc;
+            if constexpr (kScalesAhead) sc = sn;
             i32x16 nxt;
-            if constexpr (b < 7) nxt = block_sums(std::integral_constant<int, b + 1>{});
+            if constexpr (b < 7) nxt = block_sums(std::integral_constant<int, b + 1>{}, an);
+            if constexpr (b + 2 < 8) an = a_read(std::integral_constant<int, b + 2>{});
+            if constexpr (kScalesAhead && b + 1 < 8) sn = s_read(std::integral_constant<int, b + 1>{});
+            if constexpr (!kScalesAhead) sc = s_read(bi);
             __builtin_amdgcn_sched_barrier(0);
-            block_scale(bi, cur);
+            block_scale(bi, cur, sc);
+            // the scaling is plain arithmetic: pinned here, in the slot whose
+            // LDS reads it hides, instead of sunk towards its last use (which
+            // kept every block's product live)
+            pin16((NB == 4 && FMT == QG_FMT_Q8_0 && b >= 4) ? acc2 : acc);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (b < 7) cur = nxt;
         };
@@ -351,56 +425,33 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[e] = acc[e] + acc2[e];
         }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = real ? acc[e] : 0.0f;
         push(acc, index);
+        if constexpr (PF2) load_w(gclamp(s + 2), wreg[s & 1]);
         if constexpr (PF) {
 #pragma unroll
             for (int i = 0; i < DXV; ++i) dxv[i] = dxn[i];
         }
     };
     static_assert(GPS == 1 || GPS == 2 || GPS == 4 || GPS == 8, "groups per slice");
-    // with shared stages every wave takes part in every step's barrier, also
-    // past the end of a partial slice
-    auto run = [&](auto index) __attribute__((always_inline)) {
-        if (ngroups > decltype(index)::value)
-            step(index);
-        else if constexpr (TT > 1)
-            lds_barrier();
-    };
-    run(std::integral_constant<int, 0>{});
-    if constexpr (GPS > 1) run(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 0>{});
+    if constexpr (GPS > 1) step(std::integral_constant<int, 1>{});
     if constexpr (GPS > 2) {
-        run(std::integral_constant<int, 2>{});
-        run(std::integral_constant<int, 3>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
     }
     if constexpr (GPS > 4) {
-        run(std::integral_constant<int, 4>{});
-        run(std::integral_constant<int, 5>{});
-        run(std::integral_constant<int, 6>{});
-        run(std::integral_constant<int, 7>{});
+        step(std::integral_constant<int, 4>{});
+        step(std::integral_constant<int, 5>{});
+        step(std::integral_constant<int, 6>{});
+        step(std::integral_constant<int, 7>{});
     }
 
-    // The slice's subtree: top for a full slice; else the pending levels of
-    // the set bits of ngroups, lowest first (the zero-padded leaves add nothing).
+    // The slice's subtree (zero leaves past a partial slice's end).
     float r[16];
-    if (ngroups == GPS) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) r[e] = top[e];
-    } else {
-        const bool b0 = ngroups & 1, b1 = ngroups & 2, b2 = ngroups & 4;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            float t = b0 ? st0[e] : 0.0f;
-            if (GPS > 2 && b1) {
-                const float l1 = lvl[e * kWave + lane];
-                t = b0 ? l1 + t : l1;
-            }
-            if (GPS > 4 && b2) {
-                const float l2 = lvl[(16 + e) * kWave + lane];
-                t = (b0 || b1) ? l2 + t : l2;
-            }
-            r[e] = t;
-        }
-    }
+    for (int e = 0; e < 16; ++e) r[e] = top[e];
     // slices meet in LDS: TT = 1, in each wave's own stage; TT > 1, in its
     // slice's stages (4 KiB per token tile) once every wave is done with them
     static_assert(TT == 1 || TT * 4096 <= 2 * kStage, "combine area");
