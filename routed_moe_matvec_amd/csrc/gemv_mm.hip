@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kMmMaxSlices *kWave) void qgemv_mm_kernel(MmArgs a)
 template <int FMT>
 constexpr size_t mm_lds_bytes(int gps, int ks, int tt) {
     return tt == 1 ? (size_t)ks * mm_wave_lds<FMT>(gps)
-                   : (size_t)ks * 2 * mm_stage_bytes<FMT>() + (size_t)ks * tt * (mm_wave_lds<FMT>(gps) - mm_stage_bytes<FMT>());
+                   : (size_t)ks * 2 * mm_stage_bytes<FMT>() +
+                         (size_t)ks * tt * (mm_wave_lds<FMT>(gps, tt) - mm_stage_bytes<FMT>());
 }
 
 template <int FMT, int NB, int GPS, int TT>
@@ -130,7 +131,9 @@ static int launch_mm(MmArgs &a, hipStream_t stream) {
     mm_slices(a.groups, (long)(a.nt0 + nt1) * a.G * ntok32, &a.KS, &a.gps);
     int tt = 1;
     if (FMT == QG_FMT_Q8_0)
-        while (tt < 4 && 2 * tt <= ntok32 && a.KS * 2 * tt <= kMmMaxSlices) tt <<= 1;
+        while (tt < 4 && 2 * tt <= ntok32 && a.KS * 2 * tt <= kMmMaxSlices &&
+               mm_lds_bytes<FMT>(a.gps, a.KS, 2 * tt) <= (size_t)kLdsBytes)
+            tt <<= 1;
     a.ntok = (ntok32 + tt - 1) / tt;
     if constexpr (FMT == QG_FMT_Q8_0) {
         if (tt == 4) return launch_mm_tt<FMT, NB, 4>(a, nt1, stream);

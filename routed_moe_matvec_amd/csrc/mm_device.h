@@ -39,11 +39,18 @@ template <int FMT>
 constexpr int mm_stage_bytes() { return MmFmt<FMT>::parts * kMmRows * 16; }
 template <int FMT>
 constexpr int mm_loads() { return (MmFmt<FMT>::parts * kMmRows + kWave - 1) / kWave; }
-// LDS of a wave: the stage, the scale table and the pending tree levels 1
-// and 2 (slices of four or eight groups)
+// Whether a tile of gps groups per slice and tt token tiles stages its
+// activation through LDS (below): where the extra LDS costs no waves per CU.
+constexpr bool mm_act_lds(int gps, int tt) { return tt > 1 || (gps >= 2 && gps <= 4); }
+// The LDS activation tile of a wave: 8 16-byte chunks x 32 tokens, token
+// stride 33 chunks.
+constexpr int kMmActTile = 8 * 33 * 16;
+// LDS of a wave: the stage, the scale table, the pending tree levels 1 and 2
+// (slices of four or eight groups) and the activation tile
 template <int FMT>
-constexpr int mm_wave_lds(int gps) {
-    return mm_stage_bytes<FMT>() + MmFmt<FMT>::table_bytes + (gps >= 8 ? 2 : gps >= 4 ? 1 : 0) * 16 * 64 * 4;
+constexpr int mm_wave_lds(int gps, int tt = 1) {
+    return mm_stage_bytes<FMT>() + MmFmt<FMT>::table_bytes + (gps >= 8 ? 2 : gps >= 4 ? 1 : 0) * 16 * 64 * 4 +
+           (mm_act_lds(gps, tt) ? kMmActTile : 0);
 }
 constexpr int kMmMaxSlices = 8;       // waves of a workgroup
 constexpr int kMmMaxGroups = 8;       // groups of a slice (three stored tree levels)
@@ -89,7 +96,8 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     // LDS: TT = 1, per wave [stage | table | levels]; TT > 1, per slice two
     // stages (double-buffered: one barrier per group), then per wave
     // [table | levels]
-    constexpr int kWaveLds = mm_wave_lds<FMT>(GPS);
+    constexpr int kWaveLds = mm_wave_lds<FMT>(GPS, TT);
+    constexpr bool ACTL = mm_act_lds(GPS, TT);
     uint8_t *stage0 = TT == 1 ? smem + wave * kWaveLds : smem + sl * 2 * kStage;
     uint8_t *stab = TT == 1 ? stage0 + kStage : smem + KS * 2 * kStage + wave * (kWaveLds - kStage);
 
@@ -116,9 +124,23 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
         if constexpr (TT > 1) soff[i] = 16u * idx;
     }
     // activation: token lane % 32 (tokens past M re-read token M - 1; their
-    // columns are not stored), 16 quants of each block per lane half
+    // columns are not stored), 16 quants of each block per lane half.
+    // ACTL: the 32 tokens x 128 bytes of a half group are read with 16-byte
+    // loads in which lane l takes token 8 i + l / 8 of instruction i < 4 and
+    // bytes 16 (l % 8) of the half group (8 runs of 128 bytes per
+    // instruction, instead of 32 tokens x 32 bytes: the address units bounded
+    // the latter), into the wave's LDS activation tile [chunk][token], from
+    // which each block's B operand is one conflict-free 16-byte read.
     const size_t arow = (size_t)act_row(min(m0 + r32, t.M - 1));
     const int8_t *xp = t.qx + arow * t.K + 16 * half;
+    uint32_t crow[ACTL ? 4 : 1];  // ACTL: byte offsets of tokens 8 i + l / 8 (M K < 2^32)
+    if constexpr (ACTL) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            crow[i] = (uint32_t)act_row(min(m0 + 8 * i + (lane >> 3), t.M - 1)) * (uint32_t)t.K + 16u * (lane & 7);
+    }
+    constexpr int kLevels = GPS >= 8 ? 2 : GPS >= 4 ? 1 : 0;
+    uint8_t *atile = stab + F::table_bytes + kLevels * 16 * 64 * 4;
     const float *dp = t.dx + arow * (t.K / 32);
     const int32_t *sp = FMT == QG_FMT_Q4K ? t.sx + arow * (t.K / 32) : nullptr;
 
@@ -139,6 +161,17 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
         }
     };
     auto load_act = [&](int gi, int b) __attribute__((always_inline)) { return *reinterpret_cast<const i32x4 *>(xp + (size_t)gi * 256 + 32 * b); };
+    // ACTL: half ph of group gi's activation into registers, and into the tile
+    auto load_half = [&](int gi, int ph, u32x4 (&c)[4]) __attribute__((always_inline)) {
+        const int8_t *base = t.qx + (size_t)gi * 256 + 128 * ph;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = *reinterpret_cast<const u32x4 *>(base + crow[i]);
+    };
+    auto write_half = [&](const u32x4 (&c)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4 *>(atile + 16 * ((lane & 7) * 33 + 8 * i + (lane >> 3))) = c[i];
+    };
 
     // Stage layout: row r's group bytes at kParts * 16 r, i.e. chunk
     // kParts r + p at 16 times that, so the loads' chunks are written
@@ -248,10 +281,16 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     constexpr int DXV = FMT == QG_FMT_Q4K ? 4 : 2;
     u32x4 wreg[2][kLoads];
     float4 dxv[4];
-    i32x4 act[8];
+    i32x4 act[ACTL ? 1 : 8];
+    u32x4 actc[ACTL ? 2 : 1][4];  // ACTL: the two half groups in flight
     load_dx(gclamp(0), dxv);
+    if constexpr (ACTL) {
+        load_half(gclamp(0), 0, actc[0]);
+        load_half(gclamp(0), 1, actc[1]);
+    } else {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) act[b] = load_act(gclamp(0), b);
+        for (int b = 0; b < 8; ++b) act[b] = load_act(gclamp(0), b);
+    }
     load_w(gclamp(0), wreg[0]);
     if constexpr (GPS > 1) load_w(gclamp(1), wreg[1]);
 
@@ -260,6 +299,7 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     // d*sc and 32 dmin*m)
     struct ARaw {
         u32x4 c0, c1;
+        i32x4 bop;  // ACTL: the block's B operand
     };
     struct SRaw {
         u32x4 v[FMT == QG_FMT_Q4K ? 8 : 2];
@@ -285,6 +325,10 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
         build_scales(stage);
         float4 dxn[4];
         if constexpr (PF) load_dx(gnext, dxn);
+        if constexpr (ACTL) {
+            write_half(actc[0]);
+            if constexpr (PF) load_half(gnext, 0, actc[0]);
+        }
         auto a_read = [&](auto bi) __attribute__((always_inline)) {
             constexpr int b = decltype(bi)::value;
             ARaw r;
@@ -298,6 +342,7 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
                 r.c0 = *reinterpret_cast<const u32x4 *>(stage + abase + 16 * (1 + 2 * (b >> 1)));
                 r.c1 = r.c0;
             }
+            if constexpr (ACTL) r.bop = *reinterpret_cast<const i32x4 *>(atile + 16 * ((2 * (b & 3) + half) * 33 + r32));
             return r;
         };
         auto s_read = [&](auto bi) __attribute__((always_inline)) {
@@ -337,8 +382,13 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
                 for (int k = 0; k < 4; ++k) A[k] = (int)(((b & 1) ? (D[k] >> 4) : D[k]) & 0x0F0F0F0Fu);
             }
             const i32x16 zero = {};
-            const i32x16 is = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, act[b], zero, 0, 0, 0);
-            if constexpr (PF) act[b] = load_act(gnext, b);
+            i32x16 is;
+            if constexpr (ACTL) {
+                is = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, r.bop, zero, 0, 0, 0);
+            } else {
+                is = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, act[b], zero, 0, 0, 0);
+                if constexpr (PF) act[b] = load_act(gnext, b);
+            }
             return is;
         };
         float acc[16], acc2[16];
@@ -401,6 +451,11 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
             if constexpr (kScalesAhead) sc = sn;
             i32x16 nxt;
             if constexpr (b < 7) nxt = block_sums(std::integral_constant<int, b + 1>{}, an);
+            if constexpr (ACTL && b == 2) {
+                // blocks 4-7: the second half group (block 3's operand is read)
+                write_half(actc[1]);
+                if constexpr (PF) load_half(gnext, 1, actc[1]);
+            }
             if constexpr (b + 2 < 8) an = a_read(std::integral_constant<int, b + 2>{});
             if constexpr (kScalesAhead && b + 1 < 8) sn = s_read(std::integral_constant<int, b + 1>{});
             if constexpr (!kScalesAhead) sc = s_read(bi);
