@@ -5,11 +5,13 @@
  * The operations follow the statement of the problem on these pages:
  *
  *  [PR623] "ROCm: restore DeepSeek V4 Flash decode performance and Q4 SSD
- *          streaming", antirez/ds4 pull request 623 -- Summary (prequantized
- *          Q8 decode for regular, paired, HC-expand and low-rank attention
- *          output projections; the compact selected-expert table staged before
- *          the pointer-backed routed-MoE launch), Correctness (the missing
- *          compact table is a hard error) and the review comments (per-stage
+ *          streaming", antirez/ds4 pull request 623 -- Summary (the attention
+ *          output projections -- single, two-matrix, HC-expand and grouped
+ *          low-rank -- consuming an activation quantized to Q8 once; a compact
+ *          table of the experts in use, built
+ *          before the expert launch, which takes the expert matrices by
+ *          pointer), Correctness (a call without that table fails instead of
+ *          falling back) and the review comments (per-stage
  *          timing of the Q8_0 entry points; a decode log in which an expert id
  *          of -1, out of the range 0..256, fails the decode).
  *  [PR621] "Support AProjQ4 GGUFs: Q4_K dense attention projections ...",
