@@ -13,11 +13,12 @@ namespace qg {
 
 constexpr int kGemvMaxWaves = 8;
 // smallest Q8_0 token batch served by the matrix-core form (measured at
-// 16384 x 4096: the dot-product engine takes 17.8 / 23.3 us at 4 / 8 tokens,
-// the matrix-core form about 29.5; from 9 tokens the engine needs a second
-// staging chunk and 12 tokens take it 37.6 us against 30.1)
-constexpr int kMmMinTokens = 9;
-// the same for Q4_K
+// 16384 x 4096: the dot-product engine takes 17.8 / 20.8-21.3 / 22.1-22.6 us
+// at 4 / 7 / 8 tokens, the matrix-core form 21.8-22.0 / 21.2-21.3 /
+// 21.3-21.5)
+constexpr int kMmMinTokens = 8;
+// the same for Q4_K (8192 x 4096 at 8 tokens: 10.6 us on the engine, 11.2 on
+// the matrix cores)
 constexpr int kMmMinTokensQ4K = 9;
 
 struct GemvArgs {

@@ -110,17 +110,27 @@ __device__ __forceinline__ int row_exponent(float amax) {
 
 // ------------------------------------------------------------------ pre-pass
 
-// One workgroup per token m: e[m] and X16[m] = x * 2^e (fp16).
+// One workgroup per token m: e[m] and X16[m] = x * 2^e (fp16).  Each thread
+// reads its 8-value chunks once (16-byte loads) and keeps them in registers
+// for the conversion after the row's maximum is known.
+constexpr int kPfPreChunks = QG_MAX_K / (8 * kPfPreThreads);  // chunks per thread at most
 __global__ __launch_bounds__(kPfPreThreads) void prefill_prepass_kernel(const uint16_t *__restrict__ X, int K,
                                                                         _Float16 *__restrict__ X16,
                                                                         int32_t *__restrict__ e_out) {
     __shared__ float red[kPfPreThreads / kWave];
     const int m = blockIdx.x, tid = threadIdx.x;
     const uint16_t *xr = X + (size_t)m * K;
+    uint4 v[kPfPreChunks];
     float amax = 0.f;
-    for (int k = 4 * tid; k < K; k += 4 * kPfPreThreads) {
-        const uint2 w = *reinterpret_cast<const uint2 *>(xr + k);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf_lo(w.x)), fabsf(bf_hi(w.x))), fmaxf(fabsf(bf_lo(w.y)), fabsf(bf_hi(w.y)))));
+#pragma unroll
+    for (int c = 0; c < kPfPreChunks; ++c) {
+        const int k = 8 * (tid + c * kPfPreThreads);
+        if (k < K) {
+            v[c] = *reinterpret_cast<const uint4 *>(xr + k);
+            const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(w[j])), fabsf(bf_hi(w[j]))));
+        }
     }
     for (int o = 1; o < kWave; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = amax;
@@ -129,12 +139,19 @@ __global__ __launch_bounds__(kPfPreThreads) void prefill_prepass_kernel(const ui
     for (int i = 1; i < kPfPreThreads / kWave; ++i) amax = fmaxf(amax, red[i]);
     const int e = row_exponent(amax);
     if (tid == 0) e_out[m] = e;
-    for (int k = 4 * tid; k < K; k += 4 * kPfPreThreads) {
-        const uint2 w = *reinterpret_cast<const uint2 *>(xr + k);
-        const half2v h0 = {(_Float16)ldexpf(bf_lo(w.x), e), (_Float16)ldexpf(bf_hi(w.x), e)};
-        const half2v h1 = {(_Float16)ldexpf(bf_lo(w.y), e), (_Float16)ldexpf(bf_hi(w.y), e)};
-        *reinterpret_cast<uint2 *>(X16 + (size_t)m * K + k) =
-            make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
+#pragma unroll
+    for (int c = 0; c < kPfPreChunks; ++c) {
+        const int k = 8 * (tid + c * kPfPreThreads);
+        if (k < K) {
+            const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const half2v h = {(_Float16)ldexpf(bf_lo(w[j]), e), (_Float16)ldexpf(bf_hi(w[j]), e)};
+                o[j] = __builtin_bit_cast(uint32_t, h);
+            }
+            *reinterpret_cast<uint4 *>(X16 + (size_t)m * K + k) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
     }
 }
 

@@ -194,7 +194,7 @@ MM_CASES = [
     # and eight groups (K = 1280, 2304: groups per row not a power of two, with
     # enough rows that a workgroup takes few slices); the 8-block unit (K > 8192)
     # with a partial slice; the largest K; ragged row tiles; 4..32 tokens
-    # (batched calls of fewer than 9 tokens run the dot-product engine, so each
+    # (batched calls of fewer than 8 tokens run the dot-product engine, so each
     # case also runs qgemm_q8_0, which always takes the matrix cores)
     (37, 256, 4),
     (100, 1280, 5),
