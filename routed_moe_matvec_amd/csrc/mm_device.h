@@ -93,9 +93,10 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     const int tt = TT == 1 ? 0 : wave / KS;     // token tile within the workgroup
     const uint8_t *W = t.W;
     const int N = t.N, row0 = t.row0, m0 = t.m0 + kMmTokens * tt;
-    // LDS: TT = 1, per wave [stage | table | levels]; TT > 1, per slice two
-    // stages (double-buffered: one barrier per group), then per wave
-    // [table | levels]
+    // LDS: TT = 1, per wave [stage | table | levels | activation tile]; TT >
+    // 1, per slice two stages (double-buffered: one barrier per group), then
+    // per wave [table | levels | activation tile] (the activation tile only
+    // where ACTL)
     constexpr int kWaveLds = mm_wave_lds<FMT>(GPS, TT);
     constexpr bool ACTL = mm_act_lds(GPS, TT);
     uint8_t *stage0 = TT == 1 ? smem + wave * kWaveLds : smem + sl * 2 * kStage;
@@ -365,8 +366,8 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
         // block b's integer sums: A operand = quants 16 half .. 16 half + 15 of
         // block (Q4_K: sub-block) b of row lane % 32 (Q8_0: realigned bytes;
         // Q4_K: the low / high nibbles of the 32 bytes that sub-blocks 2p and
-        // 2p + 1 share); then the next group's activation for block b is
-        // requested
+        // 2p + 1 share); without ACTL the next group's activation for block b
+        // is requested after it
         auto block_sums = [&](auto bi, const ARaw &r) __attribute__((always_inline)) {
             constexpr int b = decltype(bi)::value;
             i32x4 A;
