@@ -167,8 +167,11 @@ static int gemv_dispatch(int fmt, const void *W1, int N1, const void *W2, int N2
     a.isum = isum;
     a.G = G;
     clear_stale_error();
-    // larger batches go to the matrix cores (same results bit for bit)
-    if (!f32 && !isum && M >= (fmt == QG_FMT_Q8_0 ? kMmMinTokens : kMmMinTokensQ4K))
+    // larger batches go to the matrix cores (same results bit for bit), whose
+    // activation offsets are 32-bit: a grouped batch with M G K >= 2^32 bytes
+    // of activation stays on the dot-product engine
+    if (!f32 && !isum && M >= (fmt == QG_FMT_Q8_0 ? kMmMinTokens : kMmMinTokensQ4K) &&
+        (uint64_t)M * (uint64_t)G * (uint64_t)K < (1ull << 32))
         return gemv_mm(fmt, a.W0, N1, y1, a.W1, N2, y2, K, act.qx, act.dx, act.sx, M, G, stream);
     if (isum) return launch_fmt<true, false>(fmt, a, stream);
     return f32 ? launch_fmt<false, true>(fmt, a, stream) : launch_fmt<false, false>(fmt, a, stream);

@@ -134,7 +134,11 @@ __device__ __forceinline__ void mm_tile(const MmTile &t, ActRow act_row, Out out
     // which each block's B operand is one conflict-free 16-byte read.
     const size_t arow = (size_t)act_row(min(m0 + r32, t.M - 1));
     const int8_t *xp = t.qx + arow * t.K + 16 * half;
-    uint32_t crow[ACTL ? 4 : 1];  // ACTL: byte offsets of tokens 8 i + l / 8 (M K < 2^32)
+    // ACTL: byte offsets of tokens 8 i + l / 8, in 32 bits: every caller's
+    // activation is below 4 GiB (qx rows x K < 2^32; the dense calls route
+    // larger batches to the dot-product engine; the routed experts index at
+    // most QG_MAX_MOE_PAIRS rows of at most QG_MAX_K bytes)
+    uint32_t crow[ACTL ? 4 : 1];
     if constexpr (ACTL) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)

@@ -446,6 +446,32 @@ def _grouped_equals_singles(qg, g_, G, N, K, M, fmt=0):
         assert np.array_equal(host(y1).view(np.uint32), np.ascontiguousarray(yh[:, g]).view(np.uint32)), g
 
 
+def test_grouped_past_4gib_of_activation(qg, orc):
+    """A grouped batch whose activation holds more than 2^32 bytes (32 tokens x 9000
+    slices of 16384): sampled groups, including rows past the 2^32-byte mark, match
+    the oracle."""
+    import torch
+    M, G, N, K = 32, 9000, 1, 16384
+    assert M * G * K > 1 << 32
+    progress("grouped past 4 GiB M=%d G=%d N=%d K=%d" % (M, G, N, K))
+    g_ = np.random.default_rng(4242)
+    base = synth.q8_0_weight(g_, 64, K)  # row g of the stack is row g % 64 of base
+    W = dev(base).repeat((G + 63) // 64, 1)[:G].contiguous()
+    gen = torch.Generator(device="cuda").manual_seed(4243)
+    qx = torch.randint(-127, 127, (M, G * K), dtype=torch.int8, device="cuda", generator=gen)
+    dx = torch.rand((M, G * K // 32), dtype=torch.float32, device="cuda", generator=gen) * 0.01 + 1e-3
+    y = sentinel((M, G * N), torch.float32, 99.0)
+    qg.qgemv_grouped(0, W, G, N, K, qx, dx, None, M, y)
+    yh = host(y).reshape(M, G)
+    for g in (0, 1, 4095, 4096, 8191, 8999):
+        qs = host(qx[:, g * K:(g + 1) * K].contiguous())
+        ds = host(dx[:, g * K // 32:(g + 1) * K // 32].contiguous())
+        ref, bound = orc.gemv(0, base[g % 64:g % 64 + 1].copy(), N, K, qs, ds, nthreads=oracle_threads())
+        assert_within_bound(yh[:, g:g + 1], ref, bound, what="grouped past 4 GiB g=%d" % g)
+    del qx, dx
+    torch.cuda.empty_cache()
+
+
 def test_grouped_errors(qg):
     import torch
     W = dev(synth.q8_0_weight(np.random.default_rng(1), 16, 512))
