@@ -30,9 +30,10 @@
 //   exactly) and converts the activations bf16 -> fp16 into LDS (e = 0, so it
 //   needs |x| <= 65504 and loses low bits of |x| < 2^-17), with padded rows.
 //   qgemm_prefill_ws: a pre-pass (one workgroup per token) finds e and writes
-//   x * 2^e as fp16 to a caller workspace; the GEMM (eight waves, operands
-//   through pipelined global -> LDS copies, weights dequantized in registers;
-//   described at the kernel) reads it from there.
+//   x * 2^e as fp16, and the sums of its 32-input blocks as fp16 hi + lo
+//   pairs, to a caller workspace; the GEMM (eight waves, operands through
+//   pipelined global -> LDS copies, weights dequantized in registers;
+//   described at the kernel) reads them from there.
 #include <type_traits>
 
 #include "common.h"
@@ -110,13 +111,19 @@ __device__ __forceinline__ int row_exponent(float amax) {
 
 // ------------------------------------------------------------------ pre-pass
 
-// One workgroup per token m: e[m] and X16[m] = x * 2^e (fp16).  Each thread
-// reads its 8-value chunks once (16-byte loads) and keeps them in registers
-// for the conversion after the row's maximum is known.
+// One workgroup per token m: e[m], X16[m] = x * 2^e (fp16), and for every
+// 32-input block b the sum S of its 32 fp16 values, stored as S * 2^-6 split
+// into fp16 hi + lo (SH[m][b], SL[m][b]).  Each thread reads its 8-value
+// chunks once (16-byte loads) and keeps them in registers for the conversion
+// after the row's maximum is known; a block's four chunks sit in four
+// neighbouring lanes, each chunk summed as a pairwise tree, then the four
+// chunk sums as (c0 + c1) + (c2 + c3).
 constexpr int kPfPreChunks = QG_MAX_K / (8 * kPfPreThreads);  // chunks per thread at most
 __global__ __launch_bounds__(kPfPreThreads) void prefill_prepass_kernel(const uint16_t *__restrict__ X, int K,
                                                                         _Float16 *__restrict__ X16,
-                                                                        int32_t *__restrict__ e_out) {
+                                                                        int32_t *__restrict__ e_out,
+                                                                        _Float16 *__restrict__ SH,
+                                                                        _Float16 *__restrict__ SL) {
     __shared__ float red[kPfPreThreads / kWave];
     const int m = blockIdx.x, tid = threadIdx.x;
     const uint16_t *xr = X + (size_t)m * K;
@@ -142,15 +149,27 @@ __global__ __launch_bounds__(kPfPreThreads) void prefill_prepass_kernel(const ui
 #pragma unroll
     for (int c = 0; c < kPfPreChunks; ++c) {
         const int k = 8 * (tid + c * kPfPreThreads);
+        float p = 0.0f;  // this chunk's sum (0 past the row: K / 8 chunks come in whole blocks)
         if (k < K) {
             const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
             uint32_t o[4];
+            float f[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const half2v h = {(_Float16)ldexpf(bf_lo(w[j]), e), (_Float16)ldexpf(bf_hi(w[j]), e)};
                 o[j] = __builtin_bit_cast(uint32_t, h);
+                f[2 * j] = (float)h.x;
+                f[2 * j + 1] = (float)h.y;
             }
             *reinterpret_cast<uint4 *>(X16 + (size_t)m * K + k) = make_uint4(o[0], o[1], o[2], o[3]);
+            p = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+        }
+        // lanes 4i .. 4i+3 hold the block's chunks (k / 8 = tid + 256 c)
+        p = p + __shfl_xor(p, 1, kWave);
+        p = p + __shfl_xor(p, 2, kWave);
+        if (k < K && (tid & 3) == 0) {
+            const size_t at = (size_t)m * (K / 32) + k / 32;
+            split_half(ldexpf(p, -kPfSumShift), SH[at], SL[at]);
         }
     }
 }
@@ -368,15 +387,21 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
 // one wave's copies and dequantization overlap the other's MFMAs), each wave
 // 64 tokens x 32 rows.  K advances 128 per step.
 //
-// Every global read of a step is a global -> LDS copy (global_load_lds), six
-// per thread, into one of three rotating LDS stages, issued two steps ahead:
+// Every global read of a step is a global -> LDS copy (global_load_lds), seven
+// per thread, issued two steps ahead, six into one of three rotating LDS
+// stages:
 //   * the 128 x 128 fp16 activations (from the pre-pass): rows of 16 chunks
 //     of 16 bytes, chunk c of row r stored at r*16 + (c ^ (r & 15)), so the
 //     16 lanes reading one operand column hit 16 different bank groups;
 //   * the 128 weight rows' 64 nibble bytes of this half superblock: rows of
 //     four 16-byte units, unit u of row r stored at r*4 + (u ^ ((r >> 2) & 3)),
 //     so the 8-byte operand reads are conflict-free;
-//   * the 128 superblock headers (d, dmin, scale fields).
+//   * the 128 superblock headers (d, dmin, scale fields);
+// and one into the block sums of the min-term window (four superblocks, eight
+// steps): the pre-pass's hi / lo sums of the step's four 32-input blocks for
+// the 128 tokens, stored [step in window][token][4], in one of two buffers by
+// window parity, so the next window's copies never meet the current window's
+// reads.
 // No vector register is the destination of a prefetch, so nothing makes the
 // compiler wait early; the explicit waits below are the only ones on them.
 // From LDS each lane takes the 8 nibble bytes of its B operand (column =
@@ -386,7 +411,8 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
 constexpr int kPf3Threads = 512;
 constexpr int kPf3ChunkUnits = 16;    // 16-byte chunks per 128-half activation row
 constexpr int kPf3Stages = 3;         // LDS stages: compute one, two in flight
-constexpr int kPf3LoadsPerStep = 6;   // per thread: 4 activation + 1 nibble + 1 header copy
+constexpr int kPf3LoadsPerStep = 7;   // per thread: 4 activation + 1 nibble + 1 header + 1 block-sum copy
+constexpr int kPfWinSteps = 2 * kPfWin;  // steps of a min-term window
 
 struct __attribute__((aligned(16))) Prefill3Stage {
     _Float16 a[kPfBM * kPfKS];   // 32 KiB activations, swizzled
@@ -431,38 +457,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// LDS reads issued together and completed inside one asm block, from one base
-// address and immediate offsets.  Written this way because the compiler,
+// LDS reads issued together and completed inside one asm block, from base
+// addresses and immediate offsets.  Written this way because the compiler,
 // unable to place the global -> LDS copies in flight into the other stages,
 // would otherwise wait for all of them before any LDS read; the copies are
 // ordered against these reads by the explicit wait and barrier at the end of
 // every step instead.
-template <int O1, int O2, int O3>
-__device__ __forceinline__ void lds_read4_b128(uint32_t base, u32x4p &r0, u32x4p &r1, u32x4p &r2, u32x4p &r3) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:%5\n\t"
-        "ds_read_b128 %2, %4 offset:%6\n\t"
-        "ds_read_b128 %3, %4 offset:%7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(base), "i"(O1), "i"(O2), "i"(O3)
-        : "memory");
-}
-
-__device__ __forceinline__ void lds_read4_b128_addr(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4p &r0,
-                                                    u32x4p &r1, u32x4p &r2, u32x4p &r3) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-        : "memory");
-}
-
 // two k-slices: for each, four 16-byte A fragments (rows 16 apart) and two
 // 8-byte nibble groups (rows 16 apart)
 __device__ __forceinline__ void lds_read_slice2(uint32_t a, uint32_t n, uint32_t a2, uint32_t n2, u32x4p (&r)[8],
@@ -487,20 +487,20 @@ __device__ __forceinline__ void lds_read_slice2(uint32_t a, uint32_t n, uint32_t
         : "memory");
 }
 
-// one k-slice: four 16-byte A fragments (base a, rows 16 apart) and two
-// 8-byte nibble groups (base n, rows 16 apart)
-__device__ __forceinline__ void lds_read_slice(uint32_t a, uint32_t n, u32x4p &r0, u32x4p &r1, u32x4p &r2, u32x4p &r3,
-                                               uint2 &q0, uint2 &q1) {
+// eight 8-byte reads: base + 128 i (i < 4) and base + 1024 + 128 i
+__device__ __forceinline__ void lds_read8_b64(uint32_t base, uint2 (&r)[8]) {
     asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %6 offset:4096\n\t"
-        "ds_read_b128 %2, %6 offset:8192\n\t"
-        "ds_read_b128 %3, %6 offset:12288\n\t"
-        "ds_read_b64 %4, %7\n\t"
-        "ds_read_b64 %5, %7 offset:1024\n\t"
+        "ds_read_b64 %0, %8\n\t"
+        "ds_read_b64 %1, %8 offset:128\n\t"
+        "ds_read_b64 %2, %8 offset:256\n\t"
+        "ds_read_b64 %3, %8 offset:384\n\t"
+        "ds_read_b64 %4, %8 offset:1024\n\t"
+        "ds_read_b64 %5, %8 offset:1152\n\t"
+        "ds_read_b64 %6, %8 offset:1280\n\t"
+        "ds_read_b64 %7, %8 offset:1408\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(q0), "=&v"(q1)
-        : "v"(a), "v"(n)
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(base)
         : "memory");
 }
 
@@ -530,13 +530,16 @@ __device__ __forceinline__ void wait_vmem_lgkm() {
 // re-read the last step's data, so every step issues the same copies.
 __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
     const uint8_t *__restrict__ W, int N, int K, int M, const _Float16 *__restrict__ X16,
-    const int32_t *__restrict__ E_x, float *__restrict__ Y) {
+    const int32_t *__restrict__ E_x, const _Float16 *__restrict__ SH, const _Float16 *__restrict__ SL,
+    float *__restrict__ Y) {
     // three stages as three LDS objects: the compiler tells a stage's reads
     // from the copies in flight into another stage by object, not by offset
     __shared__ Prefill3Stage st0, st1, st2;
-    // sums of the 32-input blocks of the current min-term window, S * 2^(e-6)
-    // split into fp16 hi + lo: [row][8 * (superblock in window) + sub-block]
-    __shared__ __attribute__((aligned(16))) _Float16 wsum_hi[kPfBM * 32], wsum_lo[kPfBM * 32];
+    // sums of the 32-input blocks of a min-term window, S * 2^(e-6) split into
+    // fp16 hi + lo: [window parity][step in window][token][4 blocks]
+    constexpr int kSumSlice = kPfBM * 4;  // halves of one step's sums
+    __shared__ __attribute__((aligned(16))) _Float16 wsum_hi[2 * kPfWinSteps * kSumSlice],
+        wsum_lo[2 * kPfWinSteps * kSumSlice];
     auto stage_ref = [&](auto sc) -> Prefill3Stage & {
         constexpr int i = decltype(sc)::value;
         if constexpr (i == 0)
@@ -576,6 +579,14 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
         const int s = gl >> 1, h = gl & 1;
         global_to_lds16(nib_src + (size_t)s * 144 + 64 * h, S.nib + wave * 1024);
         global_to_lds4(hdr_src + (size_t)s * 144, S.hdr + wave * 64);
+        // block sums 4 gl .. 4 gl + 3: waves 0-3 the hi halves, 4-7 the lo;
+        // lane l of wave v takes dword (v % 4) * 64 + l of the slice, i.e.
+        // token ((v % 4) * 64 + l) / 2, blocks 2 (l % 2) .. + 1
+        const int sd = (wave & 3) * 64 + lane;
+        const _Float16 *ssrc = (wave < 4 ? SH : SL) + (size_t)min(m0 + (sd >> 1), M - 1) * (K / 32) + 4 * gl + 2 * (sd & 1);
+        _Float16 *sdst = (wave < 4 ? wsum_hi : wsum_lo) +
+                         (((gl / kPfWinSteps) & 1) * kPfWinSteps + gl % kPfWinSteps) * kSumSlice + (wave & 3) * 128;
+        global_to_lds4(ssrc, sdst);
     };
 
     f32x4 acc[4][2], cs[4][2];
@@ -608,33 +619,6 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
         const bool mlive = sb_start + quad <= s;
         issue(g + 2, std::integral_constant<int, (k + 2) % kPf3Stages>{});
         const Prefill3Stage &S = stage_ref(std::integral_constant<int, stage>{});
-        {
-            // this step's 32-input block sums: thread t sums sub-block t % 4 of
-            // row t / 4 (16 fp16 pairs, dot2 against ones into fp32, in order)
-            // (the sub-block's four chunks form one 64-byte group of the swizzled
-            // row, summed in stored order: a fixed order for every row)
-            // (read in an order rotated by the row, so the 16 lanes of a read hit
-            // 16 different bank groups)
-            const int r = tid >> 2, jb = tid & 3;
-            u32x4p v[4];
-            const _Float16 *grp = S.a + r * kPf3ChunkUnits * 8 + 32 * (jb ^ ((r & 15) >> 2));
-            uint32_t ad[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) ad[c] = lds_addr(grp + 8 * ((c + r) & 3));
-            lds_read4_b128_addr(ad[0], ad[1], ad[2], ad[3], v[0], v[1], v[2], v[3]);
-            const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
-            float sum = 0.0f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                // elements go through scalars: this compiler reads element 0 for a
-                // bit cast taken straight from a vector element
-                const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w[e]), one2, sum, false);
-            }
-            const int at = r * 32 + 8 * (s & (kPfWin - 1)) + 4 * h + jb;
-            split_half(ldexpf(sum, -kPfSumShift), wsum_hi[at], wsum_lo[at]);
-        }
         // headers of this lane's two columns; scales of this step's four
         // sub-blocks (fields 4h .. 4h+3), zero for a padding step
         u32x4p hd[2];
@@ -668,8 +652,8 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
                 for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(half8, ar[4 * t + i]);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const _Float16 v = (_Float16)(float)((bits[j] >> (6 * kk)) & 63u);
-                    const _Float16 o = (_Float16)(-1024.0f * (float)v);
+                    const _Float16 v = (_Float16)(uint16_t)((bits[j] >> (6 * kk)) & 63u);
+                    const _Float16 o = v * (_Float16)(-1024.0f);  // exact: |.| <= 64512
                     bf[j] = b_operand(nb[2 * t + j], kk & 1, half2v{v, v}, half2v{o, o});
                 }
 #pragma unroll
@@ -697,17 +681,24 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
             }
         }
         if (window_end) {
-            // min term of the window; slot = lane / 16 is its superblock.  Every
-            // wave's block sums of this step are written first.
-            wait_vmem_lgkm<kPf3LoadsPerStep>();
-            barrier_no_fence();
-            // slots past the window's last superblock hold finite leftovers
-            // (the arrays start zeroed) and meet zero weights below
+            // min term of the window; slot = lane / 16 is its superblock.  The
+            // window's block sums came with its steps' copies, all waited for.
+            // Slots past the window's last superblock hold finite leftovers
+            // (the buffers start zeroed) and meet zero weights below.
             u32x4p t[8];
             {
-                const int row = 64 * wm + l16;  // rows 16 apart: +1024 bytes
-                lds_read4_b128<1024, 2048, 3072>(lds_addr(wsum_hi + row * 32 + 8 * quad), t[0], t[1], t[2], t[3]);
-                lds_read4_b128<1024, 2048, 3072>(lds_addr(wsum_lo + row * 32 + 8 * quad), t[4], t[5], t[6], t[7]);
+                // token rows 16 apart (+128 bytes); the lane's 8 blocks are those
+                // of steps 2 quad and 2 quad + 1 of the window (+1024 bytes)
+                const int row = 64 * wm + l16;
+                const int sl0 = (((g / kPfWinSteps) & 1) * kPfWinSteps + 2 * quad) * kSumSlice + 4 * row;
+                uint2 rh[8], rl[8];
+                lds_read8_b64(lds_addr(wsum_hi + sl0), rh);
+                lds_read8_b64(lds_addr(wsum_lo + sl0), rl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    t[i] = u32x4p{rh[i].x, rh[i].y, rh[4 + i].x, rh[4 + i].y};
+                    t[4 + i] = u32x4p{rl[i].x, rl[i].y, rl[4 + i].x, rl[4 + i].y};
+                }
             }
             half8 mh[2], ml[2];
             float fac[2];
@@ -749,13 +740,14 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
         barrier_no_fence();
     };
 
-    for (int i = tid; i < kPfBM * 32 / 8; i += kPf3Threads) {
+    for (int i = tid; i < 2 * kPfWinSteps * kSumSlice / 8; i += kPf3Threads) {
         reinterpret_cast<u32x4p *>(wsum_hi)[i] = u32x4p{0, 0, 0, 0};
         reinterpret_cast<u32x4p *>(wsum_lo)[i] = u32x4p{0, 0, 0, 0};
     }
+    __syncthreads();  // the zeros are written before any copy can land on them
     issue(0, std::integral_constant<int, 0>{});
     issue(1, std::integral_constant<int, 1>{});
-    wait_vmem_lgkm<kPf3LoadsPerStep>();  // step 0's copies and the zeroed sums are in LDS
+    wait_vmem_lgkm<kPf3LoadsPerStep>();  // step 0's copies are in LDS
     barrier_no_fence();
     const int nbody = nsteps - nsteps % 6;
     int g6 = 0;
@@ -795,14 +787,18 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// x * 2^e as fp16 [M][K], e [M], then the block sums' hi and lo halves
+// [M][K / 32] each, every region 256-byte aligned
 struct PrefillWs {
-    size_t off_e, total;
+    size_t off_e, off_sh, off_sl, total;
 };
 
 static PrefillWs prefill_ws_layout(int M, int K) {
     PrefillWs w;
     w.off_e = align256((size_t)M * K * 2);
-    w.total = w.off_e + align256((size_t)M * 4);
+    w.off_sh = w.off_e + align256((size_t)M * 4);
+    w.off_sl = w.off_sh + align256((size_t)M * (K / 32) * 2);
+    w.total = w.off_sl + align256((size_t)M * (K / 32) * 2);
     return w;
 }
 
@@ -844,12 +840,14 @@ extern "C" int qgemm_prefill_ws(int fmt, const void *W, int N, int K, const uint
     uint8_t *b = reinterpret_cast<uint8_t *>(ws);
     _Float16 *x16 = reinterpret_cast<_Float16 *>(b);
     int32_t *ex = reinterpret_cast<int32_t *>(b + lay.off_e);
+    _Float16 *sh = reinterpret_cast<_Float16 *>(b + lay.off_sh);
+    _Float16 *sl = reinterpret_cast<_Float16 *>(b + lay.off_sl);
     qg::clear_stale_error();
     hipLaunchKernelGGL(qg::prefill_prepass_kernel, dim3(M), dim3(qg::kPfPreThreads), 0, (hipStream_t)stream, x_bf16,
-                       K, x16, ex);
+                       K, x16, ex, sh, sl);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
     dim3 grid((N + qg::kPfBN - 1) / qg::kPfBN, (M + qg::kPfBM - 1) / qg::kPfBM);
     hipLaunchKernelGGL(qg::qgemm_prefill_q4k_ws_kernel, grid, dim3(qg::kPf3Threads), 0, (hipStream_t)stream,
-                       reinterpret_cast<const uint8_t *>(W), N, K, M, x16, ex, y);
+                       reinterpret_cast<const uint8_t *>(W), N, K, M, x16, ex, sh, sl, y);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
