@@ -412,9 +412,10 @@ int qgemm_prefill(int fmt, const void *W, int N, int K, const uint16_t *x_bf16, 
  * qgemm_prefill_workspace_bytes -- size of the device workspace that
  * qgemm_prefill_ws needs for M tokens of K inputs: x scaled by a power of two
  * per token as fp16 [M, K], the int32 exponents [M], then the sums of the
- * scaled x over each 32-input block as fp16 high and low parts [M, K/32]
- * each, every region 256-byte aligned.  Returns 0 for an invalid shape (the
- * rules of qgemm_prefill).
+ * scaled x over each 32-input block as fp16 high and low parts, [M, K/128]
+ * records of 8 halves (the high parts of four blocks, then their low parts),
+ * every region 256-byte aligned.  Returns 0 for an invalid shape (the rules
+ * of qgemm_prefill).
  */
 size_t qgemm_prefill_workspace_bytes(int M, int K);
 

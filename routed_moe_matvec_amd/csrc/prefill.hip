@@ -113,7 +113,9 @@ __device__ __forceinline__ int row_exponent(float amax) {
 
 // One workgroup per token m: e[m], X16[m] = x * 2^e (fp16), and for every
 // 32-input block b the sum S of its 32 fp16 values, stored as S * 2^-6 split
-// into fp16 hi + lo (SH[m][b], SL[m][b]).  Each thread reads its 8-value
+// into fp16 hi + lo: the four blocks of each 128-input step as one 16-byte
+// record SS[m][b / 4] = {hi of blocks 0..3, lo of blocks 0..3}, so that the
+// GEMM copies a token's step with one 16-byte read.  Each thread reads its 8-value
 // chunks once (16-byte loads) and keeps them in registers for the conversion
 // after the row's maximum is known; a block's four chunks sit in four
 // neighbouring lanes, each chunk summed as a pairwise tree, then the four
@@ -122,8 +124,7 @@ constexpr int kPfPreChunks = QG_MAX_K / (8 * kPfPreThreads);  // chunks per thre
 __global__ __launch_bounds__(kPfPreThreads) void prefill_prepass_kernel(const uint16_t *__restrict__ X, int K,
                                                                         _Float16 *__restrict__ X16,
                                                                         int32_t *__restrict__ e_out,
-                                                                        _Float16 *__restrict__ SH,
-                                                                        _Float16 *__restrict__ SL) {
+                                                                        _Float16 *__restrict__ SS) {
     __shared__ float red[kPfPreThreads / kWave];
     const int m = blockIdx.x, tid = threadIdx.x;
     const uint16_t *xr = X + (size_t)m * K;
@@ -168,8 +169,9 @@ __global__ __launch_bounds__(kPfPreThreads) void prefill_prepass_kernel(const ui
         p = p + __shfl_xor(p, 1, kWave);
         p = p + __shfl_xor(p, 2, kWave);
         if (k < K && (tid & 3) == 0) {
-            const size_t at = (size_t)m * (K / 32) + k / 32;
-            split_half(ldexpf(p, -kPfSumShift), SH[at], SL[at]);
+            const int b = k / 32;
+            _Float16 *rec = SS + ((size_t)m * (K / 128) + b / 4) * 8 + b % 4;
+            split_half(ldexpf(p, -kPfSumShift), rec[0], rec[4]);
         }
     }
 }
@@ -385,10 +387,11 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
 
 // 128 tokens x 128 weight rows per workgroup of eight waves (two per SIMD, so
 // one wave's copies and dequantization overlap the other's MFMAs), each wave
-// 64 tokens x 32 rows.  K advances 128 per step.
+// the 128 tokens x 16 rows, so that every weight is dequantized by one wave
+// (64 x 32 wave tiles dequantized each weight twice).  K advances 128 per step.
 //
-// Every global read of a step is a global -> LDS copy (global_load_lds), seven
-// per thread, issued two steps ahead, six into one of three rotating LDS
+// Every global read of a step is a global -> LDS copy (global_load_lds), six
+// or seven per thread, issued two steps ahead, into one of three rotating LDS
 // stages:
 //   * the 128 x 128 fp16 activations (from the pre-pass): rows of 16 chunks
 //     of 16 bytes, chunk c of row r stored at r*16 + (c ^ (r & 15)), so the
@@ -398,10 +401,14 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
 //     so the 8-byte operand reads are conflict-free;
 //   * the 128 superblock headers (d, dmin, scale fields);
 // and one into the block sums of the min-term window (four superblocks, eight
-// steps): the pre-pass's hi / lo sums of the step's four 32-input blocks for
-// the 128 tokens, stored [step in window][token][4], in one of two buffers by
+// steps): the pre-pass's 16-byte records of the step's four 32-input blocks
+// for the 128 tokens, stored [step in window][token], in one of two buffers by
 // window parity, so the next window's copies never meet the current window's
-// reads.
+// reads.  The headers are copied with the first half of each superblock only
+// and kept in registers for the second; the header and block-sum copies take
+// one 16-byte lane per row (rows sit 144 bytes or more apart: 4-byte lanes
+// spread the same bytes over four times the lanes and twice the cache lines,
+// 512x8192x4096 with the pre-pass: 61.5 -> 57.5 us).
 // No vector register is the destination of a prefetch, so nothing makes the
 // compiler wait early; the explicit waits below are the only ones on them.
 // From LDS each lane takes the 8 nibble bytes of its B operand (column =
@@ -411,7 +418,9 @@ __global__ __launch_bounds__(256) void qgemm_prefill_q4k_kernel(const uint8_t *_
 constexpr int kPf3Threads = 512;
 constexpr int kPf3ChunkUnits = 16;    // 16-byte chunks per 128-half activation row
 constexpr int kPf3Stages = 3;         // LDS stages: compute one, two in flight
-constexpr int kPf3LoadsPerStep = 7;   // per thread: 4 activation + 1 nibble + 1 header + 1 block-sum copy
+// copies per thread and step: 4 activation + 1 nibble + 1 block-sum copy, and
+// in the first half of a superblock (even steps) 1 header copy
+constexpr int pf3_copies(int h) { return h == 0 ? 7 : 6; }
 constexpr int kPfWinSteps = 2 * kPfWin;  // steps of a min-term window
 
 struct __attribute__((aligned(16))) Prefill3Stage {
@@ -463,53 +472,69 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // would otherwise wait for all of them before any LDS read; the copies are
 // ordered against these reads by the explicit wait and barrier at the end of
 // every step instead.
-// two k-slices: for each, four 16-byte A fragments (rows 16 apart) and two
-// 8-byte nibble groups (rows 16 apart)
-__device__ __forceinline__ void lds_read_slice2(uint32_t a, uint32_t n, uint32_t a2, uint32_t n2, u32x4p (&r)[8],
-                                                uint2 (&q)[4]) {
+// two k-slices: for each, eight 16-byte A fragments (base a, rows 16 apart,
+// +4096 bytes each) and one 8-byte nibble group (base n)
+__device__ __forceinline__ void lds_read_slice2_t(uint32_t a, uint32_t n, uint32_t a2, uint32_t n2, u32x4p (&r)[16],
+                                                  uint2 (&q)[2]) {
     asm volatile(
-        "ds_read_b128 %0, %12\n\t"
-        "ds_read_b128 %1, %12 offset:4096\n\t"
-        "ds_read_b128 %2, %12 offset:8192\n\t"
-        "ds_read_b128 %3, %12 offset:12288\n\t"
-        "ds_read_b64 %8, %13\n\t"
-        "ds_read_b64 %9, %13 offset:1024\n\t"
-        "ds_read_b128 %4, %14\n\t"
-        "ds_read_b128 %5, %14 offset:4096\n\t"
-        "ds_read_b128 %6, %14 offset:8192\n\t"
-        "ds_read_b128 %7, %14 offset:12288\n\t"
-        "ds_read_b64 %10, %15\n\t"
-        "ds_read_b64 %11, %15 offset:1024\n\t"
+        "ds_read_b128 %0, %18\n\t"
+        "ds_read_b128 %1, %18 offset:4096\n\t"
+        "ds_read_b128 %2, %18 offset:8192\n\t"
+        "ds_read_b128 %3, %18 offset:12288\n\t"
+        "ds_read_b128 %4, %18 offset:16384\n\t"
+        "ds_read_b128 %5, %18 offset:20480\n\t"
+        "ds_read_b128 %6, %18 offset:24576\n\t"
+        "ds_read_b128 %7, %18 offset:28672\n\t"
+        "ds_read_b64 %16, %19\n\t"
+        "ds_read_b128 %8, %20\n\t"
+        "ds_read_b128 %9, %20 offset:4096\n\t"
+        "ds_read_b128 %10, %20 offset:8192\n\t"
+        "ds_read_b128 %11, %20 offset:12288\n\t"
+        "ds_read_b128 %12, %20 offset:16384\n\t"
+        "ds_read_b128 %13, %20 offset:20480\n\t"
+        "ds_read_b128 %14, %20 offset:24576\n\t"
+        "ds_read_b128 %15, %20 offset:28672\n\t"
+        "ds_read_b64 %17, %21\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
-          "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3])
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+          "=&v"(r[15]), "=&v"(q[0]), "=&v"(q[1])
         : "v"(a), "v"(n), "v"(a2), "v"(n2)
         : "memory");
 }
 
-// eight 8-byte reads: base + 128 i (i < 4) and base + 1024 + 128 i
-__device__ __forceinline__ void lds_read8_b64(uint32_t base, uint2 (&r)[8]) {
+// sixteen 16-byte reads: base + 256 i and base + 2048 + 256 i (i < 8)
+__device__ __forceinline__ void lds_read16_b128(uint32_t base, u32x4p (&r)[16]) {
     asm volatile(
-        "ds_read_b64 %0, %8\n\t"
-        "ds_read_b64 %1, %8 offset:128\n\t"
-        "ds_read_b64 %2, %8 offset:256\n\t"
-        "ds_read_b64 %3, %8 offset:384\n\t"
-        "ds_read_b64 %4, %8 offset:1024\n\t"
-        "ds_read_b64 %5, %8 offset:1152\n\t"
-        "ds_read_b64 %6, %8 offset:1280\n\t"
-        "ds_read_b64 %7, %8 offset:1408\n\t"
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %16 offset:256\n\t"
+        "ds_read_b128 %2, %16 offset:512\n\t"
+        "ds_read_b128 %3, %16 offset:768\n\t"
+        "ds_read_b128 %4, %16 offset:1024\n\t"
+        "ds_read_b128 %5, %16 offset:1280\n\t"
+        "ds_read_b128 %6, %16 offset:1536\n\t"
+        "ds_read_b128 %7, %16 offset:1792\n\t"
+        "ds_read_b128 %8, %16 offset:2048\n\t"
+        "ds_read_b128 %9, %16 offset:2304\n\t"
+        "ds_read_b128 %10, %16 offset:2560\n\t"
+        "ds_read_b128 %11, %16 offset:2816\n\t"
+        "ds_read_b128 %12, %16 offset:3072\n\t"
+        "ds_read_b128 %13, %16 offset:3328\n\t"
+        "ds_read_b128 %14, %16 offset:3584\n\t"
+        "ds_read_b128 %15, %16 offset:3840\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+          "=&v"(r[15])
         : "v"(base)
         : "memory");
 }
 
-__device__ __forceinline__ void lds_read2_b128_256(uint32_t base, u32x4p &r0, u32x4p &r1) {
+__device__ __forceinline__ void lds_read1_b128(uint32_t base, u32x4p &r0) {
     asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %2 offset:256\n\t"
+        "ds_read_b128 %0, %1\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1)
+        : "=&v"(r0)
         : "v"(base)
         : "memory");
 }
@@ -530,16 +555,15 @@ __device__ __forceinline__ void wait_vmem_lgkm() {
 // re-read the last step's data, so every step issues the same copies.
 __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
     const uint8_t *__restrict__ W, int N, int K, int M, const _Float16 *__restrict__ X16,
-    const int32_t *__restrict__ E_x, const _Float16 *__restrict__ SH, const _Float16 *__restrict__ SL,
-    float *__restrict__ Y) {
+    const int32_t *__restrict__ E_x, const _Float16 *__restrict__ SS, float *__restrict__ Y) {
     // three stages as three LDS objects: the compiler tells a stage's reads
     // from the copies in flight into another stage by object, not by offset
     __shared__ Prefill3Stage st0, st1, st2;
     // sums of the 32-input blocks of a min-term window, S * 2^(e-6) split into
-    // fp16 hi + lo: [window parity][step in window][token][4 blocks]
-    constexpr int kSumSlice = kPfBM * 4;  // halves of one step's sums
-    __shared__ __attribute__((aligned(16))) _Float16 wsum_hi[2 * kPfWinSteps * kSumSlice],
-        wsum_lo[2 * kPfWinSteps * kSumSlice];
+    // fp16 hi + lo: [window parity][step in window][token] records of
+    // {hi of the step's 4 blocks, lo of them}
+    constexpr int kSumSlice = kPfBM * 8;  // halves of one step's records
+    __shared__ __attribute__((aligned(16))) _Float16 wsum[2 * kPfWinSteps * kSumSlice];
     auto stage_ref = [&](auto sc) -> Prefill3Stage & {
         constexpr int i = decltype(sc)::value;
         if constexpr (i == 0)
@@ -550,8 +574,7 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
             return st2;
     };
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;  // 64 tokens x 32 rows
+    const int lane = tid & 63, wave = tid >> 6;  // wave: all 128 tokens x weight rows 16 wave ..
     const int n0 = blockIdx.x * kPfBN, m0 = blockIdx.y * kPfBM;
     const int nsb = K / 256;
     const int nsteps = 2 * nsb;
@@ -562,10 +585,13 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
     const int nib_row = 16 * wave + (lane >> 2);                      // weight row whose nibbles it copies
     const int nib_unit = (lane & 3) ^ ((nib_row >> 2) & 3);           // logical 16-byte unit it fetches
     const uint8_t *nib_src = W + (size_t)min(n0 + nib_row, N - 1) * row_bytes + 16 + 16 * nib_unit;
-    const int hdr_row = tid >> 2;                                     // header dword tid % 4 of row tid / 4
-    const uint8_t *hdr_src = W + (size_t)min(n0 + hdr_row, N - 1) * row_bytes + 4 * (tid & 3);
+    // lanes 0-15 of wave w copy the headers of weight rows 16 w .. (16 bytes
+    // each) and the block-sum records of tokens 16 w ..; the other lanes idle
+    const bool copy16 = lane < 16;
+    const uint8_t *hdr_src = W + (size_t)min(n0 + 16 * wave + l16, N - 1) * row_bytes;
+    const _Float16 *sum_src = SS + (size_t)min(m0 + 16 * wave + l16, M - 1) * (K / 128) * 8;
 
-    auto issue = [&](int g, auto stage) {
+    auto issue = [&](int g, auto stage, auto hc) {
         const int gl = min(g, nsteps - 1);
         const int k0 = 128 * gl;
         Prefill3Stage &S = stage_ref(stage);
@@ -578,29 +604,21 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
         }
         const int s = gl >> 1, h = gl & 1;
         global_to_lds16(nib_src + (size_t)s * 144 + 64 * h, S.nib + wave * 1024);
-        global_to_lds4(hdr_src + (size_t)s * 144, S.hdr + wave * 64);
-        // block sums 4 gl .. 4 gl + 3: waves 0-3 the hi halves, 4-7 the lo;
-        // lane l of wave v takes dword (v % 4) * 64 + l of the slice, i.e.
-        // token ((v % 4) * 64 + l) / 2, blocks 2 (l % 2) .. + 1
-        const int sd = (wave & 3) * 64 + lane;
-        const _Float16 *ssrc = (wave < 4 ? SH : SL) + (size_t)min(m0 + (sd >> 1), M - 1) * (K / 32) + 4 * gl + 2 * (sd & 1);
-        _Float16 *sdst = (wave < 4 ? wsum_hi : wsum_lo) +
-                         (((gl / kPfWinSteps) & 1) * kPfWinSteps + gl % kPfWinSteps) * kSumSlice + (wave & 3) * 128;
-        global_to_lds4(ssrc, sdst);
+        if constexpr (decltype(hc)::value == 0) {
+            if (copy16) global_to_lds16(hdr_src + (size_t)s * 144, S.hdr + wave * 64);
+        }
+        if (copy16)
+            global_to_lds16(sum_src + 8 * gl,
+                            wsum + (((gl / kPfWinSteps) & 1) * kPfWinSteps + gl % kPfWinSteps) * kSumSlice + wave * 128);
     };
 
-    f32x4 acc[4][2], cs[4][2];
+    f32x4 acc[8], cs[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = cs[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i) acc[i] = cs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // this lane's B rows inside the tile
-    int brow[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) brow[j] = 32 * wn + 16 * j + l16;
-
-    u32x4p mhd[2] = {u32x4p{0, 0, 0, 0}, u32x4p{0, 0, 0, 0}};  // min-term headers of this lane's slot
+    const int brow = 16 * wave + l16;  // this lane's B row (weight row) inside the tile
+    u32x4p mhd = u32x4p{0, 0, 0, 0};   // min-term header of this lane's slot
+    u32x4p hd = u32x4p{0, 0, 0, 0};    // the current superblock's header of this lane's column
 
     // Step g = g6 + k (g6 a multiple of 6): issue step g+2 into stage
     // (k+2) % 3, compute step g from stage k % 3, wait for step g+1's copies,
@@ -617,67 +635,50 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
         // lane / 16 is the superblock whose header this lane keeps
         const int sb_start = s - (s & (kPfWin - 1));
         const bool mlive = sb_start + quad <= s;
-        issue(g + 2, std::integral_constant<int, (k + 2) % kPf3Stages>{});
+        issue(g + 2, std::integral_constant<int, (k + 2) % kPf3Stages>{}, std::integral_constant<int, h>{});
         const Prefill3Stage &S = stage_ref(std::integral_constant<int, stage>{});
-        // headers of this lane's two columns; scales of this step's four
-        // sub-blocks (fields 4h .. 4h+3), zero for a padding step
-        u32x4p hd[2];
-        lds_read2_b128_256(lds_addr(S.hdr + 4 * brow[0]), hd[0], hd[1]);  // rows brow[0], brow[0] + 16
-        uint32_t bits[2];  // the four 6-bit scale fields 4h .. 4h+3 of each column
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bits[j] = h ? ((hd[j].y >> 24) | (hd[j].z << 8)) : hd[j].y;
+        // header of this lane's column (staged with the superblock's first
+        // half); scales of this step's four sub-blocks (fields 4h .. 4h+3)
+        if constexpr (h == 0) lds_read1_b128(lds_addr(S.hdr + 4 * brow), hd);
+        const uint32_t bits = h ? ((hd.y >> 24) | (hd.z << 8)) : hd.y;  // the four 6-bit scale fields
 #pragma unroll
         for (int kp = 0; kp < 4; kp += 2) {
-            // A rows 64 wm + 16 i + l16 (i = 0..3 at +4096 bytes), chunk
-            // (4 kk + quad) ^ l16; B rows brow[j] (j = 1 at +1024 bytes), 8 bytes at
-            // byte 32 * pair + 8 * quad of the row's 64: unit 2 pair + quad / 2,
-            // swizzled by (row >> 2) & 3 = (l16 >> 2) & 3
+            // A rows 16 i + l16 (i = 0..7 at +4096 bytes), chunk (4 kk + quad) ^ l16;
+            // B row brow, 8 bytes at byte 32 * pair + 8 * quad of the row's 64:
+            // unit 2 pair + quad / 2, swizzled by (row >> 2) & 3 = (l16 >> 2) & 3
             uint32_t aa[2], na[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int kk = kp + t;
-                const int ra = 64 * wm + l16;
-                aa[t] = lds_addr(S.a + (ra * kPf3ChunkUnits + ((4 * kk + quad) ^ l16)) * 8);
+                aa[t] = lds_addr(S.a + (l16 * kPf3ChunkUnits + ((4 * kk + quad) ^ l16)) * 8);
                 const int u = (2 * (kk >> 1) + (quad >> 1)) ^ ((l16 >> 2) & 3);
-                na[t] = lds_addr(S.nib + brow[0] * 64 + 16 * u + 8 * (quad & 1));
+                na[t] = lds_addr(S.nib + brow * 64 + 16 * u + 8 * (quad & 1));
             }
-            u32x4p ar[8];
-            uint2 nb[4];
-            lds_read_slice2(aa[0], na[0], aa[1], na[1], ar, nb);
+            u32x4p ar[16];
+            uint2 nb[2];
+            lds_read_slice2_t(aa[0], na[0], aa[1], na[1], ar, nb);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int kk = kp + t;
-                half8 af[4], bf[2];
+                const _Float16 v = (_Float16)(uint16_t)((bits >> (6 * kk)) & 63u);
+                const _Float16 o = v * (_Float16)(-1024.0f);  // exact: |.| <= 64512
+                const half8 bf = b_operand(nb[t], kk & 1, half2v{v, v}, half2v{o, o});
 #pragma unroll
-                for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(half8, ar[4 * t + i]);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const _Float16 v = (_Float16)(uint16_t)((bits[j] >> (6 * kk)) & 63u);
-                    const _Float16 o = v * (_Float16)(-1024.0f);  // exact: |.| <= 64512
-                    bf[j] = b_operand(nb[2 * t + j], kk & 1, half2v{v, v}, half2v{o, o});
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        cs[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], cs[i][j], 0, 0, 0);
+                for (int i = 0; i < 8; ++i)
+                    cs[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ar[8 * t + i]), bf, cs[i],
+                                                                   0, 0, 0);
             }
         }
         if constexpr (h == 1) {
             // superblock done: acc += d * cs, d of this lane's column; the lanes
-            // of this superblock's slot keep its headers for the min term
-            const bool keep = quad == (s & (kPfWin - 1));
+            // of this superblock's slot keep its header for the min term
+            mhd = quad == (s & (kPfWin - 1)) ? hd : mhd;
+            const float d = half_lo(hd.x);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mhd[j] = keep ? hd[j] : mhd[j];
+            for (int i = 0; i < 8; ++i) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float d = half_lo(hd[j].x);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf_exact(d, cs[i][j][e], acc[i][j][e]);
-                    cs[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                for (int e = 0; e < 4; ++e) acc[i][e] = fmaf_exact(d, cs[i][e], acc[i][e]);
+                cs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
         if (window_end) {
@@ -685,69 +686,51 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
             // window's block sums came with its steps' copies, all waited for.
             // Slots past the window's last superblock hold finite leftovers
             // (the buffers start zeroed) and meet zero weights below.
-            u32x4p t[8];
-            {
-                // token rows 16 apart (+128 bytes); the lane's 8 blocks are those
-                // of steps 2 quad and 2 quad + 1 of the window (+1024 bytes)
-                const int row = 64 * wm + l16;
-                const int sl0 = (((g / kPfWinSteps) & 1) * kPfWinSteps + 2 * quad) * kSumSlice + 4 * row;
-                uint2 rh[8], rl[8];
-                lds_read8_b64(lds_addr(wsum_hi + sl0), rh);
-                lds_read8_b64(lds_addr(wsum_lo + sl0), rl);
+            // Token rows 16 i + l16 (+256 bytes per i); the lane's 8 blocks are
+            // those of steps 2 quad and 2 quad + 1 of the window (+2048 bytes).
+            const int sl0 = (((g / kPfWinSteps) & 1) * kPfWinSteps + 2 * quad) * kSumSlice + 8 * l16;
+            u32x4p rs[16];
+            lds_read16_b128(lds_addr(wsum + sl0), rs);
+            const float dmin = mlive ? half_hi(mhd.x) : 0.0f;
+            float dmax = dmin;
+            dmax = fmaxf(dmax, __shfl_xor(dmax, 16, kWave));
+            dmax = fmaxf(dmax, __shfl_xor(dmax, 32, kWave));
+            const int E = row_exponent(dmax) - 6;
+            const float fac = -ldexpf(1.0f, kPfSumShift - E);
+            half8 mh, ml;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    t[i] = u32x4p{rh[i].x, rh[i].y, rh[4 + i].x, rh[4 + i].y};
-                    t[4 + i] = u32x4p{rl[i].x, rl[i].y, rl[4 + i].x, rl[4 + i].y};
-                }
-            }
-            half8 mh[2], ml[2];
-            float fac[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float dmin = mlive ? half_hi(mhd[j].x) : 0.0f;
-                float dmax = dmin;
-                dmax = fmaxf(dmax, __shfl_xor(dmax, 16, kWave));
-                dmax = fmaxf(dmax, __shfl_xor(dmax, 32, kWave));
-                const int E = row_exponent(dmax) - 6;
-                fac[j] = -ldexpf(1.0f, kPfSumShift - E);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float mv = ldexpf(dmin * (float)field6(mhd[j].y, mhd[j].z, mhd[j].w, 8 + e), E);
-                    _Float16 hi, lo;
-                    split_half(mv, hi, lo);
-                    mh[j][e] = hi;
-                    ml[j][e] = lo;
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float mv = ldexpf(dmin * (float)field6(mhd.y, mhd.z, mhd.w, 8 + e), E);
+                _Float16 hi, lo;
+                split_half(mv, hi, lo);
+                mh[e] = hi;
+                ml[e] = lo;
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 8; ++i) {
+                const half8 shi = __builtin_bit_cast(half8, u32x4p{rs[i].x, rs[i].y, rs[8 + i].x, rs[8 + i].y});
+                const half8 slo = __builtin_bit_cast(half8, u32x4p{rs[i].z, rs[i].w, rs[8 + i].z, rs[8 + i].w});
+                f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi, mh, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi, ml, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(slo, mh, c, 0, 0, 0);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const half8 shi = __builtin_bit_cast(half8, t[i]), slo = __builtin_bit_cast(half8, t[4 + i]);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi, mh[j], c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi, ml[j], c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(slo, mh[j], c, 0, 0, 0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf_exact(fac[j], c[e], acc[i][j][e]);
-                }
+                for (int e = 0; e < 4; ++e) acc[i][e] = fmaf_exact(fac, c[e], acc[i][e]);
+            }
         }
         // step g+1's copies have landed (this wave's; the barrier makes it every
-        // wave's) while step g+2's stay in flight; the block sums are written;
-        // after the barrier every wave is also done with stage g % 3, which step
-        // g+3 refills, and with the window's sums before the next window's
-        wait_vmem_lgkm<kPf3LoadsPerStep>();
+        // wave's) while step g+2's stay in flight; after the barrier every wave
+        // is also done with stage g % 3, which step g+3 refills
+        wait_vmem_lgkm<pf3_copies(h)>();
         barrier_no_fence();
     };
 
-    for (int i = tid; i < 2 * kPfWinSteps * kSumSlice / 8; i += kPf3Threads) {
-        reinterpret_cast<u32x4p *>(wsum_hi)[i] = u32x4p{0, 0, 0, 0};
-        reinterpret_cast<u32x4p *>(wsum_lo)[i] = u32x4p{0, 0, 0, 0};
-    }
+    for (int i = tid; i < 2 * kPfWinSteps * kSumSlice / 8; i += kPf3Threads)
+        reinterpret_cast<u32x4p *>(wsum)[i] = u32x4p{0, 0, 0, 0};
     __syncthreads();  // the zeros are written before any copy can land on them
-    issue(0, std::integral_constant<int, 0>{});
-    issue(1, std::integral_constant<int, 1>{});
-    wait_vmem_lgkm<kPf3LoadsPerStep>();  // step 0's copies are in LDS
+    issue(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    issue(1, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    wait_vmem_lgkm<pf3_copies(1)>();  // step 0's copies are in LDS
     barrier_no_fence();
     const int nbody = nsteps - nsteps % 6;
     int g6 = 0;
@@ -770,35 +753,29 @@ __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
     }
     wait_vmem_at_most<0>();  // no copy into LDS may still be in flight when the workgroup ends
 
+    const int n = n0 + brow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int m = m0 + 64 * wm + 16 * i + 4 * quad + e;
-            if (m >= M) continue;
-            const int ex = E_x[m];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int n = n0 + 32 * wn + 16 * j + l16;
-                if (n < N) Y[(size_t)m * N + n] = ldexpf(acc[i][j][e], -ex);
-            }
+            const int m = m0 + 16 * i + 4 * quad + e;
+            if (m < M && n < N) Y[(size_t)m * N + n] = ldexpf(acc[i][e], -E_x[m]);
         }
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// x * 2^e as fp16 [M][K], e [M], then the block sums' hi and lo halves
-// [M][K / 32] each, every region 256-byte aligned
+// x * 2^e as fp16 [M][K], e [M], then the block-sum records [M][K / 128][8]
+// (fp16), every region 256-byte aligned
 struct PrefillWs {
-    size_t off_e, off_sh, off_sl, total;
+    size_t off_e, off_s, total;
 };
 
 static PrefillWs prefill_ws_layout(int M, int K) {
     PrefillWs w;
     w.off_e = align256((size_t)M * K * 2);
-    w.off_sh = w.off_e + align256((size_t)M * 4);
-    w.off_sl = w.off_sh + align256((size_t)M * (K / 32) * 2);
-    w.total = w.off_sl + align256((size_t)M * (K / 32) * 2);
+    w.off_s = w.off_e + align256((size_t)M * 4);
+    w.total = w.off_s + align256((size_t)M * (K / 128) * 16);
     return w;
 }
 
@@ -840,14 +817,13 @@ extern "C" int qgemm_prefill_ws(int fmt, const void *W, int N, int K, const uint
     uint8_t *b = reinterpret_cast<uint8_t *>(ws);
     _Float16 *x16 = reinterpret_cast<_Float16 *>(b);
     int32_t *ex = reinterpret_cast<int32_t *>(b + lay.off_e);
-    _Float16 *sh = reinterpret_cast<_Float16 *>(b + lay.off_sh);
-    _Float16 *sl = reinterpret_cast<_Float16 *>(b + lay.off_sl);
+    _Float16 *ss = reinterpret_cast<_Float16 *>(b + lay.off_s);
     qg::clear_stale_error();
     hipLaunchKernelGGL(qg::prefill_prepass_kernel, dim3(M), dim3(qg::kPfPreThreads), 0, (hipStream_t)stream, x_bf16,
-                       K, x16, ex, sh, sl);
+                       K, x16, ex, ss);
     if (hipGetLastError() != hipSuccess) return QG_ERR_LAUNCH;
     dim3 grid((N + qg::kPfBN - 1) / qg::kPfBN, (M + qg::kPfBM - 1) / qg::kPfBM);
     hipLaunchKernelGGL(qg::qgemm_prefill_q4k_ws_kernel, grid, dim3(qg::kPf3Threads), 0, (hipStream_t)stream,
-                       reinterpret_cast<const uint8_t *>(W), N, K, M, x16, ex, sh, sl, y);
+                       reinterpret_cast<const uint8_t *>(W), N, K, M, x16, ex, ss, y);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
