@@ -552,7 +552,8 @@ __device__ __forceinline__ void wait_vmem_lgkm() {
 // sees that a step's LDS reads and the copies in flight into the other stages
 // are disjoint and waits for nothing early.  Up to five remaining steps run
 // in a guarded tail with the same property.  Copies past the last step
-// re-read the last step's data, so every step issues the same copies.
+// re-read the last step's data, so every step of a parity issues the same
+// copies (the waits count them: pf3_copies).
 __global__ __launch_bounds__(kPf3Threads) void qgemm_prefill_q4k_ws_kernel(
     const uint8_t *__restrict__ W, int N, int K, int M, const _Float16 *__restrict__ X16,
     const int32_t *__restrict__ E_x, const _Float16 *__restrict__ SS, float *__restrict__ Y) {
