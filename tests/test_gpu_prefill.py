@@ -37,9 +37,9 @@ def run_prefill(qg, W, N, K, xb, M, variant="plain"):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("N,K,M", [(96, 512, 40), (130, 1280, 129), (256, 1024, 256), (1, 256, 1), (300, 2304, 7),
-                                   (200, 2560, 300)])
+                                   (200, 2560, 300), (64, 16384, 33)])
 def test_prefill_parity_small(qg, orc, N, K, M, variant):
-    """Ragged N and M tails, K of 1..10 superblocks (partial min-term windows)."""
+    """Ragged N and M tails, K of 1..10 superblocks (partial min-term windows) and the largest K."""
     progress("prefill %s N=%d K=%d M=%d" % (variant, N, K, M))
     g = np.random.default_rng(500 + N + K + M)
     W = synth.q4k_weight(g, N, K)
