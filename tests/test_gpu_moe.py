@@ -243,6 +243,27 @@ def test_moe_popular_experts_on_matrix_cores(qg, orc, E, D, F, T, topk, seed, zi
             assert np.array_equal(host(out)[0].view(np.uint32), R["o"][p].view(np.uint32)), ("o", p)
 
 
+def test_moe_largest_table(qg, orc):
+    """The largest table: the most experts and the most pairs (4096 experts, 1024 tokens x
+    top-8 = 8192 pairs, Zipf(1.1) popularity, small matrices D = F = 256): the table and
+    the matrix-core work list exactly, and every stage of every pair and every token's
+    output against the oracle."""
+    E, D, F, T, topk = qg.MAX_EXPERTS, 256, 256, 1024, 8
+    assert T * topk == qg.MAX_MOE_PAIRS
+    progress("moe largest table E=%d T=%d topk=%d" % (E, T, topk))
+    pb = MoeProblem(qg, E, D, F, T, topk, 77, zipf=True, only_selected=True)
+    y, ws, st = pb.run()
+    assert st == 0
+    R = check_staged(qg, orc, pb, y, ws)
+    counts = np.diff(R["pair_off"])
+    assert counts.max() > 32 * 8 and R["n_uniq"] > 1000  # many-tile experts and a wide table
+    lay = qg.moe_routed_workspace_layout(T, topk, E, D, F)
+    hot = host(ws)[lay["HOT"]:].view(np.int32)
+    want = [(u, m0) for u in range(R["n_uniq"]) if counts[u] >= qg.MOE_MM_PAIRS for m0 in range(0, counts[u], 32)]
+    assert hot[0] == len(want)
+    assert [tuple(hot[1 + 2 * i:3 + 2 * i]) for i in range(len(want))] == want
+
+
 def test_moe_invariants(qg):
     pb = MoeProblem(qg, 20, 512, 256, 6, 6, 11)
     y, _, _ = pb.run()
