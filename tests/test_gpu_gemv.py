@@ -472,6 +472,27 @@ def test_grouped_past_4gib_of_activation(qg, orc):
     torch.cuda.empty_cache()
 
 
+def test_grouped_most_groups(qg, orc):
+    """The most groups a call takes (65535: the grid's y extent), 2 tokens, N = 3, K = 256:
+    sampled groups against the oracle, including the first and the last."""
+    import torch
+    G, N, K, M = 65535, 3, 256, 2
+    progress("grouped most groups G=%d" % G)
+    g_ = np.random.default_rng(4343)
+    base = synth.q8_0_weight(g_, 64 * N, K)  # matrix g is rows 3 (g % 64) .. + 2 of base
+    W = dev(base).reshape(64, N, -1).repeat((G + 63) // 64, 1, 1)[:G].reshape(G * N, -1).contiguous()
+    x = synth.activations(g_, M, G * K)
+    qx, dx, _ = orc.quantize_act_q8(x)
+    y = sentinel((M, G * N), torch.float32, 99.0)
+    qg.qgemv_grouped(0, W, G, N, K, dev(qx), dev(dx), None, M, y)
+    yh = host(y).reshape(M, G, N)
+    for gi in sorted(set([0, 1, 63, 64, G - 2, G - 1] + list(g_.choice(G, 40, replace=False)))):
+        wg = base[N * (gi % 64):N * (gi % 64) + N].copy()
+        sl = slice(gi * K, (gi + 1) * K)
+        ref, bound = orc.gemv(0, wg, N, K, qx[:, sl].copy(), dx[:, gi * K // 32:(gi + 1) * K // 32].copy())
+        assert_within_bound(yh[:, gi], ref, bound, what="grouped g=%d" % gi)
+
+
 def test_grouped_errors(qg):
     import torch
     W = dev(synth.q8_0_weight(np.random.default_rng(1), 16, 512))
@@ -504,6 +525,7 @@ PREFILL_Q8_0_CASES = [
     (2048, 8192, 300),
     (8192, 2304, 200),
     (8192, 4096, 512),  # the 512-token prefill of the 4096 -> 8192 projection
+    (64, 256, 65536),  # the most tokens (2048 token tiles)
 ]
 
 
