@@ -1,31 +1,39 @@
-// Batched decode mat-vec on the matrix cores: Q8_0 weights x Q8 activation
-// for a batch of tokens ("ROCm: restore DeepSeek V4 Flash decode performance
-// and Q4 SSD streaming", antirez/ds4 PR 623: the Q8_0 projections on a
-// prequantized activation; the page's kernels take one token per call, this
-// form serves the batched calls of the same projections).
+// Batched decode mat-vec on the matrix cores: Q8_0 or Q4_K weights x Q8
+// activation for a batch of tokens ("ROCm: restore DeepSeek V4 Flash decode
+// performance and Q4 SSD streaming", antirez/ds4 PR 623: the Q8_0 projections
+// on a prequantized activation; the page's kernels take one token per call,
+// this form serves the batched calls of the same projections, and prefill
+// batches of Q8_0 through qgemm_q8_0).
 //
 // Numerics are those of the one-token engine, so a batched call reproduces
 // the one-token call bit for bit on every token:
 //   * a v_mfma_i32_32x32x32_i8 per 32-block gives the exact integer block sum
-//     isum[n, m, b] for 32 rows x 32 tokens;
-//   * s = fp32(dw[n, b] * dx[m, b]) and acc = fma(isum, s, acc) in block
+//     isum[n, m, b] for 32 rows x 32 tokens (Q4_K: the A operand holds the
+//     sub-block's nibbles);
+//   * Q8_0: s = fp32(dw[n, b] * dx[m, b]) and acc = fma(isum, s, acc) in block
 //     order inside each unit of NB blocks (the one-token engine's per-lane
-//     unit), starting from +0;
+//     unit), starting from +0; Q4_K: inner = fma(d sc_j, isum, -(dmin m_j) sx_j)
+//     and acc = fma(inner, dx_j, acc) over the superblock's sub-blocks;
 //   * the units of a row are summed by the same pairwise tree over the next
 //     power of two of units (the one-token engine's xor butterfly, padded
 //     with zeros).
 //
-// Token tiles: a workgroup takes 32 tokens; larger batches (the prefill
-// product qgemm_q8_0) run one workgroup per (row tile, token tile), the token
-// tiles of a row tile next to each other in the launch order.
+// Token tiles: a workgroup takes TT tiles of 32 tokens (TT > 1 for Q8_0
+// batches of several tiles, whose waves then share each slice's weight
+// stage); larger batches run one workgroup per (row tile, token block).
+// With several token blocks per row tile, the workgroups are remapped so that
+// each XCD runs a contiguous range of row tiles (workgroups are dealt to the
+// XCDs in turn), so a row tile's weights are fetched into one XCD's L2.
 //
-// Work split: a workgroup owns 32 rows of one matrix; its KS waves take
-// consecutive, power-of-two-aligned slices of the row's 256-weight groups, so
-// each slice is a subtree of the unit tree.  A wave streams its 32 rows'
-// groups through registers into a private LDS stage (the next group's loads
-// stay in flight while the current one is multiplied), builds a small table of
-// the stage's fp16 block scales, and keeps one partial sum per tree level.  The
-// slices' subtree sums meet in LDS and are added in tree order.
+// Work split: a workgroup owns 32 rows of one matrix; its KS slices (waves per
+// token tile) take consecutive, power-of-two-aligned runs of the row's
+// 256-weight groups, so each slice is a subtree of the unit tree.  A slice
+// streams its 32 rows' groups through registers into an LDS stage (the
+// groups two ahead stay in flight while the current one is multiplied),
+// builds a small table of the stage's scales, and keeps one partial sum per
+// tree level.  Where the LDS allows it, the activation goes through a small
+// LDS tile too (see mm_device.h).  The slices' subtree sums meet in LDS and
+// are added in tree order.
 //
 // MFMA roles: A = weights (row i = lane % 32, 16 of the block's 32 quants per
 // lane half), B = activation (token j = lane % 32).  The 32x32 i32 result puts
